@@ -1,0 +1,205 @@
+"""Seeded synthetic inputs for selected-cell INT8 decode attention.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no gather, no dot product, no softmax).  Both the CPU
+oracle (through the tests and the bench's CPU leg) and the HIP path consume
+exactly the arrays produced here.
+
+Workload shapes follow the kernel benchmark on the Strata PR #2220 page
+("Kernel (chunk kernel + merge, synthetic INT8 pools, permuted page table,
+200 calls)"): INT8 K/V pools behind a permuted page table, 12 query heads per
+KV head with head_dim 256 (the PR's description of one lane holding 8 dims of
+each of the 12 heads across a 32-lane warp), 1-4 query positions (MTP verify
+positions), 600 or 2,051 selected cells.
+
+Layout produced (all numpy, C-contiguous):
+
+  k_codes, v_codes  int8   [n_inst * pool_cells, head_dim]  one global pool;
+                           instance i physically owns pages
+                           [i*pages, (i+1)*pages)
+  k_scales, v_scales uint16 [n_inst * pool_cells]  IEEE binary16 bit patterns,
+                           one scale per physical cell
+  page_table        int32  [n_inst, pages]  global physical page id per
+                           logical page (a random permutation of the
+                           instance's own pages); -1 would mask a page
+  sel               int32  [n_inst, n_sel]  selected logical cell ids
+  n_sel             int32  [n_inst]
+  q                 float32 [n_inst, n_q, n_qheads, head_dim]
+
+Random streams: numpy Generator(PCG64); the config seed is 20261200 + cfg
+unless given; instance i draws from SeedSequence(seed).spawn(n_inst)[i] in a
+fixed order (page permutation, selection, K codes, V codes, K scales,
+V scales, heavy-tail offsets, q), so any instance can be regenerated alone.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import os
+
+import numpy as np
+
+PAGE_SIZE = 16
+HEAD_DIM = 256
+N_QHEADS = 12
+SOFTMAX_SCALE = 1.0 / 16.0
+SCALE_LO, SCALE_HI = 0.002, 0.02
+
+# The five workloads.  "chunk" is the chunk size in selected cells; the batched
+# decode workload leaves it open, so a value is chosen here (see DEFAULT_CHUNK_2).
+DEFAULT_CHUNK_2 = 1024
+
+CONFIGS = {
+    0: dict(workload="tiny_single_step", n_inst=1, n_q=1, pool_cells=4096,
+            n_sel=600, sel="uniform", heavy=False, chunk=256),
+    1: dict(workload="pages_kernel_point_2051x1-4q", n_inst=1, n_q=4,
+            pool_cells=32768, n_sel=2051, sel="uniform", heavy=False, chunk=256),
+    2: dict(workload="batched_decode_256inst_2051x4q", n_inst=256, n_q=4,
+            pool_cells=32768, n_sel=2051, sel="uniform", heavy=True,
+            chunk=DEFAULT_CHUNK_2),
+    3: dict(workload="long_context_runs_64inst_16384x2q", n_inst=64, n_q=2,
+            pool_cells=131072, n_sel=16384, sel="runs", heavy=False, chunk=512,
+            n_runs=64, run_len=256),
+    4: dict(workload="dense_fallback_32inst_131072x4q", n_inst=32, n_q=4,
+            pool_cells=131072, n_sel=131072, sel="all", heavy=False, chunk=1024),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    k_codes: np.ndarray
+    v_codes: np.ndarray
+    k_scales: np.ndarray
+    v_scales: np.ndarray
+    page_table: np.ndarray
+    sel: np.ndarray
+    n_sel: np.ndarray
+    q: np.ndarray
+    softmax_scale: float
+    chunk: int
+    workload: str
+    seed: int
+
+    @property
+    def n_inst(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def n_q(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def n_qheads(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def head_dim(self) -> int:
+        return int(self.q.shape[3])
+
+    @property
+    def n_logical_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def n_phys_pages(self) -> int:
+        return int(self.k_codes.shape[0] // PAGE_SIZE)
+
+    def with_n_q(self, n_q: int) -> "Inputs":
+        """View with the first n_q query positions (same pools and selection)."""
+        return dataclasses.replace(self, q=np.ascontiguousarray(self.q[:, :n_q]))
+
+
+def config_seed(cfg: int) -> int:
+    return 20261200 + int(cfg)
+
+
+def _draw_selection(rng, mode, pool_cells, n_sel, spec):
+    if mode == "uniform":
+        s = rng.choice(pool_cells, size=n_sel, replace=False)
+        return np.sort(s).astype(np.int32)
+    if mode == "all":
+        return np.arange(pool_cells, dtype=np.int32)[:n_sel]
+    if mode == "runs":
+        # n_runs non-overlapping runs of run_len cells at random offsets: the
+        # unselected cells are cut into n_runs+1 gaps at sorted uniform points
+        # and run k starts after gap k.  Gaps may be empty (runs may touch).
+        n_runs, run_len = spec["n_runs"], spec["run_len"]
+        assert n_runs * run_len == n_sel
+        free = pool_cells - n_sel
+        cuts = np.sort(rng.integers(0, free, size=n_runs, endpoint=True))
+        starts = cuts + run_len * np.arange(n_runs)
+        s = (starts[:, None] + np.arange(run_len)[None, :]).reshape(-1)
+        return s.astype(np.int32)
+    raise ValueError(mode)
+
+
+def _fill_instance(i, ss, spec, out, heavy):
+    rng = np.random.Generator(np.random.PCG64(ss))
+    pool_cells = spec["pool_cells"]
+    pages = pool_cells // PAGE_SIZE
+    D = out["k_codes"].shape[1]
+    lo, hi = i * pool_cells, (i + 1) * pool_cells
+    out["page_table"][i] = (rng.permutation(pages) + i * pages).astype(np.int32)
+    out["sel"][i] = _draw_selection(rng, spec["sel"], pool_cells, spec["n_sel"], spec)
+    out["k_codes"][lo:hi] = rng.integers(-127, 127, size=(pool_cells, D),
+                                         dtype=np.int8, endpoint=True)
+    out["v_codes"][lo:hi] = rng.integers(-127, 127, size=(pool_cells, D),
+                                         dtype=np.int8, endpoint=True)
+    ks = rng.uniform(SCALE_LO, SCALE_HI, size=pool_cells)
+    vs = rng.uniform(SCALE_LO, SCALE_HI, size=pool_cells)
+    if heavy:
+        # Heavy-tailed K scales: a per-cell N(0, sigma=3) offset added to the
+        # (positive) scale magnitude; the sign is kept positive by taking the
+        # magnitude of the sum.
+        ks = np.abs(ks + rng.normal(0.0, 3.0, size=pool_cells))
+    out["k_scales"][lo:hi] = ks.astype(np.float16).view(np.uint16)
+    out["v_scales"][lo:hi] = vs.astype(np.float16).view(np.uint16)
+    out["q"][i] = rng.standard_normal(size=out["q"].shape[1:], dtype=np.float32)
+
+
+def make(cfg: int | None = None, seed: int | None = None, *, threads: int | None = None,
+         **overrides) -> Inputs:
+    """Generate the inputs of workload `cfg` (0-4), optionally with overrides.
+
+    Overrides accept any key of CONFIGS[cfg] plus n_qheads / head_dim, e.g.
+    make(1, n_sel=65, pool_cells=1024) for an edge case with a given seed.
+    With cfg=None the overrides must give the whole spec.
+    """
+    spec = dict(CONFIGS[cfg]) if cfg is not None else {}
+    spec.update(overrides)
+    spec.setdefault("n_qheads", N_QHEADS)
+    spec.setdefault("head_dim", HEAD_DIM)
+    spec.setdefault("heavy", False)
+    spec.setdefault("chunk", 256)
+    spec.setdefault("workload", "custom")
+    if seed is None:
+        seed = config_seed(cfg if cfg is not None else 99)
+    n_inst, pool_cells = int(spec["n_inst"]), int(spec["pool_cells"])
+    if pool_cells % PAGE_SIZE:
+        raise ValueError("pool_cells must be a multiple of the page size")
+    n_sel, D = int(spec["n_sel"]), int(spec["head_dim"])
+    if n_sel > pool_cells:
+        raise ValueError("n_sel > pool_cells")
+    pages = pool_cells // PAGE_SIZE
+    total = n_inst * pool_cells
+    out = dict(
+        k_codes=np.empty((total, D), np.int8),
+        v_codes=np.empty((total, D), np.int8),
+        k_scales=np.empty((total,), np.uint16),
+        v_scales=np.empty((total,), np.uint16),
+        page_table=np.empty((n_inst, pages), np.int32),
+        sel=np.empty((n_inst, n_sel), np.int32),
+        q=np.empty((n_inst, int(spec["n_q"]), int(spec["n_qheads"]), D), np.float32),
+    )
+    children = np.random.SeedSequence(seed).spawn(n_inst)
+    heavy = bool(spec["heavy"])
+    if n_inst == 1:
+        _fill_instance(0, children[0], spec, out, heavy)
+    else:
+        nt = threads or min(16, os.cpu_count() or 1)
+        with _cf.ThreadPoolExecutor(nt) as ex:
+            list(ex.map(lambda i: _fill_instance(i, children[i], spec, out, heavy),
+                        range(n_inst)))
+    return Inputs(n_sel=np.full((n_inst,), n_sel, np.int32),
+                  softmax_scale=SOFTMAX_SCALE, chunk=int(spec["chunk"]),
+                  workload=str(spec["workload"]), seed=int(seed), **out)

@@ -1,0 +1,232 @@
+/*
+ * CPU oracle for decode-time attention over a selected subset of KV cells
+ * held as INT8 K/V pools behind a page table.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * loads this file; only the tests, the package's smoke check and the bench's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * HIP path.
+ *
+ * Everything is plain C with fp64 arithmetic, written as the definition of
+ * the result rather than as a fast algorithm.  OpenMP only distributes
+ * independent (instance, query row) pairs over host threads; it does not
+ * change any arithmetic.
+ *
+ * Source: Strata PR #2220 page (the decode attention over the QSA selection,
+ * "attn_chunk_q8_v3_kernel"): each selected cell is scored against the
+ * grouped query heads sharing its KV head, a softmax runs over the selected
+ * cells, the INT8 V rows are accumulated into per-chunk partials, and a merge
+ * combines the partials into the head output.  The Strata round-9 page
+ * (section "R9-gpu-11: four score cells per step in daily INT8 attention",
+ * its "Tests and rejection" paragraph) names the partials (accumulators,
+ * maxima, denominators), page -1 masking and the 0/1/2/3/63/64/65-cell edge
+ * counts.  Readings where the pages are silent:
+ *   - one IEEE binary16 scale per physical cell for K and one for V; the
+ *     dequantised value is code * scale;
+ *   - score = softmax_scale * k_scale * sum_d q[d] * k_code[d];
+ *   - page = 16 cells: logical cell c lives at slot c % 16 of logical page
+ *     c / 16; physical cell = page_table[c / 16] * 16 + c % 16;
+ *   - a page id of -1 (or any id outside [0, n_phys_pages)) masks the cell,
+ *     and so does a selected id outside the instance's logical range;
+ *   - every query position attends to the whole selection of its instance
+ *     (no causal mask between verify positions);
+ *   - with no unmasked cell the output is 0 and the log-sum-exp is -inf;
+ *   - partial of a chunk (a run of `chunk` consecutive list positions):
+ *     m = max score, l = sum exp(score - m), acc = sum exp(score - m) * v_hat;
+ *     an all-masked chunk has m = -inf, l = 0, acc = 0;
+ *   - merge: M = max m_c, L = sum l_c e^(m_c - M),
+ *     out = sum acc_c e^(m_c - M) / L, lse = M + ln L (natural log).
+ *
+ * Parity pins (tests/test_oracle.py): binary16 decode against numpy on all
+ * 65,536 bit patterns; dense result against a textbook softmax-attention
+ * built with numpy/scipy on tiny inputs; closed forms (one cell, two cells,
+ * identical keys, zero query); invariants (selection order, chunking for
+ * several chunk sizes, uniform score shift realised through the inputs,
+ * physical page relabelling, masking equals deletion, exact doubling of V
+ * scales); brute force over subsets of a tiny pool.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#define ORACLE_PAGE 16
+
+/* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
+ * 5 exponent bits with bias 15, 10 fraction bits; exponent 0 encodes
+ * subnormals f * 2^-24, exponent 31 encodes inf/nan. */
+double oracle_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* Page-table gather for one selected logical cell.  Returns the physical cell
+ * index or -1 when the cell is masked. */
+static int64_t gather_one(int32_t c, const int32_t *pt, int64_t n_logical_pages,
+                          int64_t n_phys_pages) {
+    if (c < 0) return -1;
+    int64_t lp = (int64_t)c / ORACLE_PAGE;
+    int64_t slot = (int64_t)c % ORACLE_PAGE;
+    if (lp >= n_logical_pages) return -1;
+    int64_t pp = pt[lp];
+    if (pp < 0 || pp >= n_phys_pages) return -1;
+    return pp * ORACLE_PAGE + slot;
+}
+
+/* Gather for every instance: phys_out[i][j] for j < n_sel[i]; entries from
+ * n_sel[i] to sel_stride-1 are left untouched. */
+void oracle_gather(int64_t n_inst, const int32_t *sel, int64_t sel_stride,
+                   const int32_t *n_sel, const int32_t *page_table, int64_t pt_stride,
+                   int64_t n_logical_pages, int64_t n_phys_pages, int64_t *phys_out) {
+    for (int64_t i = 0; i < n_inst; ++i)
+        for (int64_t j = 0; j < n_sel[i]; ++j)
+            phys_out[i * sel_stride + j] =
+                gather_one(sel[i * sel_stride + j], page_table + i * pt_stride,
+                           n_logical_pages, n_phys_pages);
+}
+
+typedef struct {
+    const int8_t *k_codes, *v_codes;     /* [cells][head_dim] */
+    const uint16_t *k_scales, *v_scales; /* [cells] binary16 bits */
+    int64_t n_phys_pages;
+    int64_t head_dim;
+} pool_t;
+
+/* score of one query row against one physical cell */
+static double score(const pool_t *P, const float *qrow, int64_t phys, double sm_scale) {
+    const int8_t *k = P->k_codes + phys * P->head_dim;
+    double dot = 0.0;
+    for (int64_t d = 0; d < P->head_dim; ++d) dot += (double)qrow[d] * (double)k[d];
+    return sm_scale * oracle_half_to_double(P->k_scales[phys]) * dot;
+}
+
+/* Softmax attention of one query row over list positions [j0, j1) of one
+ * instance's selection.  Writes the unnormalised accumulator acc[d]
+ * (= sum_j e^(s_j - m) v_hat_j[d]), the maximum m and the denominator l.
+ * No unmasked cell: m = -inf, l = 0, acc = 0. */
+static void attend_range(const pool_t *P, const float *qrow, const int32_t *sel,
+                         int64_t j0, int64_t j1, const int32_t *pt,
+                         int64_t n_logical_pages, double sm_scale, double *acc,
+                         double *m_out, double *l_out) {
+    const int64_t D = P->head_dim;
+    double m = -INFINITY;
+    for (int64_t j = j0; j < j1; ++j) {
+        int64_t ph = gather_one(sel[j], pt, n_logical_pages, P->n_phys_pages);
+        if (ph < 0) continue;
+        double s = score(P, qrow, ph, sm_scale);
+        if (s > m) m = s;
+    }
+    for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
+    double l = 0.0;
+    if (m != -INFINITY) {
+        for (int64_t j = j0; j < j1; ++j) {
+            int64_t ph = gather_one(sel[j], pt, n_logical_pages, P->n_phys_pages);
+            if (ph < 0) continue;
+            double p = exp(score(P, qrow, ph, sm_scale) - m);
+            double w = p * oracle_half_to_double(P->v_scales[ph]);
+            const int8_t *v = P->v_codes + ph * D;
+            l += p;
+            for (int64_t d = 0; d < D; ++d) acc[d] += w * (double)v[d];
+        }
+    }
+    *m_out = m;
+    *l_out = l;
+}
+
+/* Dense result: out[i][r][d] and lse[i][r] for every instance i in
+ * `inst_ids` (n_ids of them; NULL means 0..n_inst-1) and every query row
+ * r = t * n_qheads + h.  out/lse are indexed by position in the id list.
+ * q is float32 [n_inst][n_rows][head_dim]; sel is [n_inst][sel_stride];
+ * page_table is [n_inst][pt_stride]. */
+void oracle_attend(const int8_t *k_codes, const uint16_t *k_scales, const int8_t *v_codes,
+                   const uint16_t *v_scales, int64_t n_phys_pages, int64_t head_dim,
+                   const int32_t *page_table, int64_t pt_stride, int64_t n_logical_pages,
+                   const int32_t *sel, int64_t sel_stride, const int32_t *n_sel,
+                   const float *q, int64_t n_rows, double sm_scale, const int64_t *inst_ids,
+                   int64_t n_ids, double *out, double *lse) {
+    pool_t P = {k_codes, v_codes, k_scales, v_scales, n_phys_pages, head_dim};
+    const int64_t D = head_dim;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < n_ids * n_rows; ++u) {
+        int64_t k = u / n_rows, r = u % n_rows;
+        int64_t i = inst_ids ? inst_ids[k] : k;
+        double m, l;
+        double *o = out + (k * n_rows + r) * D;
+        attend_range(&P, q + (i * n_rows + r) * D, sel + i * sel_stride, 0, n_sel[i],
+                     page_table + i * pt_stride, n_logical_pages, sm_scale, o, &m, &l);
+        if (m == -INFINITY) {
+            lse[k * n_rows + r] = -INFINITY; /* o already zero */
+        } else {
+            for (int64_t d = 0; d < D; ++d) o[d] /= l;
+            lse[k * n_rows + r] = m + log(l);
+        }
+    }
+}
+
+/* Chunk partials: for each listed instance, chunk c (list positions
+ * [c*chunk, min((c+1)*chunk, n_sel))) and row r: acc[k][c][r][D], m, l
+ * ([k][c][r]).  Chunks past the instance's last (c >= ceil(n_sel/chunk)) are
+ * written as empty partials. */
+void oracle_chunk_partials(const int8_t *k_codes, const uint16_t *k_scales,
+                           const int8_t *v_codes, const uint16_t *v_scales,
+                           int64_t n_phys_pages, int64_t head_dim, const int32_t *page_table,
+                           int64_t pt_stride, int64_t n_logical_pages, const int32_t *sel,
+                           int64_t sel_stride, const int32_t *n_sel, const float *q,
+                           int64_t n_rows, double sm_scale, int64_t chunk, int64_t n_chunks,
+                           const int64_t *inst_ids, int64_t n_ids, double *acc, double *m,
+                           double *l) {
+    pool_t P = {k_codes, v_codes, k_scales, v_scales, n_phys_pages, head_dim};
+    const int64_t D = head_dim;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < n_ids * n_chunks * n_rows; ++u) {
+        int64_t k = u / (n_chunks * n_rows);
+        int64_t c = (u / n_rows) % n_chunks;
+        int64_t r = u % n_rows;
+        int64_t i = inst_ids ? inst_ids[k] : k;
+        int64_t j0 = c * chunk, j1 = j0 + chunk;
+        if (j1 > n_sel[i]) j1 = n_sel[i];
+        if (j0 > j1) j0 = j1;
+        int64_t o = (k * n_chunks + c) * n_rows + r;
+        attend_range(&P, q + (i * n_rows + r) * D, sel + i * sel_stride, j0, j1,
+                     page_table + i * pt_stride, n_logical_pages, sm_scale, acc + o * D,
+                     m + o, l + o);
+    }
+}
+
+/* Log-sum-exp merge of n_chunks partials for each of n_units (instance,row)
+ * units: acc [u][c][D] as laid out by the caller through strides, m and l
+ * [u][c].  out [u][D], lse [u].  All-empty: out = 0, lse = -inf. */
+void oracle_merge(int64_t n_units, int64_t n_chunks, int64_t head_dim, const double *acc,
+                  const double *m, const double *l, double *out, double *lse) {
+    const int64_t D = head_dim;
+    for (int64_t u = 0; u < n_units; ++u) {
+        double M = -INFINITY;
+        for (int64_t c = 0; c < n_chunks; ++c)
+            if (m[u * n_chunks + c] > M) M = m[u * n_chunks + c];
+        double *o = out + u * D;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (M == -INFINITY) {
+            lse[u] = -INFINITY;
+            continue;
+        }
+        double L = 0.0;
+        for (int64_t c = 0; c < n_chunks; ++c) {
+            double mc = m[u * n_chunks + c];
+            if (mc == -INFINITY) continue; /* empty chunk: contributes nothing */
+            double w = exp(mc - M);
+            L += l[u * n_chunks + c] * w;
+            const double *a = acc + (u * n_chunks + c) * D;
+            for (int64_t d = 0; d < D; ++d) o[d] += a[d] * w;
+        }
+        for (int64_t d = 0; d < D; ++d) o[d] /= L;
+        lse[u] = M + log(L);
+    }
+}

@@ -1,0 +1,361 @@
+"""Pins for the CPU oracle: checks that tie it to something other than itself.
+
+Each pin takes an oracle module-like object `O` (functions gather, attend,
+chunk_partials, merge, half_to_double) and raises AssertionError when the
+oracle disagrees with:
+  - a library routine (numpy's binary16 decode; scipy's softmax and
+    logsumexp applied to a dense matrix built by numpy reshapes of the pool);
+  - a closed form (one cell, two cells, identical keys, zero query, a
+    hand-computed example stored under tests/golden/, the merge of two
+    partials with known values);
+  - an invariant that the exact result has (selection order, chunk size,
+    a uniform score shift realised through the inputs, relabelling of
+    physical pages, masking equals deletion, doubling V scales doubles the
+    output, duplicate entries).
+test_oracle.py runs every pin against the oracle, and also against mutated
+copies of the oracle source to show that plausible mistakes are caught.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+import os
+import types
+
+import numpy as np
+import scipy.special
+
+from decode_attention_sparse_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def f16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def tiny(seed, **kw):
+    spec = dict(n_inst=1, n_q=1, n_qheads=3, head_dim=8, pool_cells=64, n_sel=10,
+                sel="uniform", heavy=False, chunk=4)
+    spec.update(kw)
+    return gen.make(None, seed=seed, **spec)
+
+
+def textbook(x, i):
+    """softmax(S) V over the selected rows of a dense dequantised matrix.
+
+    The logical view of the pool is built with numpy: the physical pool is
+    reshaped into pages, the page table indexes pages, and the result is
+    flattened back to cells; a selected id then indexes that flattened view."""
+    D = x.q.shape[-1]
+    n_pages_phys = x.k_codes.shape[0] // 16
+    Kp = (x.k_codes.astype(np.float64) * f16(x.k_scales)[:, None]).reshape(n_pages_phys, 16, D)
+    Vp = (x.v_codes.astype(np.float64) * f16(x.v_scales)[:, None]).reshape(n_pages_phys, 16, D)
+    pt = np.asarray(x.page_table[i], np.int64)
+    page_ok = (pt >= 0) & (pt < n_pages_phys)
+    safe = np.where(page_ok, pt, 0)
+    Klog = Kp[safe].reshape(-1, D)
+    Vlog = Vp[safe].reshape(-1, D)
+    ok_log = np.repeat(page_ok, 16)
+    s = np.asarray(x.sel[i, : x.n_sel[i]], np.int64)
+    in_range = (s >= 0) & (s < Klog.shape[0])
+    s_in = s[in_range]
+    keep = ok_log[s_in]
+    Ks, Vs = Klog[s_in][keep], Vlog[s_in][keep]
+    Q = np.asarray(x.q[i], np.float64).reshape(-1, D)
+    R = Q.shape[0]
+    if Ks.shape[0] == 0:
+        return np.zeros((R, D)), np.full((R,), -np.inf)
+    S = float(x.softmax_scale) * (Q @ Ks.T)
+    P = scipy.special.softmax(S, axis=1)
+    return P @ Vs, scipy.special.logsumexp(S, axis=1)
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    bad = ~same_inf & ~(np.abs(a - b) <= atol + rtol * np.abs(b))
+    assert not bad.any(), f"{what}: max |diff| {np.nanmax(np.abs(np.where(same_inf, 0, a - b)))}"
+
+
+def _attend_flat(O, x, ids=None):
+    out, lse = O.attend(x, ids)
+    k = out.shape[0]
+    D = out.shape[-1]
+    return out.reshape(k, -1, D), lse.reshape(k, -1)
+
+
+# ---------------------------------------------------------------- library pins
+def pin_half_decode(O):
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = O.half_to_double(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def pin_textbook(O):
+    cases = [
+        tiny(1),
+        tiny(2, n_q=2, n_sel=40, pool_cells=128),
+        tiny(3, n_inst=3, n_q=2, n_qheads=2, head_dim=16, pool_cells=96, n_sel=64),
+        tiny(4, head_dim=256, n_qheads=12, pool_cells=256, n_sel=33),
+        tiny(5, n_sel=20, pool_cells=64, heavy=True),
+    ]
+    # masked pages and out-of-range entries
+    x = tiny(6, n_sel=30, pool_cells=128)
+    pt = x.page_table.copy()
+    pt[0, 1] = -1
+    pt[0, 5] = 10_000
+    sel = x.sel.copy()
+    sel[0, 0] = -3
+    sel[0, 1] = 128 + 5
+    cases.append(dataclasses.replace(x, page_table=pt, sel=sel))
+    for x in cases:
+        out, lse = _attend_flat(O, x)
+        for i in range(x.q.shape[0]):
+            ro, rl = textbook(x, i)
+            _close(out[i], ro, 1e-12, 1e-14, "textbook out")
+            _close(lse[i], rl, 1e-12, 1e-14, "textbook lse")
+
+
+def pin_gather_exhaustive(O):
+    """Every logical cell of a 4,096-cell pool (one chunk of 256 pages) against
+    the numpy page view of physical cell ids, with masked pages."""
+    x = gen.make(0, n_sel=4096)  # all cells, permuted table
+    pt = x.page_table.copy()
+    pt[0, [0, 7, 255]] = -1
+    x = dataclasses.replace(x, page_table=pt)
+    got = O.gather(x)[0]
+    phys_ids = np.arange(x.k_codes.shape[0], dtype=np.int64).reshape(-1, 16)
+    ok = pt[0] >= 0
+    view = np.where(ok[:, None], phys_ids[np.where(ok, pt[0], 0)], -1).reshape(-1)
+    assert np.array_equal(got, view[x.sel[0]])
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_one_cell(O):
+    x = tiny(11, n_sel=1, n_qheads=4)
+    out, lse = _attend_flat(O, x)
+    c = int(x.sel[0, 0])
+    ph = int(x.page_table[0, c // 16]) * 16 + c % 16
+    v_hat = x.v_codes[ph].astype(np.float64) * f16(x.v_scales[ph])
+    for r in range(out.shape[1]):
+        assert np.array_equal(out[0, r], v_hat)  # weight exactly 1
+    # lse equals the score; the score itself is pinned by pin_textbook
+    ro, rl = textbook(x, 0)
+    _close(lse[0], rl, 1e-13, 0, "one-cell lse")
+
+
+def pin_two_cells(O):
+    x = tiny(12, n_sel=2, n_qheads=2, heavy=True)
+    out, lse = _attend_flat(O, x)
+    D = x.q.shape[-1]
+    phs = [int(x.page_table[0, c // 16]) * 16 + c % 16 for c in x.sel[0]]
+    vh = [x.v_codes[p].astype(np.float64) * f16(x.v_scales[p]) for p in phs]
+    kh = [x.k_codes[p].astype(np.float64) * f16(x.k_scales[p]) for p in phs]
+    for r in range(out.shape[1]):
+        q = x.q[0].reshape(-1, D)[r].astype(np.float64)
+        s1, s2 = (x.softmax_scale * float(q @ k) for k in kh)
+        w1 = 1.0 / (1.0 + math.exp(s2 - s1))
+        w2 = 1.0 / (1.0 + math.exp(s1 - s2))
+        _close(out[0, r], w1 * vh[0] + w2 * vh[1], 1e-12, 1e-15, "two-cell out")
+        _close(lse[0, r], np.logaddexp(s1, s2), 1e-13, 0, "two-cell lse")
+
+
+def pin_zero_query(O):
+    """q = 0: every score is 0, weights are uniform, lse = ln n."""
+    x = tiny(13, n_sel=37, pool_cells=128, n_qheads=2)
+    x = dataclasses.replace(x, q=np.zeros_like(x.q))
+    out, lse = _attend_flat(O, x)
+    phs = [int(x.page_table[0, c // 16]) * 16 + c % 16 for c in x.sel[0]]
+    mean = np.mean([x.v_codes[p].astype(np.float64) * f16(x.v_scales[p]) for p in phs], axis=0)
+    for r in range(out.shape[1]):
+        assert lse[0, r] == math.log(37)
+        _close(out[0, r], mean, 1e-13, 1e-16, "zero-q out")
+
+
+def pin_identical_keys(O):
+    """All selected cells share one key row and scale: uniform weights,
+    lse = s + ln n with s the common score."""
+    x = tiny(14, n_sel=9, pool_cells=64, n_qheads=3)
+    kc = x.k_codes.copy()
+    kc[:] = kc[5]
+    ks = x.k_scales.copy()
+    ks[:] = ks[5]
+    y = dataclasses.replace(x, k_codes=kc, k_scales=ks)
+    out, lse = _attend_flat(O, y)
+    D = x.q.shape[-1]
+    k_hat = kc[5].astype(np.float64) * f16(ks[5])
+    phs = [int(x.page_table[0, c // 16]) * 16 + c % 16 for c in x.sel[0]]
+    mean = np.mean([x.v_codes[p].astype(np.float64) * f16(x.v_scales[p]) for p in phs], axis=0)
+    for r in range(out.shape[1]):
+        s = x.softmax_scale * float(x.q[0].reshape(-1, D)[r].astype(np.float64) @ k_hat)
+        _close(lse[0, r], s + math.log(9), 1e-13, 1e-15, "identical-keys lse")
+        _close(out[0, r], mean, 1e-13, 1e-16, "identical-keys out")
+
+
+def load_worked_example():
+    """tests/golden/worked_example.txt: a hand-computed instance (see the file)."""
+    vals = {}
+    with open(os.path.join(GOLDEN, "worked_example.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, rest = line.split("=", 1)
+            vals[key.strip()] = [float(t) for t in rest.split()]
+    return vals
+
+
+def pin_worked_example(O):
+    g = load_worked_example()
+    D = 4
+    # pool: one physical page (16 cells); page table maps logical page 0 to it
+    kc = np.zeros((16, D), np.int8)
+    vc = np.zeros((16, D), np.int8)
+    kc[2, 0], kc[7, 0], kc[9, 0] = 8, 0, -8
+    vc[2] = [1, 2, 3, 4]
+    vc[7] = [10, 0, -10, 0]
+    vc[9] = [-4, 4, -4, 4]
+    one = np.full(16, np.float16(1.0)).view(np.uint16)
+    half = np.full(16, np.float16(0.5)).view(np.uint16)
+    q = np.zeros((1, 1, 1, D), np.float32)
+    q[..., 0] = 2.0  # scores: (1/16) * 1 * 2 * {8, 0, -8} = {1, 0, -1}
+    x = types.SimpleNamespace(k_codes=kc, v_codes=vc, k_scales=one, v_scales=half,
+                              page_table=np.zeros((1, 1), np.int32),
+                              sel=np.array([[2, 7, 9]], np.int32), n_sel=np.array([3], np.int32),
+                              q=q, softmax_scale=1.0 / 16.0)
+    out, lse = _attend_flat(O, x)
+    _close(out[0, 0], np.array(g["out"]), 1e-15, 1e-15, "worked out")
+    _close(lse[0], np.array(g["lse"]), 1e-15, 0, "worked lse")
+
+
+def pin_merge_closed_form(O):
+    """Two partials: (acc a, m 0, l 1) and (acc b, m ln 3, l 1), plus an empty
+    one.  M = ln 3, L = 1/3 + 1 = 4/3, out = (a + 3b)/4, lse = ln 4."""
+    a = np.array([4.0, -8.0, 0.5])
+    b = np.array([0.0, 8.0, 2.5])
+    acc = np.zeros((1, 3, 1, 3))
+    acc[0, 0, 0], acc[0, 1, 0] = a, b
+    m = np.array([[[0.0], [math.log(3.0)], [-np.inf]]])
+    l = np.array([[[1.0], [1.0], [0.0]]])
+    out, lse = O.merge(acc, m, l)
+    _close(out[0, 0], (a + 3 * b) / 4, 1e-15, 1e-15, "merge out")
+    _close(lse[0, 0], math.log(4.0), 1e-15, 0, "merge lse")
+    out, lse = O.merge(np.zeros((1, 2, 1, 3)), np.full((1, 2, 1), -np.inf), np.zeros((1, 2, 1)))
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------- invariants
+def pin_empty_and_masked(O):
+    x = tiny(21, n_sel=12)
+    y = dataclasses.replace(x, n_sel=np.zeros(1, np.int32))
+    out, lse = _attend_flat(O, y)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+    pt = np.full_like(x.page_table, -1)
+    out, lse = _attend_flat(O, dataclasses.replace(x, page_table=pt))
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def pin_permutation(O):
+    x = tiny(22, n_sel=50, pool_cells=256, n_q=2)
+    rng = np.random.default_rng(5)
+    y = dataclasses.replace(x, sel=x.sel[:, rng.permutation(50)].copy())
+    a, b = _attend_flat(O, x), _attend_flat(O, y)
+    _close(b[0], a[0], 1e-12, 1e-15, "perm out")
+    _close(b[1], a[1], 1e-13, 0, "perm lse")
+
+
+def pin_chunking(O):
+    x = tiny(23, n_sel=67, pool_cells=256, n_q=2, heavy=True)
+    ref = _attend_flat(O, x)
+    for C in (1, 3, 64, 66, 67, 256):
+        acc, m, l = O.chunk_partials(x, C)
+        out, lse = O.merge(acc, m, l)
+        _close(out, ref[0], 1e-12, 1e-15, f"chunk {C} out")
+        _close(lse, ref[1], 1e-13, 0, f"chunk {C} lse")
+    # a partial over one chunk is the dense un-normalised result
+    acc, m, l = O.chunk_partials(x, 1000)
+    _close(acc[:, 0] / l[:, 0, :, None], ref[0], 1e-12, 1e-15, "single chunk")
+    _close(m[:, 0] + np.log(l[:, 0]), ref[1], 1e-13, 0, "single chunk lse")
+
+
+def pin_score_shift(O):
+    """Scores shifted by a constant through the inputs: every cell has the same
+    K scale and code 127 in dimension 0; adding delta to q[..., 0] shifts all
+    scores by softmax_scale * k_scale * 127 * delta.  Output unchanged, lse
+    shifted by that amount."""
+    x = tiny(24, n_sel=25, pool_cells=128, n_qheads=2, head_dim=8)
+    kc = x.k_codes.copy()
+    kc[:, 0] = 127
+    ks = np.full_like(x.k_scales, np.float16(0.25).view(np.uint16))
+    x = dataclasses.replace(x, k_codes=kc, k_scales=ks)
+    delta = 3.0
+    q2 = x.q.copy()
+    q2[..., 0] += np.float32(delta)
+    shift = (1.0 / 16.0) * 0.25 * 127 * (float(q2[0, 0, 0, 0]) - float(x.q[0, 0, 0, 0]))
+    y = dataclasses.replace(x, q=q2)
+    a, b = _attend_flat(O, x), _attend_flat(O, y)
+    _close(b[0], a[0], 1e-12, 1e-15, "shift out")
+    for r in range(a[1].shape[1]):
+        s_r = (1.0 / 16.0) * 0.25 * 127 * (float(q2[0].reshape(-1, 8)[r, 0])
+                                            - float(x.q[0].reshape(-1, 8)[r, 0]))
+        _close(b[1][0, r], a[1][0, r] + s_r, 1e-13, 0, "shift lse")
+    assert shift != 0
+
+
+def pin_relabel_pages(O):
+    """Moving physical pages and rewriting the table leaves results unchanged."""
+    x = tiny(25, n_sel=40, pool_cells=256, n_q=2)
+    n_pages = x.k_codes.shape[0] // 16
+    perm = np.random.default_rng(7).permutation(n_pages)  # new page p holds old page perm[p]
+    inv = np.argsort(perm)
+    def mv(a, w):
+        return np.ascontiguousarray(a.reshape(n_pages, 16, *a.shape[1:])[perm].reshape(a.shape))
+    y = dataclasses.replace(x, k_codes=mv(x.k_codes, 1), v_codes=mv(x.v_codes, 1),
+                            k_scales=mv(x.k_scales, 0), v_scales=mv(x.v_scales, 0),
+                            page_table=inv[x.page_table].astype(np.int32))
+    a, b = _attend_flat(O, x), _attend_flat(O, y)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def pin_mask_equals_delete(O):
+    x = tiny(26, n_sel=60, pool_cells=256)
+    lp = x.sel[0] // 16
+    victim = int(lp[10])
+    pt = x.page_table.copy()
+    pt[0, victim] = -1
+    masked = dataclasses.replace(x, page_table=pt)
+    keep = x.sel[0][lp != victim]
+    deleted = dataclasses.replace(x, sel=keep[None].copy(),
+                                  n_sel=np.array([keep.size], np.int32))
+    a, b = _attend_flat(O, masked), _attend_flat(O, deleted)
+    _close(a[0], b[0], 1e-13, 1e-16, "mask=delete out")
+    _close(a[1], b[1], 1e-14, 0, "mask=delete lse")
+
+
+def pin_double_v_scales(O):
+    x = tiny(27, n_sel=30, pool_cells=128, n_q=2)
+    vs2 = (f16(x.v_scales) * 2).astype(np.float16).view(np.uint16)
+    y = dataclasses.replace(x, v_scales=vs2)
+    a, b = _attend_flat(O, x), _attend_flat(O, y)
+    assert np.array_equal(b[0], 2 * a[0]) and np.array_equal(b[1], a[1])
+
+
+def pin_duplicates(O):
+    """An entry listed twice counts twice: [c, c] gives lse = s + ln 2 and the
+    same output as [c]."""
+    x = tiny(28, n_sel=1)
+    y = dataclasses.replace(x, sel=np.repeat(x.sel, 2, axis=1), n_sel=np.array([2], np.int32))
+    a, b = _attend_flat(O, x), _attend_flat(O, y)
+    _close(b[0], a[0], 1e-15, 0, "dup out")
+    _close(b[1], a[1] + math.log(2), 1e-14, 0, "dup lse")
+
+
+ALL_PINS = [pin_half_decode, pin_textbook, pin_gather_exhaustive, pin_one_cell, pin_two_cells,
+            pin_zero_query, pin_identical_keys, pin_worked_example, pin_merge_closed_form,
+            pin_empty_and_masked, pin_permutation, pin_chunking, pin_score_shift,
+            pin_relabel_pages, pin_mask_equals_delete, pin_double_v_scales, pin_duplicates]
