@@ -1,0 +1,170 @@
+"""Thin Python binding of libsda.so (include/sda.h), argument marshalling only.
+
+PyTorch provides device memory and the stream; every step of the attention
+runs in the library's HIP kernels.  If libsda.so is missing the calls raise;
+there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsda.so")
+
+SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_LAUNCH = 0, -1, -2, -3, -4
+PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN = 16, 256, 64, 64
+
+EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
+            "sda_status_string")
+
+
+class SdaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {library().sda_status_string(status).decode()}")
+
+
+class _Pool(C.Structure):
+    _fields_ = [("k_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_codes", C.c_void_p),
+                ("v_scales", C.c_void_p), ("n_phys_pages", C.c_int64), ("page_size", C.c_int32),
+                ("head_dim", C.c_int32)]
+
+
+_lib = None
+
+
+def library() -> C.CDLL:
+    """Load libsda.so (built by decode_attention_sparse_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m decode_attention_sparse_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        i32, i64, vp, f32, sz = C.c_int32, C.c_int64, C.c_void_p, C.c_float, C.c_size_t
+        lib.sda_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, C.POINTER(sz)]
+        lib.sda_workspace_bytes.restype = C.c_int
+        lib.sda_decode_attn_step.argtypes = [C.POINTER(_Pool), vp, i32, vp, i32, vp, i32, i32, f32,
+                                             i32, vp, vp, vp, vp, sz, vp]
+        lib.sda_decode_attn_step.restype = C.c_int
+        lib.sda_decode_attn_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, i64, vp, i32,
+                                              vp, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
+        lib.sda_decode_attn_batch.restype = C.c_int
+        lib.sda_status_string.argtypes = [C.c_int]
+        lib.sda_status_string.restype = C.c_char_p
+        _lib = lib
+    return _lib
+
+
+@dataclasses.dataclass
+class Pool:
+    """Device tensors of the INT8 pools: codes int8 [cells][256], scales
+    binary16 bit patterns (int16/uint16/float16 tensors) [cells]."""
+    k_codes: torch.Tensor
+    k_scales: torch.Tensor
+    v_codes: torch.Tensor
+    v_scales: torch.Tensor
+
+    @property
+    def n_phys_pages(self) -> int:
+        return self.k_codes.shape[0] // PAGE_SIZE
+
+    def c_struct(self) -> _Pool:
+        return _Pool(_ptr(self.k_codes), _ptr(self.k_scales), _ptr(self.v_codes),
+                     _ptr(self.v_scales), self.n_phys_pages, PAGE_SIZE,
+                     int(self.k_codes.shape[1]) if self.k_codes.dim() == 2 else 0)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libsda must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def workspace_bytes(n_inst: int, n_q: int, n_qheads: int, max_sel: int, chunk_cells: int,
+                    head_dim: int = HEAD_DIM) -> int:
+    out = C.c_size_t(0)
+    st = library().sda_workspace_bytes(n_inst, n_q, n_qheads, head_dim, max_sel, chunk_cells,
+                                       C.byref(out))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_workspace_bytes")
+    return int(out.value)
+
+
+def workspace(n_inst, n_q, n_qheads, max_sel, chunk_cells, device="cuda") -> torch.Tensor:
+    """A device buffer of the required size (torch allocates it)."""
+    nb = workspace_bytes(n_inst, n_q, n_qheads, max_sel, chunk_cells)
+    return torch.empty(max(nb, 256), dtype=torch.uint8, device=device)
+
+
+def partials(ws: torch.Tensor, n_inst, n_q, n_qheads, max_sel, chunk_cells):
+    """Views (acc, m, l) of the chunk partials inside a workspace, as the
+    header lays them out."""
+    R = n_q * n_qheads
+    nch = -(-max_sel // chunk_cells)
+    units = n_inst * nch * R
+    al = lambda x: (x + 255) // 256 * 256
+    f = ws.view(torch.float32) if ws.dtype != torch.float32 else ws
+    m_off = al(units * HEAD_DIM * 4) // 4
+    l_off = m_off + al(units * 4) // 4
+    acc = f[: units * HEAD_DIM].view(n_inst, nch, R, HEAD_DIM)
+    m = f[m_off: m_off + units].view(n_inst, nch, R)
+    l = f[l_off: l_off + units].view(n_inst, nch, R)
+    return acc, m, l
+
+
+def decode_attn_step(pool: Pool, page_table, sel, q, softmax_scale: float, chunk_cells: int,
+                     out, lse, gather_out=None, ws=None, stream=None, n_sel: int | None = None):
+    """One sequence: q [n_q][n_qheads][256] fp32; out like q; lse [n_q][n_qheads]."""
+    n_q, n_qheads = int(q.shape[0]), int(q.shape[1])
+    n = int(sel.numel()) if n_sel is None else int(n_sel)
+    if ws is None:
+        ws = workspace(1, n_q, n_qheads, n, chunk_cells, q.device)
+    ps = pool.c_struct()
+    st = library().sda_decode_attn_step(
+        C.byref(ps), _ptr(page_table), int(page_table.numel()), _ptr(sel), n, _ptr(q), n_q,
+        n_qheads, float(softmax_scale), int(chunk_cells), _ptr(out), _ptr(lse), _ptr(gather_out),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_decode_attn_step")
+    return ws
+
+
+def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softmax_scale: float,
+                      chunk_cells: int, out, lse, gather_out=None, ws=None, stream=None,
+                      n_logical_pages: int | None = None):
+    """Many instances: page_table [n_inst][pt_stride], sel [n_inst][sel_stride],
+    n_sel device int32 [n_inst], q [n_inst][n_q][n_qheads][256]."""
+    n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    if ws is None:
+        ws = workspace(n_inst, n_q, n_qheads, max_sel, chunk_cells, q.device)
+    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    ps = pool.c_struct()
+    st = library().sda_decode_attn_batch(
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.stride(0)), nlp, _ptr(sel),
+        int(sel.stride(0)), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
+        float(softmax_scale), int(chunk_cells), _ptr(out), _ptr(lse), _ptr(gather_out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_decode_attn_batch")
+    return ws
+
+
+def to_device(x, device="cuda"):
+    """Upload generated inputs (decode_attention_sparse_amd.inputs.Inputs):
+    returns (Pool, dict of device tensors)."""
+    t = lambda a: torch.from_numpy(a).to(device)
+    pool = Pool(t(x.k_codes), t(x.k_scales.view("int16")), t(x.v_codes), t(x.v_scales.view("int16")))
+    dev = dict(page_table=t(x.page_table), sel=t(x.sel), n_sel=t(x.n_sel), q=t(x.q))
+    return pool, dev

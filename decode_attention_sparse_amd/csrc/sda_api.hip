@@ -1,0 +1,156 @@
+// extern "C" entry points of libsda.so (declared in include/sda.h):
+// host-side validation, workspace layout, and the chunk + merge launches on
+// the caller's stream.  No allocation, no synchronisation, no global state.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/sda.h"
+#include "sda_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+struct Layout {
+    size_t acc_off, m_off, l_off, total;
+    int32_t n_chunks;
+};
+
+// Returns SDA_OK and the partials layout, or an error for bad geometry.
+int layout_of(int64_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim, int32_t max_sel,
+              int32_t chunk_cells, Layout *L) {
+    if (n_inst < 0 || n_q < 1 || n_qheads < 1 || max_sel < 0 || chunk_cells < 1)
+        return SDA_ERR_INVALID_ARG;
+    if (head_dim != SDA_HEAD_DIM) return SDA_ERR_UNSUPPORTED;
+    if ((int64_t)n_q * n_qheads > SDA_MAX_ROWS) return SDA_ERR_UNSUPPORTED;
+    if (chunk_cells % SDA_CHUNK_ALIGN) return SDA_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)n_q * n_qheads;
+    const int64_t n_chunks = (max_sel + (int64_t)chunk_cells - 1) / chunk_cells;
+    const size_t units = (size_t)n_inst * (size_t)n_chunks * (size_t)rows;
+    L->n_chunks = (int32_t)n_chunks;
+    L->acc_off = 0;
+    L->m_off = align_up(units * head_dim * sizeof(float));
+    L->l_off = L->m_off + align_up(units * sizeof(float));
+    L->total = L->l_off + align_up(units * sizeof(float));
+    if (units == 0) L->total = 0;
+    return SDA_OK;
+}
+
+int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
+        int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
+        const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
+        int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
+        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!pool) return SDA_ERR_INVALID_ARG;
+    if (pool->page_size != SDA_PAGE_SIZE || pool->head_dim != SDA_HEAD_DIM)
+        return SDA_ERR_UNSUPPORTED;
+    if (!pool->k_codes || !pool->v_codes || !pool->k_scales || !pool->v_scales)
+        return SDA_ERR_INVALID_ARG;
+    if (pool->n_phys_pages < 1 || pool->n_phys_pages > ((int64_t)1 << 27))
+        return SDA_ERR_INVALID_ARG;
+    if (!aligned(pool->k_codes, 16) || !aligned(pool->v_codes, 16) ||
+        !aligned(pool->k_scales, 2) || !aligned(pool->v_scales, 2))
+        return SDA_ERR_INVALID_ARG;
+    Layout L;
+    int st = layout_of(n_inst, n_q, n_qheads, pool->head_dim, max_sel, chunk_cells, &L);
+    if (st != SDA_OK) return st;
+    if (n_logical_pages < 0 || pt_stride < n_logical_pages || sel_stride < max_sel)
+        return SDA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale)) return SDA_ERR_INVALID_ARG;
+    if (n_inst == 0) return SDA_OK;
+    if (!q || !out || !lse || !aligned(q, 16) || !aligned(out, 4) || !aligned(lse, 4))
+        return SDA_ERR_INVALID_ARG;
+    if (n_logical_pages > 0 && !page_table) return SDA_ERR_INVALID_ARG;
+    if (max_sel > 0 && !sel) return SDA_ERR_INVALID_ARG;
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)))
+        return SDA_ERR_WORKSPACE;
+
+    sda::Params p;
+    memset(&p, 0, sizeof p);
+    p.k_codes = pool->k_codes;
+    p.k_scales = pool->k_scales;
+    p.v_codes = pool->v_codes;
+    p.v_scales = pool->v_scales;
+    p.n_phys_pages = pool->n_phys_pages;
+    p.page_table = page_table;
+    p.pt_stride = pt_stride;
+    p.n_logical_pages = n_logical_pages;
+    p.sel = sel;
+    p.sel_stride = sel_stride;
+    p.n_sel_dev = n_sel_dev;
+    p.n_sel_host = n_sel_host;
+    p.max_sel = max_sel;
+    p.q = q;
+    p.n_inst = n_inst;
+    p.n_rows = n_q * n_qheads;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.chunk = chunk_cells;
+    p.n_chunks = L.n_chunks;
+    char *ws = static_cast<char *>(workspace);
+    p.acc = L.total ? reinterpret_cast<float *>(ws + L.acc_off) : nullptr;
+    p.m = L.total ? reinterpret_cast<float *>(ws + L.m_off) : nullptr;
+    p.l = L.total ? reinterpret_cast<float *>(ws + L.l_off) : nullptr;
+    p.gather_out = gather_out;
+    p.out = out;
+    p.lse = lse;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // clear a stale error so it is not blamed on us
+    if (p.n_chunks > 0 && sda::launch_chunk(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
+    if (sda::launch_merge(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
+    return SDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim,
+                        int32_t max_sel, int32_t chunk_cells, size_t *bytes) {
+    if (!bytes) return SDA_ERR_INVALID_ARG;
+    Layout L;
+    int st = layout_of(n_inst, n_q, n_qheads, head_dim, max_sel, chunk_cells, &L);
+    if (st == SDA_OK) *bytes = L.total;
+    return st;
+}
+
+int sda_decode_attn_step(const sda_pool *pool, const int32_t *page_table,
+                         int32_t n_logical_pages, const int32_t *sel, int32_t n_sel,
+                         const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
+                         int32_t chunk_cells, float *out, float *lse, int32_t *gather_out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_sel < 0) return SDA_ERR_INVALID_ARG;
+    return run(pool, 1, page_table, n_logical_pages, n_logical_pages, sel, n_sel, nullptr,
+               n_sel, n_sel, q, n_q, n_qheads, softmax_scale, chunk_cells, out, lse, gather_out,
+               workspace, workspace_bytes, stream);
+}
+
+int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                          int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
+                          int64_t sel_stride, const int32_t *n_sel, int32_t max_sel,
+                          const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
+                          int32_t chunk_cells, float *out, float *lse, int32_t *gather_out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_inst > 0 && !n_sel) return SDA_ERR_INVALID_ARG;
+    return run(pool, n_inst, page_table, pt_stride, n_logical_pages, sel, sel_stride, n_sel, 0,
+               max_sel, q, n_q, n_qheads, softmax_scale, chunk_cells, out, lse, gather_out,
+               workspace, workspace_bytes, stream);
+}
+
+const char *sda_status_string(int status) {
+    switch (status) {
+        case SDA_OK: return "SDA_OK";
+        case SDA_ERR_INVALID_ARG: return "SDA_ERR_INVALID_ARG: invalid argument";
+        case SDA_ERR_UNSUPPORTED: return "SDA_ERR_UNSUPPORTED: unsupported geometry";
+        case SDA_ERR_WORKSPACE: return "SDA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case SDA_ERR_LAUNCH: return "SDA_ERR_LAUNCH: kernel launch failed";
+        default: return "unknown sda status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the HIP translation units of libsda.so.
+// Not part of the public ABI (include/sda.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sda {
+
+constexpr int kPage = 16;
+constexpr int kDim = 256;
+constexpr int kMaxRows = 64;
+
+// Everything one call needs on the device, already validated on the host.
+struct Params {
+    // pools (physical cell = page * 16 + slot)
+    const int8_t *k_codes;
+    const uint16_t *k_scales;
+    const int8_t *v_codes;
+    const uint16_t *v_scales;
+    int64_t n_phys_pages;
+    // per-instance inputs
+    const int32_t *page_table;
+    int64_t pt_stride;
+    int32_t n_logical_pages;
+    const int32_t *sel;
+    int64_t sel_stride;
+    const int32_t *n_sel_dev;  // device counts (batch) or nullptr (step)
+    int32_t n_sel_host;        // count used when n_sel_dev is nullptr
+    int32_t max_sel;
+    const float *q;            // [n_inst][n_rows][kDim]
+    int32_t n_inst;
+    int32_t n_rows;            // n_q * n_qheads
+    float scale_log2;          // softmax_scale * log2(e): scores in base-2 units
+    int32_t chunk;             // cells per chunk
+    int32_t n_chunks;          // ceil(max_sel / chunk)
+    // chunk partials (workspace)
+    float *acc;                // [n_inst][n_chunks][n_rows][kDim]
+    float *m;                  // [n_inst][n_chunks][n_rows], natural-log units
+    float *l;                  // [n_inst][n_chunks][n_rows]
+    // outputs
+    int32_t *gather_out;       // nullable [n_inst][sel_stride]
+    float *out;                // [n_inst][n_rows][kDim]
+    float *lse;                // [n_inst][n_rows]
+};
+
+// IEEE binary16 bit pattern -> float (exact).
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Number of selected entries instance i actually uses.
+__device__ __forceinline__ int count_of(const Params &p, int i) {
+    int n = p.n_sel_dev ? p.n_sel_dev[i] : p.n_sel_host;
+    n = n < 0 ? 0 : n;
+    return n > p.max_sel ? p.max_sel : n;
+}
+
+// Page-table gather of one selected logical cell: physical cell or -1.
+__device__ __forceinline__ int gather_cell(const Params &p, const int32_t *pt, int32_t c) {
+    if (c < 0) return -1;
+    const int lp = c >> 4;
+    if (lp >= p.n_logical_pages) return -1;
+    const int pg = pt[lp];
+    if (pg < 0 || (int64_t)pg >= p.n_phys_pages) return -1;
+    return (pg << 4) | (c & 15);
+}
+
+hipError_t launch_chunk(const Params &p, hipStream_t s);
+hipError_t launch_merge(const Params &p, hipStream_t s);
+
+}  // namespace sda

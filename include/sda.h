@@ -1,0 +1,155 @@
+/*
+ * sda.h -- C ABI of libsda.so: decode-time attention over a selected subset
+ * of KV cells held as INT8 K/V pools behind a page table, on MI355X (gfx950).
+ *
+ * What is computed (Strata PR #2220 page, the decode attention over the QSA
+ * selection and its "Kernel (chunk kernel + merge ...)" benchmark; Strata
+ * round-9 page, section "R9-gpu-11: four score cells per step in daily INT8
+ * attention"):
+ *
+ *   For every instance i (one sequence x one KV head), every query row
+ *   r = t * n_qheads + h (query position t, grouped query head h sharing the
+ *   KV head) and every selected list entry j < n_sel[i]:
+ *
+ *     gather    c = sel[i][j];  p = page_table[i][c / 16];
+ *               phys_j = p * 16 + c % 16, or -1 ("masked") when c is outside
+ *               [0, 16 * n_logical_pages) or p is outside [0, n_phys_pages)
+ *               (page id -1 is the documented way to mask a page)
+ *     score     s_j = softmax_scale * k_scale[phys_j] * sum_d q[r][d] * k_code[phys_j][d]
+ *     chunk     list positions [c*chunk_cells, (c+1)*chunk_cells) form chunk c;
+ *               its partial is m_c = max s_j, l_c = sum e^(s_j - m_c),
+ *               acc_c[d] = sum e^(s_j - m_c) * v_scale[phys_j] * v_code[phys_j][d]
+ *               over the chunk's unmasked cells (empty: m = -inf, l = 0, acc = 0)
+ *     merge     M = max m_c, L = sum l_c e^(m_c - M),
+ *               out[r][d] = sum acc_c[d] e^(m_c - M) / L,  lse[r] = M + ln L
+ *               (no unmasked cell: out = 0, lse = -inf)
+ *
+ *   Every query position of an instance attends to the instance's whole
+ *   selection (no causal mask between verify positions).  Duplicate list
+ *   entries count once each.
+ *
+ * Two entry points mirror the pages' step (one sequence) and batch (many
+ * instances) entry points; both run the same two kernels (chunk, then merge)
+ * on the caller's stream.
+ *
+ * Memory and threading contract (all entry points):
+ *   - Every array argument is a DEVICE pointer unless marked "host".  The
+ *     caller owns all memory; the library never allocates, frees, copies to
+ *     the host or synchronises, and keeps no state between calls, so calls
+ *     may be captured into a HIP graph and replayed.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     non-zero status means nothing was launched.  Unsupported geometry
+ *     returns SDA_ERR_UNSUPPORTED so that a caller can fall back.
+ *   - Launch failures reported by the runtime return SDA_ERR_LAUNCH.
+ *   - Device-side contents are trusted for shape (n_sel[i] is clamped to
+ *     [0, max_sel]); ids out of range are masked, never dereferenced.
+ *   - Calls on different streams that share a workspace race.
+ */
+#ifndef SDA_H
+#define SDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDA_PAGE_SIZE 16 /* cells per page (the only supported value) */
+#define SDA_HEAD_DIM 256 /* dims per head (the only supported value) */
+#define SDA_MAX_ROWS 64  /* n_q * n_qheads limit */
+#define SDA_CHUNK_ALIGN 64 /* chunk_cells must be a positive multiple of this */
+
+typedef enum {
+    SDA_OK = 0,
+    SDA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride/alignment */
+    SDA_ERR_UNSUPPORTED = -2, /* geometry this library does not implement */
+    SDA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
+    SDA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
+} sda_status;
+
+/* The INT8 pools, indexed by physical cell = physical page * 16 + slot.
+ *   k_codes, v_codes: int8 [n_phys_pages * 16][head_dim], row-major, 16-byte
+ *                     aligned; the dequantised value is code * scale.
+ *   k_scales, v_scales: IEEE binary16 bit patterns [n_phys_pages * 16], one
+ *                     scale per physical cell.
+ * n_phys_pages must be in [1, 2^27]. */
+typedef struct sda_pool {
+    const int8_t *k_codes;
+    const uint16_t *k_scales;
+    const int8_t *v_codes;
+    const uint16_t *v_scales;
+    int64_t n_phys_pages;
+    int32_t page_size; /* must be SDA_PAGE_SIZE */
+    int32_t head_dim;  /* must be SDA_HEAD_DIM */
+} sda_pool;
+
+/* Workspace needed by one call (host only, no device access).
+ * bytes (host out) = size of the chunk partials, laid out from the start of
+ * the workspace as
+ *     acc  float [n_inst][n_chunks][R][head_dim]
+ *     m    float [n_inst][n_chunks][R]   (natural-log units, -inf if empty)
+ *     l    float [n_inst][n_chunks][R]
+ * with R = n_q * n_qheads, n_chunks = ceil(max_sel / chunk_cells), and each
+ * of the three arrays starting at a 256-byte aligned offset (acc at 0, m at
+ * align256(sizeof acc), l at m + align256(sizeof m)).  After a call these
+ * hold the chunk partials of the chunks that instance actually has
+ * (c < ceil(n_sel[i] / chunk_cells)); other entries are unspecified.
+ * Returns SDA_OK, SDA_ERR_INVALID_ARG or SDA_ERR_UNSUPPORTED. */
+int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim,
+                        int32_t max_sel, int32_t chunk_cells, size_t *bytes);
+
+/* One sequence (one KV head), the pages' single-step entry point.
+ *   pool          host pointer to the pool descriptor
+ *   page_table    int32 [n_logical_pages] global physical page ids
+ *   sel           int32 [n_sel] selected logical cell ids (may be NULL if n_sel == 0)
+ *   n_sel         host, >= 0
+ *   q             float [n_q][n_qheads][head_dim], 16-byte aligned
+ *   n_q, n_qheads host; 1 <= n_q, 1 <= n_qheads, n_q * n_qheads <= SDA_MAX_ROWS
+ *   softmax_scale host, finite
+ *   chunk_cells   host, positive multiple of SDA_CHUNK_ALIGN
+ *   out           float [n_q][n_qheads][head_dim]
+ *   lse           float [n_q][n_qheads]
+ *   gather_out    nullable int32 [n_sel]: physical cell per entry, -1 if masked
+ *   workspace     device buffer of at least sda_workspace_bytes(1, ..., n_sel, ...)
+ *                 bytes, 256-byte aligned (may be NULL if that size is 0)
+ *   stream        hipStream_t (NULL = default stream)
+ */
+int sda_decode_attn_step(const sda_pool *pool, const int32_t *page_table,
+                         int32_t n_logical_pages, const int32_t *sel, int32_t n_sel,
+                         const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
+                         int32_t chunk_cells, float *out, float *lse, int32_t *gather_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Many independent (sequence, KV head) instances sharing one pool, the
+ * pages' batch entry point.
+ *   n_inst        host, >= 0 (0: nothing is launched)
+ *   page_table    int32 [n_inst][pt_stride]; the first n_logical_pages entries
+ *                 of each row are used (pt_stride >= n_logical_pages)
+ *   sel           int32 [n_inst][sel_stride] (sel_stride >= max_sel)
+ *   n_sel         DEVICE int32 [n_inst]: entries used per instance; read on the
+ *                 device so that a captured graph replays with new counts;
+ *                 clamped to [0, max_sel]
+ *   max_sel       host upper bound of n_sel[i]; sizes the grid and workspace
+ *   q             float [n_inst][n_q][n_qheads][head_dim]
+ *   out           float [n_inst][n_q][n_qheads][head_dim]
+ *   lse           float [n_inst][n_q][n_qheads]
+ *   gather_out    nullable int32 [n_inst][sel_stride]
+ *   other arguments as for sda_decode_attn_step, with the workspace sized by
+ *   sda_workspace_bytes(n_inst, n_q, n_qheads, head_dim, max_sel, chunk_cells).
+ */
+int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                          int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
+                          int64_t sel_stride, const int32_t *n_sel, int32_t max_sel,
+                          const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
+                          int32_t chunk_cells, float *out, float *lse, int32_t *gather_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *sda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDA_H */

@@ -1,0 +1,50 @@
+"""Helpers shared by the GPU tests: run the HIP path through the C ABI on
+generated inputs and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+# Tolerances: elementwise |gpu - oracle| <= atol + rtol * |oracle|.
+OUT_ATOL, OUT_RTOL = 1e-3, 1e-3
+LSE_ATOL, LSE_RTOL = 1e-4, 1e-4
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def assert_close(got, ref, atol, rtol, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    both_ninf = np.isneginf(got) & np.isneginf(ref)
+    diff = np.where(both_ninf, 0.0, np.abs(got - ref))
+    tol = atol + rtol * np.where(both_ninf, 0.0, np.abs(ref))
+    bad = ~(diff <= tol)
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, diff - tol, -np.inf)), bad.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst at "
+                             f"{idx}: got {got[idx]!r} ref {ref[idx]!r}; max|diff| {diff.max():.3e}")
+    return float(diff.max()) if diff.size else 0.0
+
+
+def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda"):
+    """Upload inputs and run sda_decode_attn_batch; returns numpy out, lse,
+    gather indices and the device workspace."""
+    import torch
+    from decode_attention_sparse_amd import api
+    if n_q is not None:
+        x = x.with_n_q(n_q)
+    chunk = chunk or x.chunk
+    pool, dev = api.to_device(x, device)
+    n_inst, nq, nh, D = x.q.shape
+    out = torch.full((n_inst, nq, nh, D), float("nan"), device=device)
+    lse = torch.full((n_inst, nq, nh), float("nan"), device=device)
+    g = torch.full(x.sel.shape, -7, dtype=torch.int32, device=device) if gather else None
+    max_sel = int(x.sel.shape[1])
+    ws = api.decode_attn_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel,
+                               dev["q"], x.softmax_scale, chunk, out, lse, gather_out=g)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)

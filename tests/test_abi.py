@@ -1,0 +1,158 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/sda.h declares, sizes the workspace as documented, and
+rejects bad arguments with the documented status before launching anything."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from decode_attention_sparse_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sda_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert set(api.EXPORTED) <= set(declared_functions())
+
+
+def test_library_exports_every_declared_symbol():
+    lib = api.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = set(re.findall(r"\bT (sda_\w+)", out))
+    assert set(declared_functions()) <= syms
+
+
+def test_header_compiles_as_c():
+    src = '#include "sda.h"\nint main(void){ sda_pool p; (void)p; return SDA_OK; }\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                        "-x", "c", "-", "-fsyntax-only"], input=src, text=True,
+                       capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    lib = api.library()
+    for st in (0, -1, -2, -3, -4, 7):
+        assert lib.sda_status_string(st)
+
+
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("n_inst,n_q,nh,max_sel,chunk", [
+    (1, 1, 12, 600, 256), (1, 4, 12, 2051, 256), (256, 4, 12, 2051, 1024),
+    (64, 2, 12, 16384, 512), (32, 4, 12, 131072, 1024), (3, 2, 5, 1, 64)])
+def test_workspace_layout(n_inst, n_q, nh, max_sel, chunk):
+    R = n_q * nh
+    nch = -(-max_sel // chunk)
+    units = n_inst * nch * R
+    expect = _al(units * 256 * 4) + 2 * _al(units * 4)
+    assert api.workspace_bytes(n_inst, n_q, nh, max_sel, chunk) == expect
+
+
+def test_workspace_monotone_and_zero():
+    assert api.workspace_bytes(1, 1, 12, 0, 256) == 0
+    prev = 0
+    for n in range(0, 3000, 97):
+        cur = api.workspace_bytes(2, 3, 12, n, 256)
+        assert cur >= prev
+        prev = cur
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 12, 256, 100, 256), 0),
+    ((1, 1, 12, 128, 100, 256), api.SDA_ERR_UNSUPPORTED),      # head_dim
+    ((1, 5, 13, 256, 100, 256), api.SDA_ERR_UNSUPPORTED),      # rows > 64
+    ((1, 1, 12, 256, 100, 100), api.SDA_ERR_UNSUPPORTED),      # chunk not multiple of 64
+    ((1, 0, 12, 256, 100, 256), api.SDA_ERR_INVALID_ARG),      # n_q
+    ((-1, 1, 12, 256, 100, 256), api.SDA_ERR_INVALID_ARG),
+    ((1, 1, 12, 256, -5, 256), api.SDA_ERR_INVALID_ARG),
+    ((1, 1, 12, 256, 100, 0), api.SDA_ERR_INVALID_ARG),
+])
+def test_workspace_status(args, status):
+    out = C.c_size_t(0)
+    assert api.library().sda_workspace_bytes(*args, C.byref(out)) == status
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: every case below fails validation first
+
+
+def _pool(**kw):
+    d = dict(k_codes=FAKE, k_scales=FAKE, v_codes=FAKE, v_scales=FAKE, n_phys_pages=16,
+             page_size=16, head_dim=256)
+    d.update(kw)
+    return api._Pool(**d)
+
+
+def _step(pool, **kw):
+    a = dict(page_table=FAKE, nlp=4, sel=FAKE, n_sel=10, q=FAKE, n_q=1, nh=12, scale=0.0625,
+             chunk=256, out=FAKE, lse=FAKE, gather=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return api.library().sda_decode_attn_step(
+        C.byref(pool) if pool is not None else None, a["page_table"], a["nlp"], a["sel"],
+        a["n_sel"], a["q"], a["n_q"], a["nh"], a["scale"], a["chunk"], a["out"], a["lse"],
+        a["gather"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("pool_kw,kw,status", [
+    ({}, dict(n_sel=-1), api.SDA_ERR_INVALID_ARG),
+    (dict(page_size=8), {}, api.SDA_ERR_UNSUPPORTED),
+    (dict(head_dim=128), {}, api.SDA_ERR_UNSUPPORTED),
+    (dict(k_codes=None), {}, api.SDA_ERR_INVALID_ARG),
+    (dict(v_scales=None), {}, api.SDA_ERR_INVALID_ARG),
+    (dict(k_codes=FAKE + 8), {}, api.SDA_ERR_INVALID_ARG),          # misaligned codes
+    (dict(n_phys_pages=0), {}, api.SDA_ERR_INVALID_ARG),
+    (dict(n_phys_pages=(1 << 27) + 1), {}, api.SDA_ERR_INVALID_ARG),
+    ({}, dict(n_q=5, nh=13), api.SDA_ERR_UNSUPPORTED),
+    ({}, dict(chunk=96), api.SDA_ERR_UNSUPPORTED),
+    ({}, dict(q=None), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(q=FAKE + 4), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(out=None), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(lse=None), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(sel=None), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(page_table=None), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(scale=float("nan")), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(ws=None), api.SDA_ERR_WORKSPACE),
+    ({}, dict(wsb=1024), api.SDA_ERR_WORKSPACE),
+    ({}, dict(ws=FAKE + 64), api.SDA_ERR_WORKSPACE),
+])
+def test_step_rejects_before_launch(pool_kw, kw, status):
+    assert _step(_pool(**pool_kw), **kw) == status
+
+
+def test_null_pool():
+    assert _step(None) == api.SDA_ERR_INVALID_ARG
+
+
+def test_batch_rejects_before_launch():
+    lib = api.library()
+    p = _pool()
+    def call(**kw):
+        a = dict(n_inst=2, pt=FAKE, pts=4, nlp=4, sel=FAKE, sels=10, nsel=FAKE, max_sel=10,
+                 q=FAKE, n_q=1, nh=12, scale=0.0625, chunk=256, out=FAKE, lse=FAKE, g=None,
+                 ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.sda_decode_attn_batch(C.byref(p), a["n_inst"], a["pt"], a["pts"], a["nlp"],
+                                         a["sel"], a["sels"], a["nsel"], a["max_sel"], a["q"],
+                                         a["n_q"], a["nh"], a["scale"], a["chunk"], a["out"],
+                                         a["lse"], a["g"], a["ws"], a["wsb"], None)
+    assert call(nsel=None) == api.SDA_ERR_INVALID_ARG
+    assert call(pts=3) == api.SDA_ERR_INVALID_ARG        # pt_stride < n_logical_pages
+    assert call(sels=9) == api.SDA_ERR_INVALID_ARG       # sel_stride < max_sel
+    assert call(max_sel=-1) == api.SDA_ERR_INVALID_ARG
+    assert call(n_inst=-1) == api.SDA_ERR_INVALID_ARG
+    assert call(wsb=100) == api.SDA_ERR_WORKSPACE
+    assert call(n_inst=0) == api.SDA_OK                  # nothing to do, nothing launched

@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances (elementwise, |gpu - oracle| <= atol + rtol*|oracle|): out 1e-3 /
+1e-3, per-head lse 1e-4 / 1e-4; gather indices bit-exact; -inf lse and zero
+output for instances with no unmasked cell.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_sparse_amd import inputs as gen
+from tests.gpu_util import (LSE_ATOL, LSE_RTOL, OUT_ATOL, OUT_RTOL, assert_close, run_batch,
+                            say)
+
+pytestmark = pytest.mark.gpu
+
+
+def check(x, out, lse, g=None, inst_ids=None, what=""):
+    ro, rl = oracle.attend(x, inst_ids)
+    sl = slice(None) if inst_ids is None else np.asarray(inst_ids)
+    e1 = assert_close(out[sl], ro, OUT_ATOL, OUT_RTOL, f"{what} out")
+    e2 = assert_close(lse[sl], rl, LSE_ATOL, LSE_RTOL, f"{what} lse")
+    if g is not None:
+        rg = oracle.gather(x)
+        valid = np.arange(x.sel.shape[1])[None, :] < x.n_sel[:, None]
+        assert np.array_equal(g[valid], rg[valid]), f"{what}: gather indices differ"
+    say(f"  {what}: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
+
+
+@pytest.mark.parametrize("n_q", [1])
+def test_config0_tiny_single_step(n_q):
+    say("case: config 0 (600 cells, 1 q), batch entry point")
+    x = gen.make(0)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what="cfg0")
+
+
+@pytest.mark.parametrize("n_q", [1, 2, 3, 4])
+def test_config1_pages_kernel_point(n_q):
+    say(f"case: config 1 (2,051 cells), n_q={n_q}")
+    x = gen.make(1).with_n_q(n_q)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what=f"cfg1 nq{n_q}")
+
+
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_step_entry_matches_batch(n_q):
+    """sda_decode_attn_step on one sequence equals the batch entry bit for bit."""
+    import torch
+    from decode_attention_sparse_amd import api
+    say(f"case: step entry, config 1, n_q={n_q}")
+    x = gen.make(1).with_n_q(n_q)
+    out_b, lse_b, g_b, _ = run_batch(x)
+    pool, dev = api.to_device(x)
+    out = torch.empty(x.q.shape[1:], device="cuda")
+    lse = torch.empty(x.q.shape[1:3], device="cuda")
+    g = torch.empty(x.sel.shape[1], dtype=torch.int32, device="cuda")
+    api.decode_attn_step(pool, dev["page_table"][0], dev["sel"][0], dev["q"][0], x.softmax_scale,
+                         x.chunk, out, lse, gather_out=g)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), out_b[0])
+    assert np.array_equal(lse.cpu().numpy(), lse_b[0])
+    assert np.array_equal(g.cpu().numpy(), g_b[0])
+
+
+@pytest.mark.parametrize("cfg,n_q", [(0, 1), (1, 4), (1, 2)])
+def test_chunk_partials(cfg, n_q):
+    """The partials (acc, m, l) left in the workspace against the oracle's."""
+    from decode_attention_sparse_amd import api
+    say(f"case: partials, config {cfg}, n_q={n_q}")
+    x = gen.make(cfg).with_n_q(n_q)
+    _, _, _, ws = run_batch(x)
+    acc, m, l = (t.cpu().numpy() for t in api.partials(ws, x.n_inst, n_q, x.n_qheads,
+                                                       x.sel.shape[1], x.chunk))
+    racc, rm, rl = oracle.chunk_partials(x, x.chunk)
+    nch = racc.shape[1]
+    assert_close(m, rm, LSE_ATOL, LSE_RTOL, "partial m")
+    assert_close(l, rl, 0, 1e-3, "partial l")
+    assert_close(acc / l[..., None], racc / rl[..., None], OUT_ATOL, OUT_RTOL, "partial acc/l")
+    assert nch == acc.shape[1]
+
+
+EDGE_COUNTS = [0, 1, 2, 3, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+@pytest.mark.parametrize("n_q", [1, 2, 3, 4])
+def test_edge_counts(n_q, chunk):
+    """The pages' 0/1/2/3/63/64/65 selected-cell cases plus chunk edges, one
+    instance per count in one batched call (device n_sel per instance)."""
+    say(f"case: edge counts {EDGE_COUNTS}, n_q={n_q}, chunk={chunk}")
+    k = len(EDGE_COUNTS)
+    x = gen.make(None, seed=77 + n_q, n_inst=k, n_q=n_q, pool_cells=1024, n_sel=257,
+                 sel="uniform", chunk=chunk)
+    x = dataclasses.replace(x, n_sel=np.array(EDGE_COUNTS, np.int32))
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what=f"edges nq{n_q} C{chunk}")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_masking():
+    """Page -1 masking, page ids past the pool, selected ids past the logical
+    range, and an instance whose every page is masked."""
+    say("case: masking")
+    x = gen.make(None, seed=5, n_inst=4, n_q=3, pool_cells=2048, n_sel=300, sel="uniform",
+                 chunk=128)
+    pt = x.page_table.copy()
+    sel = x.sel.copy()
+    pt[0, ::3] = -1
+    pt[1, 5:40] = -1
+    pt[1, 50] = x.n_phys_pages + 3
+    pt[2, :] = -1
+    sel[3, ::7] = 2048 + 11       # past the logical range
+    sel[3, 1] = -5
+    x = dataclasses.replace(x, page_table=pt, sel=sel)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what="masking")
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+    assert np.all(g[2] == -1) and g[3, 0] == -1 and g[3, 1] == -1
+
+
+def test_ragged_batch_and_unsorted():
+    """Per-instance counts below max_sel (read on the device), unsorted
+    selections and duplicate entries."""
+    say("case: ragged batch")
+    x = gen.make(None, seed=9, n_inst=6, n_q=4, pool_cells=4096, n_sel=700, sel="uniform",
+                 chunk=256)
+    rng = np.random.default_rng(3)
+    sel = x.sel.copy()
+    sel[1] = sel[1, rng.permutation(700)]
+    sel[2, 100:200] = sel[2, 0:100]  # duplicates
+    x = dataclasses.replace(x, sel=sel, n_sel=np.array([700, 511, 700, 1, 0, 257], np.int32))
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what="ragged")
+
+
+@pytest.mark.parametrize("cfg,ids", [(2, [0, 1, 97, 255]), (3, [0, 31, 63]), (4, [0, 31])])
+def test_full_size_configs_sampled(cfg, ids):
+    """The batched workloads at full size, in the launch configuration the
+    bench times; sampled instances against the oracle, every gather index
+    bit-exact."""
+    say(f"case: config {cfg} full size, oracle on instances {ids}")
+    x = gen.make(cfg)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, inst_ids=ids, what=f"cfg{cfg}")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def test_workspace_sentinel():
+    """Bytes past the contracted workspace size stay untouched."""
+    import torch
+    from decode_attention_sparse_amd import api
+    say("case: workspace sentinel")
+    x = gen.make(1).with_n_q(3)
+    pool, dev = api.to_device(x)
+    nb = api.workspace_bytes(1, 3, 12, 2051, 256)
+    ws = torch.full((nb + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 3, 12, 256), device="cuda")
+    lse = torch.empty((1, 3, 12), device="cuda")
+    api.decode_attn_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], 2051, dev["q"],
+                          x.softmax_scale, 256, out, lse, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.all(ws[nb:] == 0xA5).item()
+
+
+def test_graph_replay_changing_counts():
+    """The batch call captured in a HIP graph and replayed with new device
+    counts and query values; every replay equals the eager call bit for bit."""
+    import torch
+    from decode_attention_sparse_amd import api
+    say("case: graph replay")
+    x = gen.make(None, seed=11, n_inst=8, n_q=4, pool_cells=8192, n_sel=1500, sel="uniform",
+                 chunk=256)
+    pool, dev = api.to_device(x)
+    out = torch.empty(x.q.shape, device="cuda")
+    lse = torch.empty(x.q.shape[:3], device="cuda")
+    ws = api.workspace(8, 4, 12, 1500, 256)
+    args = lambda: (pool, dev["page_table"], dev["sel"], dev["n_sel"], 1500, dev["q"],
+                    x.softmax_scale, 256, out, lse)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.decode_attn_batch(*args(), ws=ws)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.decode_attn_batch(*args(), ws=ws)
+    rng = np.random.default_rng(0)
+    for rep in range(4):
+        counts = rng.integers(0, 1501, size=8).astype(np.int32)
+        counts[rep % 8] = 0
+        dev["n_sel"].copy_(torch.from_numpy(counts))
+        dev["q"].copy_(torch.from_numpy(rng.standard_normal(x.q.shape, dtype=np.float32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        g_out, g_lse = out.clone(), lse.clone()
+        api.decode_attn_batch(*args(), ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(g_out, out) and torch.equal(g_lse, lse), f"replay {rep}"
+        y = dataclasses.replace(x, n_sel=counts, q=dev["q"].cpu().numpy())
+        check(y, out.cpu().numpy(), lse.cpu().numpy(), what=f"replay {rep}")
