@@ -1,0 +1,329 @@
+#!/usr/bin/env python3
+"""Benchmark: selected-cell INT8 decode attention (chunk + merge) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-batched] [--no-cpu]
+
+Workload of the headline line: the pages' kernel point (Strata PR #2220,
+"Kernel (chunk kernel + merge, synthetic INT8 pools, permuted page table,
+200 calls)"): one sequence, one KV head, 12 query heads, head_dim 256,
+32,768-cell INT8 pool behind a permuted page table, 2,051 selected cells,
+chunk 256.  One step = four calls, one per query count 1, 2, 3, 4 (the
+page's table axis), each call the chunk pass then the merge pass, launched
+back to back on one stream.  Inputs are generated on the host, uploaded, and
+resident in HBM before the timed region.
+
+Printed: one JSON line.  value = selected cells per second over the step;
+roofline = the chunk kernel's algorithmic HBM bytes (520 B per selected cell,
+4 B per touched page-table entry, the fp32 queries) over its mean duration,
+timed with HIP events on the launch stream; cpu_baseline = the fp64 CPU
+oracle on the same workload; "batched" = the three batched workloads (256 x
+2,051 cells x 4 q, 64 x 16,384 x 2 q, 32 x 131,072 x 4 q) measured the same
+way with a cache flush between calls.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = ("selected KV cells/s and HBM GB/s (chunk+merge), µs/call at 2,051 cells "
+          "× 1–4 q")
+HBM_PEAK_GBS = 8000.0
+# chunk + merge on RTX 2080 Ti (sm_75), attn_chunk_q8_v3_kernel, 2,051 cells (Strata PR #2220)
+PAGES_V3_US = {1: 34.5, 2: 41.0, 3: 73.0, 4: 84.9}
+PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
+
+
+def algorithmic_bytes(x) -> int:
+    """Bytes the method must move for one chunk pass over inputs x: K and V
+    code rows (256 B each), K and V scales (2 B each) and the list entry (4 B)
+    per selected cell, 4 B per distinct page-table entry touched, and the
+    fp32 query rows."""
+    cells = int(np.sum(x.n_sel))
+    pages = 0
+    for i in range(x.sel.shape[0]):
+        s = x.sel[i, : x.n_sel[i]]
+        pages += int(np.unique(s >> 4).size)
+    q_bytes = int(np.prod(x.q.shape)) * 4
+    return cells * 520 + pages * 4 + q_bytes
+
+
+def out_bytes(x) -> int:
+    n_inst, n_q, nh, D = x.q.shape
+    return n_inst * n_q * nh * (D + 1) * 4
+
+
+class Case:
+    """One workload resident on the GPU, with its buffers and timing hooks."""
+
+    def __init__(self, x, chunk):
+        import torch
+        from decode_attention_sparse_amd import api
+        self.api, self.torch = api, torch
+        self.x, self.chunk = x, chunk
+        self.pool, self.dev = api.to_device(x)
+        n_inst, n_q, nh, D = x.q.shape
+        self.max_sel = int(x.sel.shape[1])
+        self.out = torch.empty((n_inst, n_q, nh, D), device="cuda")
+        self.lse = torch.empty((n_inst, n_q, nh), device="cuda")
+        self.ws = api.workspace(n_inst, n_q, nh, self.max_sel, chunk)
+        self.bytes = algorithmic_bytes(x)
+        self.cells = int(np.sum(x.n_sel))
+
+    def chunk_pass(self):
+        d = self.dev
+        self.api.chunk_batch(self.pool, d["page_table"], d["sel"], d["n_sel"], self.max_sel, d["q"],
+                             self.x.softmax_scale, self.chunk, self.ws)
+
+    def merge_pass(self):
+        self.api.merge_batch(self.dev["n_sel"], self.max_sel, self.chunk, self.ws, self.out,
+                             self.lse)
+
+
+def time_calls(cases, iters, flush=None):
+    """Eager calls: run every case `iters` times (chunk pass, merge pass), HIP
+    events on the launch stream around each kernel, an optional cache flush
+    before each call outside the events.  Returns per-case lists of
+    (chunk_ms, merge_ms)."""
+    import torch
+    evs = []
+    for _ in range(iters):
+        row = []
+        for c in cases:
+            if flush is not None:
+                flush()
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            c.chunk_pass()
+            e1.record()
+            c.merge_pass()
+            e2.record()
+            row.append((e0, e1, e2))
+        evs.append(row)
+    torch.cuda.synchronize()
+    res = [[] for _ in cases]
+    for row in evs:
+        for k, (e0, e1, e2) in enumerate(row):
+            res[k].append((e0.elapsed_time(e1), e1.elapsed_time(e2)))
+    return res
+
+
+def graph_of(fn, reps):
+    """Capture `reps` back-to-back calls of fn into one HIP graph, so that
+    short kernels run without host launch gaps."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps):
+    """Replay once untimed, then once between HIP events; ms per captured call."""
+    import torch
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def make_flush():
+    import torch
+    buf = torch.empty(768 << 20, dtype=torch.uint8, device="cuda")  # > L2 + MALL
+
+    def flush():
+        buf.fill_(1)
+    return flush
+
+
+def summarize(case, samples):
+    ch = np.array([s[0] for s in samples]) * 1e3  # us
+    mg = np.array([s[1] for s in samples]) * 1e3
+    tot = ch + mg
+    med = float(np.median(tot))
+    return {
+        "us_per_call_median": round(med, 3),
+        "us_per_call_p10": round(float(np.percentile(tot, 10)), 3),
+        "us_per_call_p90": round(float(np.percentile(tot, 90)), 3),
+        "chunk_us_mean": round(float(ch.mean()), 3),
+        "merge_us_mean": round(float(mg.mean()), 3),
+        "cells_per_s": round(case.cells / (med * 1e-6), 1),
+        "GBps_chunk_merge": round(case.bytes / (med * 1e-6) / 1e9, 1),
+        "GBps_chunk_kernel": round(case.bytes / (ch.mean() * 1e-6) / 1e9, 1),
+        "frac_hbm_peak_chunk_merge": round(case.bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def cpu_baseline(xs, budget_s):
+    """The fp64 oracle on the step's inputs, repeated for about budget_s."""
+    import oracle
+    cells, t0, reps = 0, time.perf_counter(), 0
+    while True:
+        for x in xs:
+            oracle.attend(x)
+            cells += int(np.sum(x.n_sel))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(cells / el, 1), "unit": "selected cells/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full steps of the headline workload (4 calls, n_q=1..4, "
+                      f"2,051 cells each) in {el:.1f} s, fp64 C, OpenMP over query rows"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--batched-iters", type=int, default=20)
+    ap.add_argument("--no-batched", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--chunk2", type=int, default=None,
+                    help="chunk size for the 256-instance batched workload")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print("bench.py measures one GPU: the path shards across GPUs without communication "
+              "(instances are independent); run with --gpus 1", file=sys.stderr)
+        return 2
+    import torch
+    from decode_attention_sparse_amd import api, inputs
+    api.library()
+    torch.cuda.init()
+    dev_name = torch.cuda.get_device_name(0)
+
+    # ---- headline workload: 2,051 cells, n_q = 1..4
+    base = inputs.make(1)
+    xs = [base.with_n_q(nq) for nq in (1, 2, 3, 4)]
+    cases = [Case(x, base.chunk) for x in xs]
+    time_calls(cases, a.warmup)  # W untimed eager steps
+
+    def step():
+        for c in cases:
+            c.chunk_pass()
+            c.merge_pass()
+
+    # the timed region: exactly K steps, captured into one graph and replayed
+    g_steps = graph_of(step, a.steps)
+    g_steps.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_steps.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / a.steps
+    del g_steps
+    # per-kernel means, each kernel alone in a graph of K launches
+    per_q = {}
+    chunk_us_sum, bytes_sum = 0.0, 0
+    for nq, c in zip((1, 2, 3, 4), cases):
+        g_c = graph_of(c.chunk_pass, a.steps)
+        ch_ms = time_graph(g_c, a.steps)
+        del g_c
+        g_m = graph_of(c.merge_pass, a.steps)
+        mg_ms = time_graph(g_m, a.steps)
+        del g_m
+        g_b = graph_of(lambda: (c.chunk_pass(), c.merge_pass()), a.steps)
+        both_ms = time_graph(g_b, a.steps)
+        del g_b
+        per_q[f"q{nq}"] = {
+            "us_per_call": round(both_ms * 1e3, 3),
+            "chunk_us": round(ch_ms * 1e3, 3), "merge_us": round(mg_ms * 1e3, 3),
+            "cells_per_s": round(c.cells / (both_ms * 1e-3), 1),
+            "GBps_chunk_merge": round(c.bytes / (both_ms * 1e-3) / 1e9, 1),
+            "pages_2080ti_v3_us": PAGES_V3_US[nq], "pages_2080ti_default_us": PAGES_DEFAULT_US[nq],
+        }
+        chunk_us_sum += ch_ms * 1e3
+        bytes_sum += c.bytes
+    cells_step = sum(c.cells for c in cases)
+    value = cells_step / (step_ms * 1e-3)
+    pages_step_us = sum(PAGES_V3_US.values())
+    achieved = bytes_sum / (chunk_us_sum * 1e-6) / 1e9
+    flush = make_flush()
+    cold = time_calls(cases, 20, flush=flush)
+    cold_us = {f"q{nq}": round(float(np.median([u[0] + u[1] for u in s])) * 1e3, 3)
+               for nq, s in zip((1, 2, 3, 4), cold)}
+    del cases
+    torch.cuda.empty_cache()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "selected cells/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (cells_step / (pages_step_us * 1e-6)), 3),
+        "dtype": "i8 K/V codes, i8 MFMA with digit-split fp32 operands, fp32 softmax",
+        "data": "synthetic (seeded PCG64; int8 codes uniform [-127,127], fp16 scales U[0.002,0.02], q N(0,1))",
+        "config": {"workload": base.workload, "instances": 1, "n_qheads": 12, "head_dim": 256,
+                   "queries": [1, 2, 3, 4], "selected_cells": 2051, "pool_cells": 32768,
+                   "chunk": base.chunk, "calls_per_step": 4, "device": dev_name,
+                   "timing": "K steps captured in one HIP graph, HIP events around its replay; back-to-back calls with warm caches, as the pages' 200-call loop"},
+        "roofline": {"bound": "hbm", "kernel": "chunk pass", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "bytes_per_step": bytes_sum, "chunk_us_per_step": round(chunk_us_sum, 3)},
+        "per_query_count": per_q,
+        "cold_us_per_call_median": cold_us,
+        "cold_note": "eager calls with a 768 MB cache flush before each, HIP events around the kernels",
+        "vs_baseline_ref": "pages' v3 kernel on RTX 2080 Ti, sum over q=1..4 of chunk+merge us (context, other hardware)",
+        "wall_s_timed_region": round(wall, 3),
+    }
+
+    # ---- batched workloads (HBM-scale), cold caches between calls
+    if not a.no_batched:
+        batched = {}
+        for cfg in (2, 3, 4):
+            kw = {}
+            if cfg == 2 and a.chunk2:
+                kw["chunk"] = a.chunk2
+            x = inputs.make(cfg, **kw)
+            c = Case(x, x.chunk)
+            time_calls([c], 3)
+            s = time_calls([c], a.batched_iters, flush=flush)[0]
+            d = summarize(c, s)
+            d.update({"instances": x.n_inst, "n_q": x.n_q, "selected_cells_per_instance":
+                      int(x.sel.shape[1]), "chunk": x.chunk,
+                      "bytes_algorithmic": c.bytes, "partials_bytes_written":
+                      int(x.n_inst * -(-x.sel.shape[1] // x.chunk) * x.n_q * 12 * 258 * 4)})
+            batched[x.workload] = d
+            print(f"# {x.workload}: {d['us_per_call_median']} us/call, "
+                  f"{d['GBps_chunk_merge']} GB/s ({d['frac_hbm_peak_chunk_merge']*100:.1f}% of HBM peak)",
+                  file=sys.stderr, flush=True)
+            del c, x
+            torch.cuda.empty_cache()
+        result["batched"] = batched
+
+    if not a.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(xs, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

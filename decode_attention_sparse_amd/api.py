@@ -19,7 +19,7 @@ SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_LAU
 PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN = 16, 256, 64, 64
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
-            "sda_status_string")
+            "sda_chunk_batch", "sda_merge_batch", "sda_status_string")
 
 
 class SdaError(RuntimeError):
@@ -53,6 +53,11 @@ def library() -> C.CDLL:
         lib.sda_decode_attn_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, i64, vp, i32,
                                               vp, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
         lib.sda_decode_attn_batch.restype = C.c_int
+        lib.sda_chunk_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, i64, vp, i32, vp,
+                                        i32, i32, f32, i32, vp, vp, sz, vp]
+        lib.sda_chunk_batch.restype = C.c_int
+        lib.sda_merge_batch.argtypes = [i32, i32, i32, vp, i32, i32, vp, sz, vp, vp, vp]
+        lib.sda_merge_batch.restype = C.c_int
         lib.sda_status_string.argtypes = [C.c_int]
         lib.sda_status_string.restype = C.c_char_p
         _lib = lib
@@ -159,6 +164,30 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
     if st != SDA_OK:
         raise SdaError(st, "sda_decode_attn_batch")
     return ws
+
+
+def chunk_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softmax_scale: float,
+                chunk_cells: int, ws, gather_out=None, stream=None):
+    """Chunk pass only: partials into ws (see partials())."""
+    n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    ps = pool.c_struct()
+    st = library().sda_chunk_batch(
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.stride(0)), int(page_table.shape[1]),
+        _ptr(sel), int(sel.stride(0)), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
+        float(softmax_scale), int(chunk_cells), _ptr(gather_out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_chunk_batch")
+
+
+def merge_batch(n_sel, max_sel: int, chunk_cells: int, ws, out, lse, stream=None):
+    """Merge pass only: partials in ws -> out [n_inst][n_q][n_qheads][256], lse."""
+    n_inst, n_q, n_qheads = int(out.shape[0]), int(out.shape[1]), int(out.shape[2])
+    st = library().sda_merge_batch(n_inst, n_q, n_qheads, _ptr(n_sel), int(max_sel),
+                                   int(chunk_cells), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _ptr(out), _ptr(lse), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_merge_batch")
 
 
 def to_device(x, device="cuda"):

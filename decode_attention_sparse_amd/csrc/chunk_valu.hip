@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(Params p) {
 
 }  // namespace
 
-hipError_t launch_chunk(const Params &p, hipStream_t s) {
+hipError_t launch_chunk_valu(const Params &p, hipStream_t s) {
     dim3 grid(p.n_chunks, p.n_inst), block(kThreads);
     if (p.n_rows <= 16)
         chunk_valu_kernel<16><<<grid, block, 0, s>>>(p);

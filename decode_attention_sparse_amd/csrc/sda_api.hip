@@ -41,11 +41,14 @@ int layout_of(int64_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim, i
     return SDA_OK;
 }
 
+enum Passes { kChunk = 1, kMerge = 2, kBoth = 3 };
+
 int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
         int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
         const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
         int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
-        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream) {
+        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream,
+        int passes = kBoth) {
     if (!pool) return SDA_ERR_INVALID_ARG;
     if (pool->page_size != SDA_PAGE_SIZE || pool->head_dim != SDA_HEAD_DIM)
         return SDA_ERR_UNSUPPORTED;
@@ -63,7 +66,8 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
         return SDA_ERR_INVALID_ARG;
     if (!isfinite(softmax_scale)) return SDA_ERR_INVALID_ARG;
     if (n_inst == 0) return SDA_OK;
-    if (!q || !out || !lse || !aligned(q, 16) || !aligned(out, 4) || !aligned(lse, 4))
+    if (!q || !aligned(q, 16)) return SDA_ERR_INVALID_ARG;
+    if ((passes & kMerge) && (!out || !lse || !aligned(out, 4) || !aligned(lse, 4)))
         return SDA_ERR_INVALID_ARG;
     if (n_logical_pages > 0 && !page_table) return SDA_ERR_INVALID_ARG;
     if (max_sel > 0 && !sel) return SDA_ERR_INVALID_ARG;
@@ -101,8 +105,9 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so it is not blamed on us
-    if (p.n_chunks > 0 && sda::launch_chunk(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
-    if (sda::launch_merge(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
+    if ((passes & kChunk) && p.n_chunks > 0 && sda::launch_chunk(p, s) != hipSuccess)
+        return SDA_ERR_LAUNCH;
+    if ((passes & kMerge) && sda::launch_merge(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
     return SDA_OK;
 }
 
@@ -140,6 +145,46 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
     return run(pool, n_inst, page_table, pt_stride, n_logical_pages, sel, sel_stride, n_sel, 0,
                max_sel, q, n_q, n_qheads, softmax_scale, chunk_cells, out, lse, gather_out,
                workspace, workspace_bytes, stream);
+}
+
+int sda_chunk_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                    int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
+                    int64_t sel_stride, const int32_t *n_sel, int32_t max_sel, const float *q,
+                    int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells,
+                    int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_inst > 0 && !n_sel) return SDA_ERR_INVALID_ARG;
+    return run(pool, n_inst, page_table, pt_stride, n_logical_pages, sel, sel_stride, n_sel, 0,
+               max_sel, q, n_q, n_qheads, softmax_scale, chunk_cells, nullptr, nullptr,
+               gather_out, workspace, workspace_bytes, stream, kChunk);
+}
+
+int sda_merge_batch(int32_t n_inst, int32_t n_q, int32_t n_qheads, const int32_t *n_sel,
+                    int32_t max_sel, int32_t chunk_cells, const void *workspace,
+                    size_t workspace_bytes, float *out, float *lse, void *stream) {
+    Layout L;
+    int st = layout_of(n_inst, n_q, n_qheads, SDA_HEAD_DIM, max_sel, chunk_cells, &L);
+    if (st != SDA_OK) return st;
+    if (n_inst == 0) return SDA_OK;
+    if (!n_sel || !out || !lse || !aligned(out, 4) || !aligned(lse, 4)) return SDA_ERR_INVALID_ARG;
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)))
+        return SDA_ERR_WORKSPACE;
+    sda::Params p;
+    memset(&p, 0, sizeof p);
+    p.n_sel_dev = n_sel;
+    p.max_sel = max_sel;
+    p.n_inst = n_inst;
+    p.n_rows = n_q * n_qheads;
+    p.chunk = chunk_cells;
+    p.n_chunks = L.n_chunks;
+    char *ws = static_cast<char *>(const_cast<void *>(workspace));
+    p.acc = L.total ? reinterpret_cast<float *>(ws + L.acc_off) : nullptr;
+    p.m = L.total ? reinterpret_cast<float *>(ws + L.m_off) : nullptr;
+    p.l = L.total ? reinterpret_cast<float *>(ws + L.l_off) : nullptr;
+    p.out = out;
+    p.lse = lse;
+    (void)hipGetLastError();
+    if (sda::launch_merge(p, static_cast<hipStream_t>(stream)) != hipSuccess) return SDA_ERR_LAUNCH;
+    return SDA_OK;
 }
 
 const char *sda_status_string(int status) {

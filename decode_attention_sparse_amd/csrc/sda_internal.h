@@ -67,6 +67,7 @@ __device__ __forceinline__ int gather_cell(const Params &p, const int32_t *pt, i
 }
 
 hipError_t launch_chunk(const Params &p, hipStream_t s);
+hipError_t launch_chunk_valu(const Params &p, hipStream_t s);
 hipError_t launch_merge(const Params &p, hipStream_t s);
 
 }  // namespace sda

@@ -145,6 +145,33 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
                           int32_t chunk_cells, float *out, float *lse, int32_t *gather_out,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* The two passes of sda_decode_attn_batch, callable on their own.
+ *
+ * sda_chunk_batch runs only the chunk pass: same arguments and validation as
+ * sda_decode_attn_batch without out/lse; it leaves the chunk partials in the
+ * workspace (layout under sda_workspace_bytes) for each instance's first
+ * ceil(n_sel[i] / chunk_cells) chunks.  Partials from several sources can be
+ * combined by any log-sum-exp merge; this is also the unit one would shard
+ * across devices for a single very long selection.
+ *
+ * sda_merge_batch runs only the merge pass over partials laid out as
+ * sda_workspace_bytes(n_inst, n_q, n_qheads, SDA_HEAD_DIM, max_sel,
+ * chunk_cells) describes: n_sel (device, [n_inst]) gives each instance's
+ * chunk count as above; out float [n_inst][n_q][n_qheads][head_dim],
+ * lse float [n_inst][n_q][n_qheads].
+ *
+ * Running sda_chunk_batch then sda_merge_batch on one stream gives exactly
+ * the result of sda_decode_attn_batch. */
+int sda_chunk_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                    int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
+                    int64_t sel_stride, const int32_t *n_sel, int32_t max_sel, const float *q,
+                    int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells,
+                    int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream);
+
+int sda_merge_batch(int32_t n_inst, int32_t n_q, int32_t n_qheads, const int32_t *n_sel,
+                    int32_t max_sel, int32_t chunk_cells, const void *workspace,
+                    size_t workspace_bytes, float *out, float *lse, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *sda_status_string(int status);
 

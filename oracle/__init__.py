@@ -49,6 +49,8 @@ def _load():
     if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
     lib = C.CDLL(_LIB)
+    lib.oracle_threads.restype = C.c_int
+    lib.oracle_threads.argtypes = []
     lib.oracle_half_to_double.restype = C.c_double
     lib.oracle_half_to_double.argtypes = [C.c_uint16]
     lib.oracle_gather.restype = None
@@ -66,6 +68,11 @@ def _load():
                                  _f64p]
     _lib = lib
     return lib
+
+
+def threads() -> int:
+    """Host threads the oracle's parallel loops use."""
+    return int(_load().oracle_threads())
 
 
 def half_to_double(bits: np.ndarray) -> np.ndarray:

@@ -49,7 +49,20 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define ORACLE_PAGE 16
+
+/* Host threads the parallel loops below may use. */
+int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
  * 5 exponent bits with bias 15, 10 fraction bits; exponent 0 encodes
