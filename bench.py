@@ -197,6 +197,9 @@ def main(argv=None):
     ap.add_argument("--no-batched", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--only-batched", action="store_true",
+                    help="skip the headline workload (for profiling the batched kernels)")
+    ap.add_argument("--configs", default="2,3,4", help="batched workloads to run")
     ap.add_argument("--chunk2", type=int, default=None,
                     help="chunk size for the 256-instance batched workload")
     a = ap.parse_args(argv)
@@ -209,6 +212,19 @@ def main(argv=None):
     api.library()
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
+
+    if a.only_batched:
+        flush = make_flush()
+        for cfg in [int(v) for v in a.configs.split(",") if v]:
+            kw = {"chunk": a.chunk2} if (cfg == 2 and a.chunk2) else {}
+            x = inputs.make(cfg, **kw)
+            c = Case(x, x.chunk)
+            time_calls([c], 3)
+            d = summarize(c, time_calls([c], a.batched_iters, flush=flush)[0])
+            print(json.dumps({"workload": x.workload, "chunk": x.chunk, **d}), flush=True)
+            del c, x
+            torch.cuda.empty_cache()
+        return 0
 
     # ---- headline workload: 2,051 cells, n_q = 1..4
     base = inputs.make(1)
@@ -298,7 +314,7 @@ def main(argv=None):
     # ---- batched workloads (HBM-scale), cold caches between calls
     if not a.no_batched:
         batched = {}
-        for cfg in (2, 3, 4):
+        for cfg in [int(v) for v in a.configs.split(",") if v]:
             kw = {}
             if cfg == 2 and a.chunk2:
                 kw["chunk"] = a.chunk2

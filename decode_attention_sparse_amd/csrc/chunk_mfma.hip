@@ -7,34 +7,47 @@
 // cell-major probabilities) are prior art; this kernel is laid out for
 // CDNA4 wave64 matrix cores instead.
 //
-// Workgroup = one (chunk, instance), RB = ceil(rows / 16) waves; wave w owns
-// query rows [16w, 16w + 16) for the whole chunk, so every softmax statistic
-// of a row lives in one wave.  Cells are processed in tiles of 64.
+// Workgroup = one (instance, chunk) with RB + 1 waves: compute wave w < RB =
+// ceil(rows / 16) owns query rows [16w, 16w + 16) for the whole chunk, so
+// every softmax statistic of a row lives in one wave; the last wave is the
+// producer: it runs the gather and stages all code rows (the compute waves
+// issue no global loads and hold no staging registers).  Cells are processed
+// in tiles of 64.
 //
 // Exactness of the contractions.  The INT8 codes are used as they are; the
 // fp32 operands are split into int8 digits so that the int8 MFMA (exact
 // int32 accumulation) reproduces fp32-accurate products:
-//   QK  q_r[d] = sigma_r * (a + b/2^8 + c/2^16), sigma_r = max|q_r| / 127,
-//       a in [-127,127], b, c in [-128,127] (round-to-nearest digits with
-//       carry); S = sigma_r * ((2^8 A + B) / 2^8 + C / 2^16) where A, B, C
-//       are the exact integer dot products of the digits with the K codes
-//       (2^8 A + B is accumulated in one int32 register: the A products are
-//       shifted left by 8 between the two MFMA groups; |2^8 A + B| < 2^30).
-//   PV  p'_rj = p_rj * v_scale_j in [0, max], split per tile and row as
-//       tau * (a + b/2^8), tau = tile max / 127, a in [0,127], b in
-//       [-128,127]; the tile's (2^8 A + B) int32 sums are converted once and
-//       folded into the fp32 accumulator with the online-softmax correction.
-// The q split keeps 23 significant bits (fp32-level); the probability split
-// keeps 15 bits relative to the tile's largest weighted probability.
+//   QK  q[d] = sigma * (a + b/2^8 + c/2^16), sigma = max |q| over the wave's
+//       16 rows / 127, a in [-127,127], b, c in [-128,127] (the nearest
+//       multiple of 2^-16 written in balanced base-256 digits).  S = sigma *
+//       ((2^8 A + B) / 2^8 + C / 2^16) with A, B, C the exact integer dot
+//       products of the digits with the K codes, each accumulated by its own
+//       MFMA chain; 2^8 A + B is formed in int32 (|.| < 2^30) before the
+//       conversion to fp32.  Score errors are at fp32 level relative to the
+//       wave's largest score.
+//   PV  x = p * v_scale / tau in [0, 127], tau = 2^(tile max - running max)
+//       * (tile max v_scale) / 127 per row and tile; X = rint(256 x) in
+//       [0, 32512] is written as 2^8 hi + lo (hi in [0,127], lo in
+//       [-128,127]); the tile's sum over cells of X * v_code (two MFMAs,
+//       combined as 2^8 HI + LO) is exact in int32 and folded into the fp32
+//       accumulator once per tile.  The probability split keeps 15 bits
+//       relative to the tile's largest weighted probability.
 //
-// Data movement.  Each tile's 64 K rows and 64 V rows (256 B each) go from
-// HBM straight into LDS with global_load_lds (16 B per lane, no VGPR hop),
-// double-buffered so that tile t+1 is in flight while tile t computes.  K
-// rows are read back with ds_read_b128 as the A operand of S^T = K Q^T; V
-// rows are read back transposed with ds_read_b64_tr_b8 as the A operand of
-// O^T = V^T P^T.  16-byte chunks are XOR-swizzled per row to spread banks.
-// The page-table gather (selected id -> physical cell) and the scale loads
-// run once per segment of up to 512 cells into LDS.
+// Pipeline.  Iteration t of the tile loop computes the scores of tile t+1
+// while it runs the softmax and the V accumulation of tile t, so matrix-core
+// and vector work of neighbouring tiles interleave within a wave.  Loads run
+// ahead of use: selected ids of tile t+4, page-table entries of tile t+3,
+// scales and K rows of tile t+2, V rows of tile t+1.  Code rows (256 B) are
+// loaded into VGPRs with 16-byte loads (16 lanes per row) and written to LDS
+// rows padded to 272 B, double-buffered; the padding and a row permutation
+// make the LDS reads conflict-free with immediate offsets.  K rows feed
+// S^T = K Q^T through ds_read_b128; V rows are read transposed with
+// ds_read_b64_tr_b8 to feed O^T = V^T P^T.
+//
+// Online-softmax rescaling without a branch: the accumulator is kept in a
+// frame scaled by F = product of the per-tile corrections (O = F * O_frame);
+// each tile adds its contribution times 1/F, and the frame is renormalised
+// (a wave-uniform, rare branch) only when F drops below 2^-64.
 #include "sda_internal.h"
 
 namespace sda {
@@ -45,99 +58,194 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kTile = 64;      // cells per tile (the K extent of one PV MFMA)
-constexpr int kSeg = 512;      // cells gathered into LDS at a time
-constexpr int kRow = kDim;     // bytes per code row
-
-// physical 16-byte chunk of logical chunk x in code row c of a tile
-__device__ __forceinline__ int swz_k(int c) { return c & 7; }
-__device__ __forceinline__ int swz_v(int c) { return (c & 3) | ((c >> 2) & 4); }
+constexpr int kTile = 64;            // cells per tile (the K extent of one PV MFMA)
+constexpr int kStride = kDim + 16;   // LDS bytes per code row (padded)
+constexpr int kBuf = kTile * kStride;
+constexpr int kRows = kTile / 4;     // 1 KB staging loads per tile and pool (4 rows each)
+constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^22) to integers in the low bits
+constexpr float kFarBelow = 64.f;    // tiles 2^64 below the running max carry no weight
+constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max4(float x) {  // over lanes l, l^16, l^32, l^48
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+// Reductions over the four lanes l, l^16, l^32, l^48 (one query row), with the
+// gfx950 lane swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float max4(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ float wave_sum4(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+__device__ __forceinline__ float sum4(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Stage tile `t` (segment-relative) of K and V code rows into LDS buffer
-// `b`.  32 instructions of 1 KB (4 rows each), dealt round-robin to waves.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Maximum over all 64 lanes: quad permutes, half-row and row mirrors (DPP),
+// then the 16- and 32-lane swaps.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<0xb1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4e>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return max4(x);
+}
+
+// LDS row of the QK operand index 16*cb + l: a permutation within the tile
+// chosen so that the K reads (8 lanes) and the transposed V reads (8 rows per
+// 16 lanes) each touch 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (4 * (cb & 1))); }
+
 template <int RB>
-__device__ __forceinline__ void issue_tile(const Params &p, const int *phys_s, int t,
-                                           int8_t *kb, int8_t *vb, int wave,
-                                           int lane) {
-#pragma unroll
-    for (int it = 0; it < (32 + RB - 1) / RB; ++it) {
-        const int k = wave + it * RB;
-        if (k >= 32) break;
-        const int kk = k & 15;
-        const int row = 4 * kk + (lane >> 4);
-        int ph = phys_s[t * kTile + row];
-        ph = ph < 0 ? 0 : ph;  // masked: any valid row, its score is -inf
-        const bool is_v = k >= 16;
-        const int lc = (lane & 15) ^ (is_v ? swz_v(row) : swz_k(row));
-        const int8_t *src = (is_v ? p.v_codes : p.k_codes) + (int64_t)ph * kRow + lc * 16;
-        int8_t *dst = (is_v ? vb : kb) + kk * 1024;
-        __builtin_amdgcn_global_load_lds((const void *)src, (void LDS_AS *)(dst), 16, 0, 0);
-    }
-}
-
-template <int RB>
-__global__ __launch_bounds__(64 * RB) void chunk_mfma_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) int8_t kbuf[2][kTile * kRow];
-    __shared__ __attribute__((aligned(16))) int8_t vbuf[2][kTile * kRow];
-    __shared__ __attribute__((aligned(16))) int phys_s[kSeg];
-    __shared__ __attribute__((aligned(16))) float ks_s[kSeg];
-    __shared__ __attribute__((aligned(16))) float vs_s[kSeg];
-    __shared__ __attribute__((aligned(16))) float bias_s[kSeg];
+__global__ __launch_bounds__(64 * (RB + 1)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void chunk_mfma_kernel(Params p) {
+    constexpr int kProducer = RB;  // the last wave
+    __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kBuf];
+    __shared__ __attribute__((aligned(1024))) int8_t vbuf[2][kBuf];
+    __shared__ __attribute__((aligned(16))) int phys_s[4][kTile];
+    __shared__ __attribute__((aligned(16))) float ks_s[4][kTile];
+    __shared__ __attribute__((aligned(16))) float vs_s[4][kTile];
+    __shared__ __attribute__((aligned(16))) float bias_s[4][kTile];
+    __shared__ float vmax_s[4];
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;     // lane group: k-set of the MFMA operands
-    const int l16 = lane & 15;   // row (of this wave's 16) owned by this lane
-    const int c = blockIdx.x;
-    const int i = blockIdx.y;
+    const int g = lane >> 4;    // lane group: k-set of the MFMA operands
+    const int l16 = lane & 15;  // this lane's row within the wave's 16 rows
+    const int i = blockIdx.x;   // instance (fastest: full chunks are dispatched first)
+    const int c = blockIdx.y;   // chunk
     const int n = count_of(p, i);
     const int j_begin = c * p.chunk;
     if (j_begin >= n) return;  // this instance has fewer chunks
     const int j_end = min(j_begin + p.chunk, n);
+    const int n_tiles = (j_end - j_begin + kTile - 1) / kTile;
     const int R = p.n_rows;
-    const int row = wave * 16 + l16;
-    const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
-    const int32_t *sel = p.sel + (int64_t)i * p.sel_stride;
 
-    // ---- query digits: B operands of S^T = K Q^T for rows 16*wave + l16,
-    // dims 64s + 16g + e (byte e of slab s)
-    v4i qa[4], qb[4], qc[4];
-    float coef_q;  // sigma_r * scale_log2 / 2^8
-    {
-        float qv[4][16];
-        float mx = 0.f;
+    // scale slots read before their first write hold finite values
+    for (int e = threadIdx.x; e < 4 * kTile; e += 64 * (RB + 1)) {
+        (&ks_s[0][0])[e] = 0.f;
+        (&vs_s[0][0])[e] = 0.f;
+        (&bias_s[0][0])[e] = -INFINITY;
+    }
+    if (threadIdx.x < 4) vmax_s[threadIdx.x] = 0.f;
+    __syncthreads();
+
+    // Both roles run n_tiles + 4 iterations with one barrier each.  Iteration
+    // t: the producer loads the selected ids of tile t+4, the page-table
+    // entries of tile t+3, the scales and K rows of tile t+2 and the V rows of
+    // tile t+1 and writes them to LDS; the compute waves score tile t+1 and
+    // run the softmax and V accumulation of tile t from LDS written earlier.
+    if (wave == kProducer) {
+        const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
+        const int32_t *sel = p.sel + (int64_t)i * p.sel_stride;
+        int sel3 = -1;  // selected id of tile t+3 (this lane's cell)
+        int ph2 = -1;   // physical cell of tile t+2
+        for (int t = -4; t < n_tiles; ++t) {
+            const bool ld_k = (t + 2 >= 0) && (t + 2 < n_tiles);
+            const bool ld_v = (t + 1 >= 0) && (t + 1 < n_tiles);
+            // gather loads first, the code rows last
+            uint16_t kh2 = 0, vh2 = 0;
+            int pte3 = -1, sel4 = -1;
+            if (ld_k && ph2 >= 0) {
+                kh2 = p.k_scales[ph2];
+                vh2 = p.v_scales[ph2];
+            }
+            if (t + 3 >= 0 && t + 3 < n_tiles && sel3 >= 0 && (sel3 >> 4) < p.n_logical_pages)
+                pte3 = pt[sel3 >> 4];
+            const int j4 = j_begin + (t + 4) * kTile + lane;
+            if (t + 4 < n_tiles && j4 < j_end) sel4 = sel[j4];
+            v4i kst[kRows], vst[kRows];
+            if (ld_k) {
+                const int *ph_t = phys_s[(t + 2) & 3];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                v4f v = {0.f, 0.f, 0.f, 0.f};
-                if (row < R)
-                    v = *reinterpret_cast<const v4f *>(p.q + ((int64_t)i * R + row) * kDim +
-                                                       64 * s + 16 * g + 4 * e4);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    qv[s][4 * e4 + u] = v[u];
-                    mx = fmaxf(mx, fabsf(v[u]));
+                for (int it = 0; it < kRows; ++it) {
+                    int ph = ph_t[4 * it + g];
+                    ph = ph < 0 ? 0 : ph;  // masked cell: any valid row, its weight is 0
+                    kst[it] = *reinterpret_cast<const v4i *>(p.k_codes + (int64_t)ph * kDim + 16 * l16);
                 }
             }
+            if (ld_v) {
+                const int *ph_t = phys_s[(t + 1) & 3];
+#pragma unroll
+                for (int it = 0; it < kRows; ++it) {
+                    int ph = ph_t[4 * it + g];
+                    ph = ph < 0 ? 0 : ph;
+                    vst[it] = *reinterpret_cast<const v4i *>(p.v_codes + (int64_t)ph * kDim + 16 * l16);
+                }
+            }
+            // complete: code rows to LDS (row 4it + g, bytes 16 l16)
+            if (ld_k) {
+                int8_t *kb = kbuf[(t + 2) & 1] + g * kStride + 16 * l16;
+#pragma unroll
+                for (int it = 0; it < kRows; ++it)
+                    *reinterpret_cast<v4i *>(kb + 4 * it * kStride) = kst[it];
+            }
+            if (ld_v) {
+                int8_t *vb = vbuf[(t + 1) & 1] + g * kStride + 16 * l16;
+#pragma unroll
+                for (int it = 0; it < kRows; ++it)
+                    *reinterpret_cast<v4i *>(vb + 4 * it * kStride) = vst[it];
+            }
+            if (ld_k) {
+                const int m2 = (t + 2) & 3;
+                const bool ok = ph2 >= 0;
+                const float ksf = ok ? half_bits_to_float(kh2) : 0.f;
+                const float vsf = ok ? half_bits_to_float(vh2) : 0.f;
+                ks_s[m2][lane] = ksf;
+                vs_s[m2][lane] = vsf;
+                bias_s[m2][lane] = ok ? 0.f : -INFINITY;
+                const float vm = wave_max(vsf);
+                if (lane == 0) vmax_s[m2] = vm;
+            }
+            if (t + 3 >= 0 && t + 3 < n_tiles) {
+                int ph = -1;
+                if (pte3 >= 0 && (int64_t)pte3 < p.n_phys_pages) ph = (pte3 << 4) | (sel3 & 15);
+                phys_s[(t + 3) & 3][lane] = ph;
+                const int j3 = j_begin + (t + 3) * kTile + lane;
+                if (p.gather_out && j3 < j_end) p.gather_out[(int64_t)i * p.sel_stride + j3] = ph;
+                ph2 = ph;
+            }
+            sel3 = sel4;
+            __syncthreads();
         }
-        mx = wave_max4(mx);
-        const float inv = mx > 0.f ? 127.f / mx : 0.f;
-        coef_q = (mx / 127.f) * p.scale_log2 * (1.f / 256.f);
+        return;
+    }
+
+    // ======================= compute waves =======================
+    const int row = wave * 16 + l16;
+    // ---- query digits: B operands of S^T = K Q^T for rows 16*wave + l16,
+    // dims 64s + 16g + e (byte e of slab s).  The sign of the softmax scale is
+    // folded into the digits so that coef >= 0 and max commutes with it.
+    v4i qa[4], qb[4], qc[4];
+    float coef;  // sigma * |scale_log2| / 2^8: S (base 2) = coef * (AB + C / 2^8) * k_scale
+    {
+        v4f qv[4][4];
+        float mx = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                qv[s][w] = (v4f){0.f, 0.f, 0.f, 0.f};
+                if (row < R)
+                    qv[s][w] = *reinterpret_cast<const v4f *>(
+                        p.q + ((int64_t)i * R + row) * kDim + 64 * s + 16 * g + 4 * w);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(qv[s][w][u]));
+            }
+        mx = wave_max(mx);
+        const float inv = mx > 0.f ? (p.scale_log2 < 0.f ? -65536.f : 65536.f) * 127.f / mx : 0.f;
+        // clamped away from 0 so that masked cells (-inf) never meet a zero factor
+        coef = fmaxf((mx / 127.f) * fabsf(p.scale_log2) * (1.f / 256.f), 1e-30f);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -145,16 +253,15 @@ __global__ __launch_bounds__(64 * RB) void chunk_mfma_kernel(Params p) {
                 unsigned pa = 0, pb = 0, pc = 0;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float x = qv[s][4 * w + u] * inv;
-                    float a = rintf(x);
-                    const float r1 = (x - a) * 256.f;
-                    float b = rintf(r1);
-                    float cc = rintf((r1 - b) * 256.f);
-                    if (cc > 127.f) { cc -= 256.f; b += 1.f; }
-                    if (b > 127.f) { b -= 256.f; a += 1.f; }
-                    pa |= ((unsigned)(int)a & 0xffu) << (8 * u);
-                    pb |= ((unsigned)(int)b & 0xffu) << (8 * u);
-                    pc |= ((unsigned)(int)cc & 0xffu) << (8 * u);
+                    // X = round(q * 127 * 2^16 / max) = 2^16 a + 2^8 b + c, balanced digits
+                    const int X = (int)rintf(qv[s][w][u] * inv);
+                    const int dc = __builtin_amdgcn_sbfe(X, 0, 8);
+                    const int X1 = (X - dc) >> 8;
+                    const int db = __builtin_amdgcn_sbfe(X1, 0, 8);
+                    const int da = (X1 - db) >> 8;
+                    pa |= ((unsigned)da & 0xffu) << (8 * u);
+                    pb |= ((unsigned)db & 0xffu) << (8 * u);
+                    pc |= ((unsigned)dc & 0xffu) << (8 * u);
                 }
                 qa[s][w] = (int)pa;
                 qb[s][w] = (int)pb;
@@ -163,165 +270,145 @@ __global__ __launch_bounds__(64 * RB) void chunk_mfma_kernel(Params p) {
         }
     }
 
+    // ---- per-lane constant LDS offsets (everything else is an immediate)
+    // K operand of cell block cb, slab s: row lds_row(cb, l16), bytes 64s + 16g
+    const int k_off0 = lds_row(0, l16) * kStride + 16 * g;
+    const int k_off1 = (lds_row(1, l16) - 16) * kStride + 16 * g;
+    // transposed V read: source role (b, h) = (l16 >> 1, l16 & 1) reads row
+    // lds_row(2r + (b >> 2), 4g + (b & 3)), bytes 16db + 8h
+    const int tb = l16 >> 1, th = l16 & 1;
+    const int v_off = (16 * (tb >> 2) + 4 * (g ^ (tb >> 2)) + (tb & 3)) * kStride + 8 * th;
+    // this lane's S cells (cb, 4g + u) live in LDS rows 16cb + 4(g ^ (cb & 1)) + u
+    const int m_off0 = 4 * g, m_off1 = 4 * (g ^ 1);
+
     float m_run = -INFINITY;  // running max of this lane's row (base-2 units)
     float l_part = 0.f;       // this lane's share of the row denominator
-    v4f o[16];                // O^T[16db + 4g + u][row]
+    float frame = 1.f;        // O = frame * o
+    v4f o[16];                // O^T[16db + 4g + u][row] / frame
 #pragma unroll
     for (int db = 0; db < 16; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
+    v4f su[4];  // scores of the tile the softmax runs on next: u, S = coef * u
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 
-    for (int seg0 = j_begin; seg0 < j_end; seg0 += kSeg) {
-        const int seg_cnt = min(kSeg, j_end - seg0);
-        const int seg_tiles = (seg_cnt + kTile - 1) / kTile;
-        __syncthreads();  // LDS of the previous segment no longer read
-        {
-            // batched gather: all selected ids, then all page-table entries,
-            // then all scales, so each thread waits for three round trips
-            constexpr int kPer = (kSeg + 64 * RB - 1) / (64 * RB);
-            const int lim = seg_tiles * kTile;
-            int ids[kPer], ph[kPer];
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int jj = threadIdx.x + k * 64 * RB;
-                ids[k] = (jj < seg_cnt) ? sel[seg0 + jj] : -1;
-            }
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) ph[k] = gather_cell(p, pt, ids[k]);
-            uint16_t kh[kPer], vh[kPer];
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int q0 = ph[k] < 0 ? 0 : ph[k];
-                kh[k] = p.k_scales[q0];
-                vh[k] = p.v_scales[q0];
-            }
-#pragma unroll
-            for (int k = 0; k < kPer; ++k) {
-                const int jj = threadIdx.x + k * 64 * RB;
-                if (jj < lim) {
-                    const bool ok = ph[k] >= 0;
-                    phys_s[jj] = ph[k];
-                    ks_s[jj] = ok ? half_bits_to_float(kh[k]) : 0.f;
-                    vs_s[jj] = ok ? half_bits_to_float(vh[k]) : 0.f;
-                    bias_s[jj] = ok ? 0.f : -INFINITY;
-                    if (p.gather_out && jj < seg_cnt)
-                        p.gather_out[(int64_t)i * p.sel_stride + seg0 + jj] = ph[k];
-                }
-            }
-        }
-        __syncthreads();
-        issue_tile<RB>(p, phys_s, 0, kbuf[0], vbuf[0], wave, lane);
+    for (int t = -4; t < n_tiles; ++t) {
+        if (t >= -1) {
+            // Both halves run every iteration (no validity branches, so the
+            // scheduler can interleave them); a tile outside [0, n_tiles) has
+            // all scores at -inf and changes nothing.
+            const bool next_ok = (t + 1 >= 0) && (t + 1 < n_tiles);
+            const int b1 = (t + 1) & 1, m1 = (t + 1) & 3;
+            const int b0 = t & 1, m0 = t & 3;
 
-        for (int t = 0; t < seg_tiles; ++t) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();  // tile t staged by every wave; tile t-1 no longer read
-            if (t + 1 < seg_tiles)
-                issue_tile<RB>(p, phys_s, t + 1, kbuf[(t + 1) & 1], vbuf[(t + 1) & 1], wave,
-                               lane);
-            const int8_t *kb = kbuf[t & 1];
-            const int8_t *vb = vbuf[t & 1];
-            const int cb0 = t * kTile + 4 * g;  // this lane's first cell in the segment arrays
-
-            // ---- scores S^T[cell = 16cb + 4g + u][row], base-2 units
-            v4f sc[4];
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const int cell = 16 * cb + l16;
-                v4i ka[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    ka[s] = *reinterpret_cast<const v4i *>(
-                        kb + cell * kRow + (((4 * s + g) ^ swz_k(cell)) << 4));
-                v4i ab = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) ab = mfma_i8(ka[s], qa[s], ab);
-                ab = ab << 8;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) ab = mfma_i8(ka[s], qb[s], ab);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) cc = mfma_i8(ka[s], qc[s], cc);
-                const v4f ks = *reinterpret_cast<const v4f *>(&ks_s[cb0 + 16 * cb]);
-                const v4f bs = *reinterpret_cast<const v4f *>(&bias_s[cb0 + 16 * cb]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
-                    sc[cb][u] = fmaf(tq, ks[u] * coef_q, bs[u]);
-                }
-            }
-
-            // ---- online softmax (row max over the tile: 16 cells here, 4 lane groups)
+            // ---------------- softmax statistics of tile t (scores in su)
             float tmax = -INFINITY;
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) tmax = fmaxf(tmax, sc[cb][u]);
-            tmax = wave_max4(tmax);
+                for (int u = 0; u < 4; ++u) tmax = fmaxf(tmax, su[cb][u]);
+            tmax = max4(tmax);
+            tmax = (tmax == -INFINITY) ? -INFINITY : tmax * coef;  // base-2 tile max
             const float m_new = fmaxf(m_run, tmax);
             const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
             const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+            const float frame_new = (m_run == -INFINITY) ? 1.f : frame * corr;
             m_run = m_new;
-            float psum = 0.f, pmax = 0.f;
-            v4f pw[4];
+            // W = 256 / tau; X = rint(p * v_scale * W) lands in the low bits of
+            // fma(p, v_scale * W, 2^23)
+            const float vmax = vmax_s[m0];
+            const bool live = tmax != -INFINITY && vmax > 0.f && (m_use - tmax) < kFarBelow;
+            const float W = live ? (256.f * 127.f) * __builtin_amdgcn_rcpf(vmax) *
+                                       __builtin_amdgcn_exp2f(m_use - tmax)
+                                 : 0.f;
+
+            // ---------------- scores of tile t+1: u = (AB + C/2^8) * k_scale + bias
+            v4f sn[4];
+            {
+                const int8_t *kb = kbuf[b1];
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
+                    v4i ka[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
+                    v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        aa = mfma_i8(ka[s], qa[s], aa);
+                        bb = mfma_i8(ka[s], qb[s], bb);
+                        cc = mfma_i8(ka[s], qc[s], cc);
+                    }
+                    const v4i ab = (aa << 8) + bb;  // 2^8 A + B, |.| < 2^30
+                    const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
+                    const v4f ks = *reinterpret_cast<const v4f *>(&ks_s[m1][mo]);
+                    const v4f bs = *reinterpret_cast<const v4f *>(&bias_s[m1][mo]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
+                        sn[cb][u] = next_ok ? fmaf(tq, ks[u], bs[u]) : -INFINITY;
+                    }
+                }
+            }
+
+            // ---------------- probabilities and their digits for tile t
+            float psum = 0.f;
+            v4i xa, xb;
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
-                const v4f vs = *reinterpret_cast<const v4f *>(&vs_s[cb0 + 16 * cb]);
+                const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
+                const v4f vs = *reinterpret_cast<const v4f *>(&vs_s[m0][mo]);
+                unsigned xs[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float pr = __builtin_amdgcn_exp2f(sc[cb][u] - m_use);
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -m_use));
                     psum += pr;
-                    pw[cb][u] = pr * vs[u];
-                    pmax = fmaxf(pmax, pw[cb][u]);
+                    xs[u] = __float_as_uint(fmaf(pr, vs[u] * W, kRound));
                 }
+                // low digit = byte 0 of X; high digit = byte 1 of X + 128
+                const unsigned lo01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
+                const unsigned lo23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
+                const unsigned hi01 = __builtin_amdgcn_perm(xs[1] + 128u, xs[0] + 128u, 0x0c0c0501u);
+                const unsigned hi23 = __builtin_amdgcn_perm(xs[3] + 128u, xs[2] + 128u, 0x05010c0cu);
+                xa[cb] = (int)(hi01 | hi23);
+                xb[cb] = (int)(lo01 | lo23);
             }
             l_part = fmaf(l_part, corr, psum);
-            pmax = wave_max4(pmax);
-            const float inv_tau = pmax > 0.f ? 127.f / pmax : 0.f;
-            const float tau2 = pmax * (1.f / (127.f * 256.f));
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
 
-            // ---- probability digits: byte e = 4cb + u <-> cell 16cb + 4g + u
-            v4i pa, pb;
+            // rare: fold the frame into the accumulator before it gets too small
+            frame = frame_new;
+            if (__any(frame < kRenorm)) {
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                unsigned wa = 0, wb = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float x = pw[cb][u] * inv_tau;
-                    const float a = rintf(x);
-                    const float b = fminf(rintf(fmaf(x - a, 256.f, 128.f)), 255.f);
-                    wa |= (unsigned)a << (8 * u);
-                    wb |= (unsigned)b << (8 * u);
-                }
-                pa[cb] = (int)wa;
-                pb[cb] = (int)(wb ^ 0x80808080u);  // offset-128 bytes -> signed digits
+                for (int db = 0; db < 16; ++db) o[db] *= frame;
+                frame = 1.f;
             }
+            const float tau2 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 256 / frame
 
-            // ---- O^T += V^T P^T for 16 blocks of 16 dims
-            const int tb = l16 >> 1, th = l16 & 1;  // source role in the transposed read
+            // ---------------- O^T += V^T P^T for 16 blocks of 16 dims
+            const int8_t *vp = vbuf[b0] + v_off;
 #pragma unroll
             for (int db = 0; db < 16; ++db) {
-                v4i va;
+                const v2i h0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)(vp + 16 * db));
+                const v2i h1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (v2i LDS_AS *)(vp + 32 * kStride + 16 * db));
+                const v4i va = {h0[0], h0[1], h1[0], h1[1]};
+                const v4i hi = mfma_i8(va, xa, (v4i){0, 0, 0, 0});
+                const v4i lo = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
+                const v4i acc = (hi << 8) + lo;  // sum of X * v_code, exact
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int e = 8 * r + tb;
-                    const int cell = ((e >> 2) << 4) + 4 * g + (e & 3);
-                    const int8_t *src = vb + cell * kRow + ((db ^ swz_v(cell)) << 4) + 8 * th;
-                    const v2i h = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)(src));
-                    va[2 * r] = h[0];
-                    va[2 * r + 1] = h[1];
-                }
-                v4i acc = mfma_i8(va, pa, (v4i){0, 0, 0, 0});
-                acc = acc << 8;
-                acc = mfma_i8(va, pb, acc);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) o[db][u] = fmaf((float)acc[u], tau2, o[db][u] * corr);
+                for (int u = 0; u < 4; ++u) o[db][u] = fmaf((float)acc[u], tau2, o[db][u]);
             }
         }
+        __syncthreads();
     }
 
-    const float l_row = wave_sum4(l_part);
+    const float l_row = sum4(l_part);
     if (row < R) {
         const int64_t base = ((int64_t)i * p.n_chunks + c) * R + row;
         float *dst = p.acc + base * kDim + 4 * g;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = o[db];
+        for (int db = 0; db < 16; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
         if (g == 0) {
             // base-2 maximum back to natural-log units
             p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
@@ -333,13 +420,12 @@ __global__ __launch_bounds__(64 * RB) void chunk_mfma_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_chunk(const Params &p, hipStream_t s) {
-    dim3 grid(p.n_chunks, p.n_inst);
-    const int rb = (p.n_rows + 15) / 16;
-    switch (rb) {
-        case 1: chunk_mfma_kernel<1><<<grid, 64, 0, s>>>(p); break;
-        case 2: chunk_mfma_kernel<2><<<grid, 128, 0, s>>>(p); break;
-        case 3: chunk_mfma_kernel<3><<<grid, 192, 0, s>>>(p); break;
-        default: chunk_mfma_kernel<4><<<grid, 256, 0, s>>>(p); break;
+    dim3 grid(p.n_inst, p.n_chunks);
+    switch ((p.n_rows + 15) / 16) {
+        case 1: chunk_mfma_kernel<1><<<grid, 128, 0, s>>>(p); break;
+        case 2: chunk_mfma_kernel<2><<<grid, 192, 0, s>>>(p); break;
+        case 3: chunk_mfma_kernel<3><<<grid, 256, 0, s>>>(p); break;
+        default: chunk_mfma_kernel<4><<<grid, 320, 0, s>>>(p); break;
     }
     return hipGetLastError();
 }
