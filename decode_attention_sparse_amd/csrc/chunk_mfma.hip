@@ -112,6 +112,7 @@ void chunk_mfma_kernel(Params p) {
     constexpr int kProducer = RB;  // the last wave
     __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kBuf];
     __shared__ __attribute__((aligned(1024))) int8_t vbuf[2][kBuf];
+    // physical cell of tile cell 16k + r at [slot][4r + k]
     __shared__ __attribute__((aligned(16))) int phys_s[4][kTile];
     __shared__ __attribute__((aligned(16))) float ks_s[4][kTile];
     __shared__ __attribute__((aligned(16))) float vs_s[4][kTile];
@@ -148,59 +149,72 @@ void chunk_mfma_kernel(Params p) {
     if (wave == kProducer) {
         const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
         const int32_t *sel = p.sel + (int64_t)i * p.sel_stride;
+        // page table, or (with no logical pages, when every cell is masked) any
+        // readable int so that the unconditional loads below stay in bounds
+        const int32_t *pt_or_sel = p.n_logical_pages > 0 ? pt : sel;
         int sel3 = -1;  // selected id of tile t+3 (this lane's cell)
         int ph2 = -1;   // physical cell of tile t+2
         for (int t = -4; t < n_tiles; ++t) {
             const bool ld_k = (t + 2 >= 0) && (t + 2 < n_tiles);
             const bool ld_v = (t + 1 >= 0) && (t + 1 < n_tiles);
-            // gather loads first, the code rows last
-            uint16_t kh2 = 0, vh2 = 0;
-            int pte3 = -1, sel4 = -1;
-            if (ld_k && ph2 >= 0) {
-                kh2 = p.k_scales[ph2];
-                vh2 = p.v_scales[ph2];
-            }
-            if (t + 3 >= 0 && t + 3 < n_tiles && sel3 >= 0 && (sel3 >> 4) < p.n_logical_pages)
-                pte3 = pt[sel3 >> 4];
+            // gather loads: unconditional, from clamped (always valid) addresses,
+            // so that none of them is consumed before the end of the step; the
+            // per-lane validity is applied when the values are used
+            const bool ld_p = (t + 3 >= 0) && (t + 3 < n_tiles);
+            const bool ld_s = (t + 4 < n_tiles);
             const int j4 = j_begin + (t + 4) * kTile + lane;
-            if (t + 4 < n_tiles && j4 < j_end) sel4 = sel[j4];
+            const int lp3 = sel3 >> 4;
+            const bool id_ok = sel3 >= 0 && lp3 < p.n_logical_pages;
+            const unsigned kh2 = p.k_scales[ph2 < 0 ? 0 : ph2];
+            const unsigned vh2 = p.v_scales[ph2 < 0 ? 0 : ph2];
+            const int pte3 = pt_or_sel[id_ok ? lp3 : 0];
+            const int sel4 = sel[j4 < j_end ? j4 : j_end - 1];
+            // then the code rows: load (k, c) covers rows 16k + l16, bytes
+            // 64c + 16g, so each lane needs the physical cells of 4 rows only
+            // (one 16-byte LDS read) and every load uses an immediate offset
             v4i kst[kRows], vst[kRows];
             if (ld_k) {
-                const int *ph_t = phys_s[(t + 2) & 3];
+                const v4i ph4 = *reinterpret_cast<const v4i *>(&phys_s[(t + 2) & 3][4 * l16]);
 #pragma unroll
-                for (int it = 0; it < kRows; ++it) {
-                    int ph = ph_t[4 * it + g];
-                    ph = ph < 0 ? 0 : ph;  // masked cell: any valid row, its weight is 0
-                    kst[it] = *reinterpret_cast<const v4i *>(p.k_codes + (int64_t)ph * kDim + 16 * l16);
+                for (int k = 0; k < 4; ++k) {
+                    const int8_t *src = p.k_codes + (int64_t)(ph4[k] < 0 ? 0 : ph4[k]) * kDim + 16 * g;
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        kst[4 * k + cc] = *reinterpret_cast<const v4i *>(src + 64 * cc);
                 }
             }
             if (ld_v) {
-                const int *ph_t = phys_s[(t + 1) & 3];
+                const v4i ph4 = *reinterpret_cast<const v4i *>(&phys_s[(t + 1) & 3][4 * l16]);
 #pragma unroll
-                for (int it = 0; it < kRows; ++it) {
-                    int ph = ph_t[4 * it + g];
-                    ph = ph < 0 ? 0 : ph;
-                    vst[it] = *reinterpret_cast<const v4i *>(p.v_codes + (int64_t)ph * kDim + 16 * l16);
+                for (int k = 0; k < 4; ++k) {
+                    const int8_t *src = p.v_codes + (int64_t)(ph4[k] < 0 ? 0 : ph4[k]) * kDim + 16 * g;
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        vst[4 * k + cc] = *reinterpret_cast<const v4i *>(src + 64 * cc);
                 }
             }
-            // complete: code rows to LDS (row 4it + g, bytes 16 l16)
+            // complete: code rows to LDS (row 16k + l16, bytes 64c + 16g)
             if (ld_k) {
-                int8_t *kb = kbuf[(t + 2) & 1] + g * kStride + 16 * l16;
+                int8_t *kb = kbuf[(t + 2) & 1] + l16 * kStride + 16 * g;
 #pragma unroll
-                for (int it = 0; it < kRows; ++it)
-                    *reinterpret_cast<v4i *>(kb + 4 * it * kStride) = kst[it];
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        *reinterpret_cast<v4i *>(kb + 16 * k * kStride + 64 * cc) = kst[4 * k + cc];
             }
             if (ld_v) {
-                int8_t *vb = vbuf[(t + 1) & 1] + g * kStride + 16 * l16;
+                int8_t *vb = vbuf[(t + 1) & 1] + l16 * kStride + 16 * g;
 #pragma unroll
-                for (int it = 0; it < kRows; ++it)
-                    *reinterpret_cast<v4i *>(vb + 4 * it * kStride) = vst[it];
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc)
+                        *reinterpret_cast<v4i *>(vb + 16 * k * kStride + 64 * cc) = vst[4 * k + cc];
             }
             if (ld_k) {
                 const int m2 = (t + 2) & 3;
                 const bool ok = ph2 >= 0;
-                const float ksf = ok ? half_bits_to_float(kh2) : 0.f;
-                const float vsf = ok ? half_bits_to_float(vh2) : 0.f;
+                const float ksf = ok ? half_bits_to_float((uint16_t)kh2) : 0.f;
+                const float vsf = ok ? half_bits_to_float((uint16_t)vh2) : 0.f;
                 ks_s[m2][lane] = ksf;
                 vs_s[m2][lane] = vsf;
                 bias_s[m2][lane] = ok ? 0.f : -INFINITY;
@@ -209,13 +223,13 @@ void chunk_mfma_kernel(Params p) {
             }
             if (t + 3 >= 0 && t + 3 < n_tiles) {
                 int ph = -1;
-                if (pte3 >= 0 && (int64_t)pte3 < p.n_phys_pages) ph = (pte3 << 4) | (sel3 & 15);
-                phys_s[(t + 3) & 3][lane] = ph;
+                if (id_ok && pte3 >= 0 && (int64_t)pte3 < p.n_phys_pages) ph = (pte3 << 4) | (sel3 & 15);
+                phys_s[(t + 3) & 3][4 * l16 + g] = ph;  // cell 16g + l16
                 const int j3 = j_begin + (t + 3) * kTile + lane;
                 if (p.gather_out && j3 < j_end) p.gather_out[(int64_t)i * p.sel_stride + j3] = ph;
                 ph2 = ph;
             }
-            sel3 = sel4;
+            sel3 = (ld_s && j4 < j_end) ? sel4 : -1;
             __syncthreads();
         }
         return;
