@@ -11,7 +11,9 @@ oracle disagrees with:
   - an invariant that the exact result has (selection order, chunk size,
     a uniform score shift realised through the inputs, relabelling of
     physical pages, masking equals deletion, doubling V scales doubles the
-    output, duplicate entries).
+    output, duplicate entries);
+  - brute force: every one- and two-cell subset (and random larger ones) of
+    a 32-cell pool, recomputed with scalar Python arithmetic.
 test_oracle.py runs every pin against the oracle, and also against mutated
 copies of the oracle source to show that plausible mistakes are caught.
 """
@@ -75,7 +77,8 @@ def _close(a, b, rtol, atol=0.0, what=""):
     a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
     assert a.shape == b.shape, (what, a.shape, b.shape)
     same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    bad = ~same_inf & ~(np.abs(a - b) <= atol + rtol * np.abs(b))
+    with np.errstate(invalid="ignore"):  # inf - inf where both are the same infinity
+        bad = ~same_inf & ~(np.abs(a - b) <= atol + rtol * np.abs(b))
     assert not bad.any(), f"{what}: max |diff| {np.nanmax(np.abs(np.where(same_inf, 0, a - b)))}"
 
 
@@ -355,7 +358,67 @@ def pin_duplicates(O):
     _close(b[1], a[1] + math.log(2), 1e-14, 0, "dup lse")
 
 
+def _brute(x, subset, page_table):
+    """Attention over the logical cells in `subset` with plain Python scalar
+    arithmetic (math.fsum, math.exp): no numpy contraction, no oracle code."""
+    D = x.q.shape[-1]
+    Q = x.q[0].reshape(-1, D)
+    kc, vc = x.k_codes, x.v_codes
+    ks, vs = f16(x.k_scales), f16(x.v_scales)
+    cells = []
+    for c in subset:
+        pp = int(page_table[c // 16])
+        if 0 <= pp < kc.shape[0] // 16:
+            cells.append(pp * 16 + c % 16)
+    outs, lses = [], []
+    for r in range(Q.shape[0]):
+        q = [float(v) for v in Q[r]]
+        if not cells:
+            outs.append([0.0] * D)
+            lses.append(-math.inf)
+            continue
+        s = [float(x.softmax_scale) * float(ks[ph]) * math.fsum(q[d] * int(kc[ph, d]) for d in range(D))
+             for ph in cells]
+        m = max(s)
+        w = [math.exp(v - m) for v in s]
+        L = math.fsum(w)
+        outs.append([math.fsum(w[j] * float(vs[ph]) * int(vc[ph, d]) for j, ph in enumerate(cells)) / L
+                     for d in range(D)])
+        lses.append(m + math.log(L))
+    return np.array(outs), np.array(lses)
+
+
+def pin_brute_force_subsets(O):
+    """Every subset of one or two cells of a 32-cell pool (two pages, one of
+    them masked in a second table), and 150 random subsets of 3..8 cells,
+    each against _brute.  All subsets run as instances of one oracle call."""
+    import itertools
+    x = tiny(29, pool_cells=32, n_sel=1, n_q=2, n_qheads=2, head_dim=8)
+    rng = np.random.default_rng(2929)
+    subsets = [list(c) for k in (1, 2) for c in itertools.combinations(range(32), k)]
+    subsets += [sorted(rng.choice(32, size=int(k), replace=False).tolist())
+                for k in rng.integers(3, 9, size=150)]
+    for masked in (False, True):
+        pt = x.page_table[0].copy()
+        if masked:
+            pt[1] = -1
+        n = len(subsets)
+        sel = np.zeros((n, 8), np.int32)
+        for i, sub in enumerate(subsets):
+            sel[i, : len(sub)] = sub
+        y = dataclasses.replace(
+            x, page_table=np.repeat(pt[None], n, 0), sel=sel,
+            n_sel=np.array([len(sb) for sb in subsets], np.int32),
+            q=np.ascontiguousarray(np.repeat(x.q, n, 0)))
+        out, lse = _attend_flat(O, y)
+        for i, sub in enumerate(subsets):
+            ro, rl = _brute(x, sub, pt)
+            _close(out[i], ro, 1e-12, 1e-14, f"brute out {sub} masked={masked}")
+            _close(lse[i], rl, 1e-12, 1e-14, f"brute lse {sub} masked={masked}")
+
+
 ALL_PINS = [pin_half_decode, pin_textbook, pin_gather_exhaustive, pin_one_cell, pin_two_cells,
             pin_zero_query, pin_identical_keys, pin_worked_example, pin_merge_closed_form,
             pin_empty_and_masked, pin_permutation, pin_chunking, pin_score_shift,
-            pin_relabel_pages, pin_mask_equals_delete, pin_double_v_scales, pin_duplicates]
+            pin_relabel_pages, pin_mask_equals_delete, pin_double_v_scales, pin_duplicates,
+            pin_brute_force_subsets]
