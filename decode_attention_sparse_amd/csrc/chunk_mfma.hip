@@ -160,7 +160,6 @@ void chunk_mfma_kernel(Params p) {
             // gather loads: unconditional, from clamped (always valid) addresses,
             // so that none of them is consumed before the end of the step; the
             // per-lane validity is applied when the values are used
-            const bool ld_p = (t + 3 >= 0) && (t + 3 < n_tiles);
             const bool ld_s = (t + 4 < n_tiles);
             const int j4 = j_begin + (t + 4) * kTile + lane;
             const int lp3 = sel3 >> 4;

@@ -5,48 +5,117 @@
 // Strata round-9 page, section "R9-gpu-11" (accumulators, maxima and
 // denominators are the partials; the softmax merge order is fixed).
 //
-// One workgroup of 256 threads per (row, instance); thread d owns head
-// dimension d.  The chunk maxima and denominators are read by every thread
-// (same address, served as a broadcast), the accumulators once each,
-// coalesced along d.
+// Lane l owns head dimensions [4l, 4l + 4): one 16-byte load per chunk and
+// lane, a 1 KB coalesced row per wave.  Rows with many chunks are split over
+// the four waves of a workgroup, rows with few get one wave each (see
+// merge_kernel).  The first batch of accumulator rows is requested before
+// the maximum over the chunk maxima is known, so a short merge costs one
+// round trip to memory.  Wave sums are added in a fixed order through LDS,
+// which keeps the result deterministic.
 #include "sda_internal.h"
 
 namespace sda {
 namespace {
 
-__global__ __launch_bounds__(kDim) void merge_kernel(Params p) {
-    const int r = blockIdx.x;
-    const int i = blockIdx.y;
-    const int d = threadIdx.x;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBatch = 8;  // accumulator rows in flight per wave
+
+__device__ __forceinline__ float wave_max_shfl(float x) {
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+    return x;
+}
+
+// KW = waves that share one row's chunks.  KW = 4: workgroup = one (instance,
+// row), wave w takes chunks c = w (mod 4) (long merges).  KW = 1: workgroup =
+// four rows of one instance, one wave per row (short merges, where a row has
+// only a few chunks and splitting them would leave waves idle).
+template <int KW>
+__global__ __launch_bounds__(256) void merge_kernel(Params p) {
+    __shared__ v4f part_o[KW > 1 ? KW - 1 : 1][64];
+    __shared__ float part_l[KW > 1 ? KW - 1 : 1];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x;  // instance (x: the grid dimension without a 64K limit)
+    const int r = KW == 1 ? 4 * blockIdx.y + wave : blockIdx.y;
+    const int share = KW == 1 ? 0 : wave;
     const int R = p.n_rows;
+    if (KW == 1 && r >= R) return;
     const int n = count_of(p, i);
     const int nch = (n + p.chunk - 1) / p.chunk;
-    const int64_t row0 = (int64_t)i * p.n_chunks * R + r;  // chunk c at row0 + c*R
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, p.m[row0 + (int64_t)c * R]);
-    float *o = p.out + ((int64_t)i * R + r) * kDim;
-    if (M == -INFINITY) {
-        o[d] = 0.f;
-        if (d == 0) p.lse[(int64_t)i * R + r] = -INFINITY;
+    const int64_t row0 = (int64_t)i * p.n_chunks * R + r;  // chunk c of this row: row0 + c * R
+    const float *acc_l = p.acc + row0 * kDim + 4 * lane;
+
+    // Loads are issued for clamped chunk ids (always inside this instance's
+    // partials) and chunks past the end get weight 0, so no load is behind a
+    // branch.
+    v4f a[kBatch];
+    float mc[kBatch], lc[kBatch];
+    auto load_batch = [&](int c0) {
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int c = c0 + KW * k;
+            const int64_t e = (int64_t)(c < nch ? c : nch - 1) * R;
+            a[k] = *reinterpret_cast<const v4f *>(acc_l + e * kDim);
+            const float m = p.m[row0 + e];
+            mc[k] = c < nch ? m : -INFINITY;
+            lc[k] = p.l[row0 + e];
+        }
+    };
+
+    float M = -INFINITY, L = 0.f;
+    v4f o = (v4f){0.f, 0.f, 0.f, 0.f};
+    if (share < nch) {
+        load_batch(share);  // in flight while the maximum is formed
+        for (int c = lane; c < nch; c += 64) M = fmaxf(M, p.m[row0 + (int64_t)c * R]);
+        M = wave_max_shfl(M);
+        for (int c0 = share;;) {
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                // a chunk with no unmasked cell (m = -inf) has weight 0
+                const float w = mc[k] == -INFINITY ? 0.f : expf(mc[k] - M);
+                L = fmaf(lc[k], w, L);
+                o += w * a[k];
+            }
+            c0 += KW * kBatch;
+            if (c0 >= nch) break;
+            load_batch(c0);
+        }
+    }
+
+    if (KW > 1) {
+        if (wave > 0) {
+            part_o[wave - 1][lane] = o;
+            if (lane == 0) part_l[wave - 1] = L;
+        }
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w = 0; w < KW - 1; ++w) {
+            o += part_o[w][lane];
+            L += part_l[w];
+        }
+    }
+    v4f *out = reinterpret_cast<v4f *>(p.out + ((int64_t)i * R + r) * kDim) + lane;
+    if (!(L > 0.f)) {  // no unmasked cell in any chunk
+        *out = (v4f){0.f, 0.f, 0.f, 0.f};
+        if (lane == 0) p.lse[(int64_t)i * R + r] = -INFINITY;
         return;
     }
-    float L = 0.f, acc = 0.f;
-    for (int c = 0; c < nch; ++c) {
-        const float mc = p.m[row0 + (int64_t)c * R];
-        if (mc == -INFINITY) continue;  // chunk with no unmasked cell
-        const float w = expf(mc - M);
-        L = fmaf(p.l[row0 + (int64_t)c * R], w, L);
-        acc = fmaf(p.acc[(row0 + (int64_t)c * R) * kDim + d], w, acc);
-    }
-    o[d] = acc / L;
-    if (d == 0) p.lse[(int64_t)i * R + r] = M + logf(L);
+    *out = o * (1.f / L);
+    if (lane == 0) p.lse[(int64_t)i * R + r] = M + logf(L);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const Params &p, hipStream_t s) {
-    dim3 grid(p.n_rows, p.n_inst), block(kDim);
-    merge_kernel<<<grid, block, 0, s>>>(p);
+    // rows with more chunks than one batch split them over four waves
+    if (p.n_chunks > kBatch) {
+        merge_kernel<4><<<dim3(p.n_inst, p.n_rows), dim3(256), 0, s>>>(p);
+    } else {
+        merge_kernel<1><<<dim3(p.n_inst, (p.n_rows + 3) / 4), dim3(256), 0, s>>>(p);
+    }
     return hipGetLastError();
 }
 

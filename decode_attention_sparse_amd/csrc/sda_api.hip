@@ -31,6 +31,7 @@ int layout_of(int64_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim, i
     if (chunk_cells % SDA_CHUNK_ALIGN) return SDA_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)n_q * n_qheads;
     const int64_t n_chunks = (max_sel + (int64_t)chunk_cells - 1) / chunk_cells;
+    if (n_chunks > SDA_MAX_CHUNKS) return SDA_ERR_UNSUPPORTED;
     const size_t units = (size_t)n_inst * (size_t)n_chunks * (size_t)rows;
     L->n_chunks = (int32_t)n_chunks;
     L->acc_off = 0;
@@ -67,7 +68,7 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     if (!isfinite(softmax_scale)) return SDA_ERR_INVALID_ARG;
     if (n_inst == 0) return SDA_OK;
     if (!q || !aligned(q, 16)) return SDA_ERR_INVALID_ARG;
-    if ((passes & kMerge) && (!out || !lse || !aligned(out, 4) || !aligned(lse, 4)))
+    if ((passes & kMerge) && (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)))
         return SDA_ERR_INVALID_ARG;
     if (n_logical_pages > 0 && !page_table) return SDA_ERR_INVALID_ARG;
     if (max_sel > 0 && !sel) return SDA_ERR_INVALID_ARG;
@@ -165,7 +166,7 @@ int sda_merge_batch(int32_t n_inst, int32_t n_q, int32_t n_qheads, const int32_t
     int st = layout_of(n_inst, n_q, n_qheads, SDA_HEAD_DIM, max_sel, chunk_cells, &L);
     if (st != SDA_OK) return st;
     if (n_inst == 0) return SDA_OK;
-    if (!n_sel || !out || !lse || !aligned(out, 4) || !aligned(lse, 4)) return SDA_ERR_INVALID_ARG;
+    if (!n_sel || !out || !lse || !aligned(out, 16) || !aligned(lse, 4)) return SDA_ERR_INVALID_ARG;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)))
         return SDA_ERR_WORKSPACE;
     sda::Params p;

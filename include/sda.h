@@ -59,6 +59,7 @@ extern "C" {
 #define SDA_HEAD_DIM 256 /* dims per head (the only supported value) */
 #define SDA_MAX_ROWS 64  /* n_q * n_qheads limit */
 #define SDA_CHUNK_ALIGN 64 /* chunk_cells must be a positive multiple of this */
+#define SDA_MAX_CHUNKS 65535 /* ceil(max_sel / chunk_cells) limit (one grid dimension) */
 
 typedef enum {
     SDA_OK = 0,
@@ -90,7 +91,8 @@ typedef struct sda_pool {
  *     acc  float [n_inst][n_chunks][R][head_dim]
  *     m    float [n_inst][n_chunks][R]   (natural-log units, -inf if empty)
  *     l    float [n_inst][n_chunks][R]
- * with R = n_q * n_qheads, n_chunks = ceil(max_sel / chunk_cells), and each
+ * with R = n_q * n_qheads, n_chunks = ceil(max_sel / chunk_cells) (at most
+ * SDA_MAX_CHUNKS, else SDA_ERR_UNSUPPORTED), and each
  * of the three arrays starting at a 256-byte aligned offset (acc at 0, m at
  * align256(sizeof acc), l at m + align256(sizeof m)).  After a call these
  * hold the chunk partials of the chunks that instance actually has
@@ -108,7 +110,7 @@ int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t h
  *   n_q, n_qheads host; 1 <= n_q, 1 <= n_qheads, n_q * n_qheads <= SDA_MAX_ROWS
  *   softmax_scale host, finite
  *   chunk_cells   host, positive multiple of SDA_CHUNK_ALIGN
- *   out           float [n_q][n_qheads][head_dim]
+ *   out           float [n_q][n_qheads][head_dim], 16-byte aligned
  *   lse           float [n_q][n_qheads]
  *   gather_out    nullable int32 [n_sel]: physical cell per entry, -1 if masked
  *   workspace     device buffer of at least sda_workspace_bytes(1, ..., n_sel, ...)
@@ -132,7 +134,7 @@ int sda_decode_attn_step(const sda_pool *pool, const int32_t *page_table,
  *                 clamped to [0, max_sel]
  *   max_sel       host upper bound of n_sel[i]; sizes the grid and workspace
  *   q             float [n_inst][n_q][n_qheads][head_dim]
- *   out           float [n_inst][n_q][n_qheads][head_dim]
+ *   out           float [n_inst][n_q][n_qheads][head_dim], 16-byte aligned
  *   lse           float [n_inst][n_q][n_qheads]
  *   gather_out    nullable int32 [n_inst][sel_stride]
  *   other arguments as for sda_decode_attn_step, with the workspace sized by
@@ -157,7 +159,8 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
  * sda_merge_batch runs only the merge pass over partials laid out as
  * sda_workspace_bytes(n_inst, n_q, n_qheads, SDA_HEAD_DIM, max_sel,
  * chunk_cells) describes: n_sel (device, [n_inst]) gives each instance's
- * chunk count as above; out float [n_inst][n_q][n_qheads][head_dim],
+ * chunk count as above; out float [n_inst][n_q][n_qheads][head_dim]
+ * (16-byte aligned),
  * lse float [n_inst][n_q][n_qheads].
  *
  * Running sda_chunk_batch then sda_merge_batch on one stream gives exactly

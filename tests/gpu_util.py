@@ -20,7 +20,8 @@ def assert_close(got, ref, atol, rtol, what):
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     both_ninf = np.isneginf(got) & np.isneginf(ref)
-    diff = np.where(both_ninf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):  # -inf - -inf where both are -inf
+        diff = np.where(both_ninf, 0.0, np.abs(got - ref))
     tol = atol + rtol * np.where(both_ninf, 0.0, np.abs(ref))
     bad = ~(diff <= tol)
     if bad.any():

@@ -42,6 +42,14 @@ def test_header_compiles_as_c():
     assert r.returncode == 0, r.stderr
 
 
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define SDA_(\w+) (\d+)", text))
+    assert {k: int(v) for k, v in defs.items()} == {
+        "PAGE_SIZE": api.PAGE_SIZE, "HEAD_DIM": api.HEAD_DIM, "MAX_ROWS": api.MAX_ROWS,
+        "CHUNK_ALIGN": api.CHUNK_ALIGN, "MAX_CHUNKS": api.MAX_CHUNKS}
+
+
 def test_status_strings():
     lib = api.library()
     for st in (0, -1, -2, -3, -4, 7):
@@ -121,6 +129,8 @@ def _step(pool, **kw):
     ({}, dict(q=None), api.SDA_ERR_INVALID_ARG),
     ({}, dict(q=FAKE + 4), api.SDA_ERR_INVALID_ARG),
     ({}, dict(out=None), api.SDA_ERR_INVALID_ARG),
+    ({}, dict(out=FAKE + 4), api.SDA_ERR_INVALID_ARG),             # out rows are 16-byte stores
+    ({}, dict(n_sel=65535 * 256 + 1), api.SDA_ERR_UNSUPPORTED),    # more than 65,535 chunks
     ({}, dict(lse=None), api.SDA_ERR_INVALID_ARG),
     ({}, dict(sel=None), api.SDA_ERR_INVALID_ARG),
     ({}, dict(page_table=None), api.SDA_ERR_INVALID_ARG),
