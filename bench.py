@@ -38,6 +38,32 @@ PAGES_V3_US = {1: 34.5, 2: 41.0, 3: 73.0, 4: 84.9}
 PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 
 
+# HBM bytes per launch of the chunk kernel on the headline workload at n_q = 4
+# (cold caches), from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE),
+# each scaled by what the counter reads for a plain 256 MiB device copy
+# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary with the commands is in
+# profiles/chunk_mfma_kernel__hbm_bytes__pages_point_and_batched.md.  The
+# figures hold only for the kernel source they were taken on.
+CHUNK_TRAFFIC = {"sources_sha256": "c93cc9a12fcd229352435f89c9a598002591413924920e70621e324d2e333b3d",
+                 "fetch_bytes": 2_010_563, "write_bytes": 445_824}
+TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
+                   "decode_attention_sparse_amd/csrc/sda_internal.h")
+
+
+def chunk_traffic():
+    """Measured HBM bytes per headline chunk launch, or None when the kernel
+    source differs from the one the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != CHUNK_TRAFFIC["sources_sha256"]:
+        return None
+    return CHUNK_TRAFFIC["fetch_bytes"] + CHUNK_TRAFFIC["write_bytes"]
+
+
 def algorithmic_bytes(x) -> int:
     """Bytes the method must move for one chunk pass over inputs x: K and V
     code rows (256 B each), K and V scales (2 B each) and the list entry (4 B)
@@ -209,6 +235,9 @@ def main(argv=None):
     ap.add_argument("--configs", default="2,3,4", help="batched workloads to run")
     ap.add_argument("--chunk2", type=int, default=None,
                     help="chunk size for the 256-instance batched workload")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "reference dispatch for HBM byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print("bench.py measures one GPU: the path shards across GPUs without communication "
@@ -219,6 +248,13 @@ def main(argv=None):
     api.library()
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
+    if a.copy_probe_mib > 0:
+        src = torch.ones(a.copy_probe_mib << 18, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if a.only_batched:
         flush = make_flush()
@@ -282,7 +318,9 @@ def main(argv=None):
     cells_step = sum(c.cells for c in cases)
     value = cells_step / (step_ms * 1e-3)
     pages_step_us = sum(PAGES_V3_US.values())
-    achieved = bytes_sum / (chunk_us_sum * 1e-6) / 1e9
+    # roofline of the dominant kernel: the chunk kernel of the n_q = 4 call
+    c4, ch4_us = cases[3], per_q["q4"]["chunk_us"]
+    achieved = c4.bytes / (ch4_us * 1e-6) / 1e9
     flush = make_flush()
     cold = time_calls(cases, 20, flush=flush)
     cold_us = {f"q{nq}": round(float(np.median([u[0] + u[1] for u in s])) * 1e3, 3)
@@ -307,9 +345,15 @@ def main(argv=None):
                    "queries": [1, 2, 3, 4], "selected_cells": 2051, "pool_cells": 32768,
                    "chunk": base.chunk, "calls_per_step": 4, "device": dev_name,
                    "timing": "K steps captured in one HIP graph, HIP events around its replay; back-to-back calls with warm caches, as the pages' 200-call loop"},
-        "roofline": {"bound": "hbm", "kernel": "chunk pass", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": chunk_traffic(),
+                     "kernel": "chunk_mfma_kernel, n_q = 4 call of the step",
+                     "algorithmic_bytes_per_launch": c4.bytes,
+                     "launch_us_mean": ch4_us,
+                     "note": "latency-bound: one instance, 2,051 cells, 9 workgroups; "
+                             "traffic = HBM bytes per launch (cold, counters), null if the "
+                             "kernel changed since they were taken",
                      "bytes_per_step": bytes_sum, "chunk_us_per_step": round(chunk_us_sum, 3)},
         "per_query_count": per_q,
         "cold_us_per_call_median": cold_us,

@@ -107,7 +107,8 @@ __device__ __forceinline__ float wave_max(float x) {
 __device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (4 * (cb & 1))); }
 
 template <int RB>
-__global__ __launch_bounds__(64 * (RB + 1)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// two workgroups per CU (LDS-limited); with RB = 1 that is one wave per SIMD
+__global__ __launch_bounds__(64 * (RB + 1)) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p) {
     constexpr int kProducer = RB;  // the last wave
     __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kBuf];

@@ -56,18 +56,7 @@ __device__ __forceinline__ int count_of(const Params &p, int i) {
     return n > p.max_sel ? p.max_sel : n;
 }
 
-// Page-table gather of one selected logical cell: physical cell or -1.
-__device__ __forceinline__ int gather_cell(const Params &p, const int32_t *pt, int32_t c) {
-    if (c < 0) return -1;
-    const int lp = c >> 4;
-    if (lp >= p.n_logical_pages) return -1;
-    const int pg = pt[lp];
-    if (pg < 0 || (int64_t)pg >= p.n_phys_pages) return -1;
-    return (pg << 4) | (c & 15);
-}
-
 hipError_t launch_chunk(const Params &p, hipStream_t s);
-hipError_t launch_chunk_valu(const Params &p, hipStream_t s);
 hipError_t launch_merge(const Params &p, hipStream_t s);
 
 }  // namespace sda
