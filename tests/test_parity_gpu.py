@@ -100,6 +100,40 @@ def test_edge_counts(n_q, chunk):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_edge_counts_large_grid(n_q):
+    """The edge counts again, inside a grid of more than 256 workgroups
+    (64-cell chunks; the filler instances use the full count), so that they
+    run alongside full chunks on a busy chip."""
+    say(f"case: edge counts in a large grid, n_q={n_q}")
+    k = 64
+    counts = np.full(k, 257, np.int32)
+    counts[: len(EDGE_COUNTS)] = EDGE_COUNTS
+    x = gen.make(None, seed=91 + n_q, n_inst=k, n_q=n_q, pool_cells=1024, n_sel=257,
+                 sel="uniform", chunk=64)
+    x = dataclasses.replace(x, n_sel=counts)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what=f"edges large grid nq{n_q}")
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+def test_batch_size_independence():
+    """Instance data does not depend on the batch size, so the same instances
+    run once in a small grid and once in a large one; every instance is
+    computed by its own workgroups with the same arithmetic in the same
+    order, so outputs and gather indices must agree bit for bit."""
+    say("case: batch-size independence")
+    spec = dict(n_q=4, pool_cells=2048, n_sel=600, sel="uniform", chunk=64)
+    small = gen.make(None, seed=123, n_inst=20, **spec)   # 20 x 10 chunks
+    large = gen.make(None, seed=123, n_inst=30, **spec)   # 30 x 10 chunks
+    assert np.array_equal(small.sel, large.sel[:20]) and np.array_equal(small.q, large.q[:20])
+    o1, l1, g1, _ = run_batch(small)
+    o2, l2, g2, _ = run_batch(large)
+    assert np.array_equal(o1, o2[:20]) and np.array_equal(l1, l2[:20])
+    assert np.array_equal(g1, g2[:20])
+    check(large, o2, l2, g2, inst_ids=[0, 19, 29], what="batch of 30")
+
+
 def test_masking():
     """Page -1 masking, page ids past the pool, selected ids past the logical
     range, and an instance whose every page is masked."""
