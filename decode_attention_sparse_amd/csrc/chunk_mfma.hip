@@ -65,6 +65,7 @@ constexpr int kRows = kTile / 4;     // 1 KB staging loads per tile and pool (4 
 constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^22) to integers in the low bits
 constexpr float kFarBelow = 64.f;    // tiles 2^64 below the running max carry no weight
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
+constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -109,7 +110,7 @@ __device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (4
 template <int RB>
 // two workgroups per CU (LDS-limited); with RB = 1 that is one wave per SIMD
 __global__ __launch_bounds__(64 * (RB + 1)) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 1 : 2, 2)))
-void chunk_mfma_kernel(Params p) {
+void chunk_mfma_kernel(Params p, int cpw) {
     constexpr int kProducer = RB;  // the last wave
     __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kBuf];
     __shared__ __attribute__((aligned(1024))) int8_t vbuf[2][kBuf];
@@ -125,12 +126,16 @@ void chunk_mfma_kernel(Params p) {
     const int g = lane >> 4;    // lane group: k-set of the MFMA operands
     const int l16 = lane & 15;  // this lane's row within the wave's 16 rows
     const int i = blockIdx.x;   // instance (fastest: full chunks are dispatched first)
-    const int c = blockIdx.y;   // chunk
+    // This workgroup runs chunks [c0, c0 + cpw) of instance i as one stream
+    // of tiles: the gather pipeline runs on across chunk boundaries, and the
+    // compute waves emit a partial at the end of each chunk.
+    const int c0 = blockIdx.y * cpw;
     const int n = count_of(p, i);
-    const int j_begin = c * p.chunk;
+    const int j_begin = c0 * p.chunk;
     if (j_begin >= n) return;  // this instance has fewer chunks
-    const int j_end = min(j_begin + p.chunk, n);
+    const int j_end = (int)min((int64_t)j_begin + (int64_t)cpw * p.chunk, (int64_t)n);
     const int n_tiles = (j_end - j_begin + kTile - 1) / kTile;
+    const int tpc = p.chunk / kTile;  // tiles per chunk
     const int R = p.n_rows;
 
     // scale slots read before their first write hold finite values
@@ -413,33 +418,49 @@ void chunk_mfma_kernel(Params p) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) o[db][u] = fmaf((float)acc[u], tau2, o[db][u]);
             }
+
+            // ---------------- end of a chunk: emit its partial, start afresh
+            if (t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
+                const float l_row = sum4(l_part);
+                if (row < R) {
+                    const int64_t base = ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row;
+                    float *dst = p.acc + base * kDim + 4 * g;
+#pragma unroll
+                    for (int db = 0; db < 16; ++db)
+                        *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
+                    if (g == 0) {
+                        // base-2 maximum back to natural-log units
+                        p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
+                        p.l[base] = l_row;
+                    }
+                }
+                m_run = -INFINITY;
+                l_part = 0.f;
+                frame = 1.f;
+#pragma unroll
+                for (int db = 0; db < 16; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
+            }
         }
         __syncthreads();
-    }
-
-    const float l_row = sum4(l_part);
-    if (row < R) {
-        const int64_t base = ((int64_t)i * p.n_chunks + c) * R + row;
-        float *dst = p.acc + base * kDim + 4 * g;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
-        if (g == 0) {
-            // base-2 maximum back to natural-log units
-            p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
-            p.l[base] = l_row;
-        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_chunk(const Params &p, hipStream_t s) {
-    dim3 grid(p.n_inst, p.n_chunks);
+    // Chunks per workgroup: enough that the grid stays at about two
+    // workgroups per CU (256 CUs), so that no pipeline refills between the
+    // chunks a workgroup would otherwise have left to a later wave of
+    // workgroups; a small grid keeps one chunk per workgroup.
+    const int64_t items = (int64_t)p.n_inst * p.n_chunks;
+    int cpw = (int)(items / kResidentWorkgroups);
+    cpw = cpw < 1 ? 1 : (cpw > p.n_chunks ? p.n_chunks : cpw);
+    dim3 grid(p.n_inst, (p.n_chunks + cpw - 1) / cpw);
     switch ((p.n_rows + 15) / 16) {
-        case 1: chunk_mfma_kernel<1><<<grid, 128, 0, s>>>(p); break;
-        case 2: chunk_mfma_kernel<2><<<grid, 192, 0, s>>>(p); break;
-        case 3: chunk_mfma_kernel<3><<<grid, 256, 0, s>>>(p); break;
-        default: chunk_mfma_kernel<4><<<grid, 320, 0, s>>>(p); break;
+        case 1: chunk_mfma_kernel<1><<<grid, 128, 0, s>>>(p, cpw); break;
+        case 2: chunk_mfma_kernel<2><<<grid, 192, 0, s>>>(p, cpw); break;
+        case 3: chunk_mfma_kernel<3><<<grid, 256, 0, s>>>(p, cpw); break;
+        default: chunk_mfma_kernel<4><<<grid, 320, 0, s>>>(p, cpw); break;
     }
     return hipGetLastError();
 }

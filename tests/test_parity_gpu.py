@@ -134,6 +134,32 @@ def test_batch_size_independence():
     check(large, o2, l2, g2, inst_ids=[0, 19, 29], what="batch of 30")
 
 
+def test_several_chunks_per_workgroup():
+    """A grid of 1,600 chunks, so that each workgroup streams several
+    consecutive chunks of one instance; ragged per-instance counts put chunk
+    ends and instance ends at every position.  Outputs and every chunk's
+    partial are checked on sampled instances."""
+    from decode_attention_sparse_amd import api
+    say("case: several chunks per workgroup")
+    x = gen.make(None, seed=31, n_inst=200, n_q=2, pool_cells=1024, n_sel=512, sel="uniform",
+                 chunk=64)
+    rng = np.random.default_rng(8)
+    counts = rng.integers(0, 513, size=200).astype(np.int32)
+    counts[[0, 1, 2, 3]] = [512, 0, 65, 449]
+    x = dataclasses.replace(x, n_sel=counts)
+    ids = [0, 1, 2, 3, 57, 128, 199]
+    out, lse, g, ws = run_batch(x)
+    check(x, out, lse, g, inst_ids=ids, what="chunks per workgroup")
+    acc, m, l = (t.cpu().numpy() for t in api.partials(ws, 200, 2, 12, 512, 64))
+    racc, rm, rl = oracle.chunk_partials(x, 64, 8, inst_ids=ids)
+    for k, i in enumerate(ids):
+        nch = -(-int(counts[i]) // 64)
+        assert_close(m[i, :nch], rm[k, :nch], LSE_ATOL, LSE_RTOL, f"partial m inst {i}")
+        assert_close(l[i, :nch], rl[k, :nch], 0, 1e-3, f"partial l inst {i}")
+        assert_close(acc[i, :nch] / l[i, :nch, :, None], racc[k, :nch] / rl[k, :nch, :, None],
+                     OUT_ATOL, OUT_RTOL, f"partial acc/l inst {i}")
+
+
 def test_masking():
     """Page -1 masking, page ids past the pool, selected ids past the logical
     range, and an instance whose every page is masked."""
