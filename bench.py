@@ -86,12 +86,14 @@ def out_bytes(x) -> int:
 class Case:
     """One workload resident on the GPU, with its buffers and timing hooks."""
 
-    def __init__(self, x, chunk):
+    def __init__(self, x, chunk, interleave_scales=True):
         import torch
         from decode_attention_sparse_amd import api
         self.api, self.torch = api, torch
         self.x, self.chunk = x, chunk
-        self.pool, self.dev = api.to_device(x)
+        # the pool layout used for every measured workload: (K, V) scale pairs
+        # interleaved per cell, so a gathered cell's two scales share a sector
+        self.pool, self.dev = api.to_device(x, interleave_scales=interleave_scales)
         n_inst, n_q, nh, D = x.q.shape
         self.max_sel = int(x.sel.shape[1])
         self.out = torch.empty((n_inst, n_q, nh, D), device="cuda")
@@ -344,6 +346,7 @@ def main(argv=None):
         "config": {"workload": base.workload, "instances": 1, "n_qheads": 12, "head_dim": 256,
                    "queries": [1, 2, 3, 4], "selected_cells": 2051, "pool_cells": 32768,
                    "chunk": base.chunk, "calls_per_step": 4, "device": dev_name,
+                   "pool_layout": "int8 K and V code rows [cells][256]; binary16 (K, V) scale pairs interleaved per cell",
                    "timing": "K steps captured in one HIP graph, HIP events around its replay; back-to-back calls with warm caches, as the pages' 200-call loop"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),

@@ -31,7 +31,7 @@ class SdaError(RuntimeError):
 class _Pool(C.Structure):
     _fields_ = [("k_codes", C.c_void_p), ("k_scales", C.c_void_p), ("v_codes", C.c_void_p),
                 ("v_scales", C.c_void_p), ("n_phys_pages", C.c_int64), ("page_size", C.c_int32),
-                ("head_dim", C.c_int32)]
+                ("head_dim", C.c_int32), ("scale_stride", C.c_int32), ("reserved", C.c_int32)]
 
 
 _lib = None
@@ -66,21 +66,31 @@ def library() -> C.CDLL:
 
 @dataclasses.dataclass
 class Pool:
-    """Device tensors of the INT8 pools: codes int8 [cells][256], scales
-    binary16 bit patterns (int16/uint16/float16 tensors) [cells]."""
+    """Device tensors of the INT8 pools: codes int8 [cells][256]; scales as
+    binary16 bit patterns (int16/uint16/float16 tensors), either two arrays
+    [cells] or one array [cells][2] of interleaved (K, V) pairs (pass it as
+    `scales`, leaving k_scales / v_scales None)."""
     k_codes: torch.Tensor
-    k_scales: torch.Tensor
+    k_scales: torch.Tensor | None
     v_codes: torch.Tensor
-    v_scales: torch.Tensor
+    v_scales: torch.Tensor | None
+    scales: torch.Tensor | None = None
 
     @property
     def n_phys_pages(self) -> int:
         return self.k_codes.shape[0] // PAGE_SIZE
 
     def c_struct(self) -> _Pool:
+        hd = int(self.k_codes.shape[1]) if self.k_codes.dim() == 2 else 0
+        if self.scales is not None:
+            if self.scales.dim() != 2 or self.scales.shape[1] != 2:
+                raise ValueError("interleaved scales must have shape [cells][2]")
+            base = _ptr(self.scales)
+            es = self.scales.element_size()
+            return _Pool(_ptr(self.k_codes), base, _ptr(self.v_codes), base + es,
+                         self.n_phys_pages, PAGE_SIZE, hd, 2, 0)
         return _Pool(_ptr(self.k_codes), _ptr(self.k_scales), _ptr(self.v_codes),
-                     _ptr(self.v_scales), self.n_phys_pages, PAGE_SIZE,
-                     int(self.k_codes.shape[1]) if self.k_codes.dim() == 2 else 0)
+                     _ptr(self.v_scales), self.n_phys_pages, PAGE_SIZE, hd, 1, 0)
 
 
 def _ptr(t):
@@ -190,10 +200,17 @@ def merge_batch(n_sel, max_sel: int, chunk_cells: int, ws, out, lse, stream=None
         raise SdaError(st, "sda_merge_batch")
 
 
-def to_device(x, device="cuda"):
+def to_device(x, device="cuda", interleave_scales=False):
     """Upload generated inputs (decode_attention_sparse_amd.inputs.Inputs):
-    returns (Pool, dict of device tensors)."""
+    returns (Pool, dict of device tensors).  With interleave_scales the K and
+    V scales are stored as one [cells][2] array of (K, V) pairs."""
+    import numpy as np
     t = lambda a: torch.from_numpy(a).to(device)
-    pool = Pool(t(x.k_codes), t(x.k_scales.view("int16")), t(x.v_codes), t(x.v_scales.view("int16")))
+    if interleave_scales:
+        pairs = np.stack([x.k_scales.view("int16"), x.v_scales.view("int16")], axis=1)
+        pool = Pool(t(x.k_codes), None, t(x.v_codes), None, scales=t(np.ascontiguousarray(pairs)))
+    else:
+        pool = Pool(t(x.k_codes), t(x.k_scales.view("int16")), t(x.v_codes),
+                    t(x.v_scales.view("int16")))
     dev = dict(page_table=t(x.page_table), sel=t(x.sel), n_sel=t(x.n_sel), q=t(x.q))
     return pool, dev

@@ -170,8 +170,9 @@ void chunk_mfma_kernel(Params p, int cpw) {
             const int j4 = j_begin + (t + 4) * kTile + lane;
             const int lp3 = sel3 >> 4;
             const bool id_ok = sel3 >= 0 && lp3 < p.n_logical_pages;
-            const unsigned kh2 = p.k_scales[ph2 < 0 ? 0 : ph2];
-            const unsigned vh2 = p.v_scales[ph2 < 0 ? 0 : ph2];
+            const int64_t sc2 = (int64_t)(ph2 < 0 ? 0 : ph2) * p.scale_stride;
+            const unsigned kh2 = p.k_scales[sc2];
+            const unsigned vh2 = p.v_scales[sc2];
             const int pte3 = pt_or_sel[id_ok ? lp3 : 0];
             const int sel4 = sel[j4 < j_end ? j4 : j_end - 1];
             // then the code rows: load (k, c) covers rows 16k + l16, bytes

@@ -57,6 +57,8 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
         return SDA_ERR_INVALID_ARG;
     if (pool->n_phys_pages < 1 || pool->n_phys_pages > ((int64_t)1 << 27))
         return SDA_ERR_INVALID_ARG;
+    if (pool->scale_stride < 1 || pool->scale_stride > 64 || pool->reserved != 0)
+        return SDA_ERR_INVALID_ARG;
     if (!aligned(pool->k_codes, 16) || !aligned(pool->v_codes, 16) ||
         !aligned(pool->k_scales, 2) || !aligned(pool->v_scales, 2))
         return SDA_ERR_INVALID_ARG;
@@ -81,6 +83,7 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     p.k_scales = pool->k_scales;
     p.v_codes = pool->v_codes;
     p.v_scales = pool->v_scales;
+    p.scale_stride = pool->scale_stride;
     p.n_phys_pages = pool->n_phys_pages;
     p.page_table = page_table;
     p.pt_stride = pt_stride;

@@ -18,6 +18,7 @@ struct Params {
     const uint16_t *k_scales;
     const int8_t *v_codes;
     const uint16_t *v_scales;
+    int64_t scale_stride;       // elements between the scales of consecutive cells
     int64_t n_phys_pages;
     // per-instance inputs
     const int32_t *page_table;

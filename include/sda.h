@@ -72,8 +72,13 @@ typedef enum {
 /* The INT8 pools, indexed by physical cell = physical page * 16 + slot.
  *   k_codes, v_codes: int8 [n_phys_pages * 16][head_dim], row-major, 16-byte
  *                     aligned; the dequantised value is code * scale.
- *   k_scales, v_scales: IEEE binary16 bit patterns [n_phys_pages * 16], one
- *                     scale per physical cell.
+ *   k_scales, v_scales: IEEE binary16 bit patterns, one scale per physical
+ *                     cell: the scales of cell c are k_scales[c * scale_stride]
+ *                     and v_scales[c * scale_stride].
+ *   scale_stride:     >= 1.  1: two separate arrays.  2 with v_scales =
+ *                     k_scales + 1: (K, V) pairs interleaved per cell, so that
+ *                     the two scales of a cell share one memory sector (the
+ *                     cheaper layout when cells are gathered at random).
  * n_phys_pages must be in [1, 2^27]. */
 typedef struct sda_pool {
     const int8_t *k_codes;
@@ -81,8 +86,10 @@ typedef struct sda_pool {
     const int8_t *v_codes;
     const uint16_t *v_scales;
     int64_t n_phys_pages;
-    int32_t page_size; /* must be SDA_PAGE_SIZE */
-    int32_t head_dim;  /* must be SDA_HEAD_DIM */
+    int32_t page_size;    /* must be SDA_PAGE_SIZE */
+    int32_t head_dim;     /* must be SDA_HEAD_DIM */
+    int32_t scale_stride; /* elements between the scales of consecutive cells */
+    int32_t reserved;     /* must be 0 */
 } sda_pool;
 
 /* Workspace needed by one call (host only, no device access).

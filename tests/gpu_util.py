@@ -31,15 +31,16 @@ def assert_close(got, ref, atol, rtol, what):
     return float(diff.max()) if diff.size else 0.0
 
 
-def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda"):
+def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda", interleave=False):
     """Upload inputs and run sda_decode_attn_batch; returns numpy out, lse,
-    gather indices and the device workspace."""
+    gather indices and the device workspace.  interleave: store the K and V
+    scales as (K, V) pairs per cell (scale_stride 2)."""
     import torch
     from decode_attention_sparse_amd import api
     if n_q is not None:
         x = x.with_n_q(n_q)
     chunk = chunk or x.chunk
-    pool, dev = api.to_device(x, device)
+    pool, dev = api.to_device(x, device, interleave_scales=interleave)
     n_inst, nq, nh, D = x.q.shape
     out = torch.full((n_inst, nq, nh, D), float("nan"), device=device)
     lse = torch.full((n_inst, nq, nh), float("nan"), device=device)

@@ -100,7 +100,7 @@ FAKE = 1 << 20  # an aligned, never-dereferenced address: every case below fails
 
 def _pool(**kw):
     d = dict(k_codes=FAKE, k_scales=FAKE, v_codes=FAKE, v_scales=FAKE, n_phys_pages=16,
-             page_size=16, head_dim=256)
+             page_size=16, head_dim=256, scale_stride=1, reserved=0)
     d.update(kw)
     return api._Pool(**d)
 
@@ -124,6 +124,9 @@ def _step(pool, **kw):
     (dict(k_codes=FAKE + 8), {}, api.SDA_ERR_INVALID_ARG),          # misaligned codes
     (dict(n_phys_pages=0), {}, api.SDA_ERR_INVALID_ARG),
     (dict(n_phys_pages=(1 << 27) + 1), {}, api.SDA_ERR_INVALID_ARG),
+    (dict(scale_stride=0), {}, api.SDA_ERR_INVALID_ARG),
+    (dict(scale_stride=65), {}, api.SDA_ERR_INVALID_ARG),
+    (dict(reserved=1), {}, api.SDA_ERR_INVALID_ARG),
     ({}, dict(n_q=5, nh=13), api.SDA_ERR_UNSUPPORTED),
     ({}, dict(chunk=96), api.SDA_ERR_UNSUPPORTED),
     ({}, dict(q=None), api.SDA_ERR_INVALID_ARG),

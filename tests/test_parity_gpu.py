@@ -45,6 +45,18 @@ def test_config1_pages_kernel_point(n_q):
     check(x, out, lse, g, what=f"cfg1 nq{n_q}")
 
 
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_interleaved_scales(cfg):
+    """(K, V) scale pairs interleaved per cell (scale_stride 2) give the
+    same result as two scale arrays, bit for bit, and match the oracle."""
+    say(f"case: interleaved scales, config {cfg}")
+    x = gen.make(cfg)
+    o1, l1, g1, _ = run_batch(x)
+    o2, l2, g2, _ = run_batch(x, interleave=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(g1, g2)
+    check(x, o2, l2, g2, what=f"cfg{cfg} interleaved")
+
+
 @pytest.mark.parametrize("n_q", [1, 4])
 def test_step_entry_matches_batch(n_q):
     """sda_decode_attn_step on one sequence equals the batch entry bit for bit."""
@@ -199,11 +211,11 @@ def test_ragged_batch_and_unsorted():
 @pytest.mark.parametrize("cfg,ids", [(2, [0, 1, 97, 255]), (3, [0, 31, 63]), (4, [0, 31])])
 def test_full_size_configs_sampled(cfg, ids):
     """The batched workloads at full size, in the launch configuration the
-    bench times; sampled instances against the oracle, every gather index
-    bit-exact."""
+    bench times (interleaved scale pairs); sampled instances against the
+    oracle, every gather index bit-exact."""
     say(f"case: config {cfg} full size, oracle on instances {ids}")
     x = gen.make(cfg)
-    out, lse, g, _ = run_batch(x)
+    out, lse, g, _ = run_batch(x, interleave=True)
     check(x, out, lse, g, inst_ids=ids, what=f"cfg{cfg}")
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
