@@ -66,6 +66,7 @@ constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^22) to inte
 constexpr float kFarBelow = 64.f;    // tiles 2^64 below the running max carry no weight
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
+constexpr int64_t kLatencyWorkgroups = 256;         // grids up to one workgroup per CU
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -107,11 +108,18 @@ __device__ __forceinline__ float wave_max(float x) {
 // 16 lanes) each touch 8 distinct 16-byte bank groups.
 __device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (4 * (cb & 1))); }
 
-template <int RB>
-// two workgroups per CU (LDS-limited); with RB = 1 that is one wave per SIMD
-__global__ __launch_bounds__(64 * (RB + 1)) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 1 : 2, 2)))
+// DS = number of compute waves per 16-row group, each accumulating
+// O^T for 256 / DS of the head dimensions (every one of them scores the
+// whole tile).  DS = 1: two workgroups per CU (LDS-limited; with RB = 1 that
+// is one wave per SIMD), for grids that fill the chip.  DS = 2: half the
+// V accumulation per wave, which shortens each step of a small,
+// latency-bound grid (one workgroup per CU).
+template <int RB, int DS>
+__global__ __launch_bounds__(64 * (DS * RB + 1))
+__attribute__((amdgpu_waves_per_eu((RB == 1 || DS > 1) ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p, int cpw) {
-    constexpr int kProducer = RB;  // the last wave
+    constexpr int kProducer = DS * RB;  // the last wave
+    constexpr int kDB = 16 / DS;        // 16-dim blocks of O^T per compute wave
     __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kBuf];
     __shared__ __attribute__((aligned(1024))) int8_t vbuf[2][kBuf];
     // physical cell of tile cell 16k + r at [slot][4r + k]
@@ -139,7 +147,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     const int R = p.n_rows;
 
     // scale slots read before their first write hold finite values
-    for (int e = threadIdx.x; e < 4 * kTile; e += 64 * (RB + 1)) {
+    for (int e = threadIdx.x; e < 4 * kTile; e += 64 * (DS * RB + 1)) {
         (&ks_s[0][0])[e] = 0.f;
         (&vs_s[0][0])[e] = 0.f;
         (&bias_s[0][0])[e] = -INFINITY;
@@ -242,7 +250,8 @@ void chunk_mfma_kernel(Params p, int cpw) {
     }
 
     // ======================= compute waves =======================
-    const int row = wave * 16 + l16;
+    const int row = (wave / DS) * 16 + l16;  // this lane's query row
+    const int dh = wave % DS;                // its share of the head dimensions
     // ---- query digits: B operands of S^T = K Q^T for rows 16*wave + l16,
     // dims 64s + 16g + e (byte e of slab s).  The sign of the softmax scale is
     // folded into the digits so that coef >= 0 and max commutes with it.
@@ -304,9 +313,9 @@ void chunk_mfma_kernel(Params p, int cpw) {
     float m_run = -INFINITY;  // running max of this lane's row (base-2 units)
     float l_part = 0.f;       // this lane's share of the row denominator
     float frame = 1.f;        // O = frame * o
-    v4f o[16];                // O^T[16db + 4g + u][row] / frame
+    v4f o[kDB];               // O^T[16 (kDB dh + db) + 4g + u][row] / frame
 #pragma unroll
-    for (int db = 0; db < 16; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
     v4f su[4];  // scores of the tile the softmax runs on next: u, S = coef * u
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -400,15 +409,15 @@ void chunk_mfma_kernel(Params p, int cpw) {
             frame = frame_new;
             if (__any(frame < kRenorm)) {
 #pragma unroll
-                for (int db = 0; db < 16; ++db) o[db] *= frame;
+                for (int db = 0; db < kDB; ++db) o[db] *= frame;
                 frame = 1.f;
             }
             const float tau2 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 256 / frame
 
             // ---------------- O^T += V^T P^T for 16 blocks of 16 dims
-            const int8_t *vp = vbuf[b0] + v_off;
+            const int8_t *vp = vbuf[b0] + v_off + 16 * kDB * dh;
 #pragma unroll
-            for (int db = 0; db < 16; ++db) {
+            for (int db = 0; db < kDB; ++db) {
                 const v2i h0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)(vp + 16 * db));
                 const v2i h1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     (v2i LDS_AS *)(vp + 32 * kStride + 16 * db));
@@ -425,11 +434,11 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 const float l_row = sum4(l_part);
                 if (row < R) {
                     const int64_t base = ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row;
-                    float *dst = p.acc + base * kDim + 4 * g;
+                    float *dst = p.acc + base * kDim + 16 * kDB * dh + 4 * g;
 #pragma unroll
-                    for (int db = 0; db < 16; ++db)
+                    for (int db = 0; db < kDB; ++db)
                         *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
-                    if (g == 0) {
+                    if (g == 0 && dh == 0) {
                         // base-2 maximum back to natural-log units
                         p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
                         p.l[base] = l_row;
@@ -439,10 +448,20 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 l_part = 0.f;
                 frame = 1.f;
 #pragma unroll
-                for (int db = 0; db < 16; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
+                for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
             }
         }
         __syncthreads();
+    }
+}
+
+template <int DS>
+void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
+    switch ((p.n_rows + 15) / 16) {
+        case 1: chunk_mfma_kernel<1, DS><<<grid, 64 * (DS + 1), 0, s>>>(p, cpw); break;
+        case 2: chunk_mfma_kernel<2, DS><<<grid, 64 * (2 * DS + 1), 0, s>>>(p, cpw); break;
+        case 3: chunk_mfma_kernel<3, 1><<<grid, 64 * 4, 0, s>>>(p, cpw); break;
+        default: chunk_mfma_kernel<4, 1><<<grid, 64 * 5, 0, s>>>(p, cpw); break;
     }
 }
 
@@ -457,12 +476,13 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
     int cpw = (int)(items / kResidentWorkgroups);
     cpw = cpw < 1 ? 1 : (cpw > p.n_chunks ? p.n_chunks : cpw);
     dim3 grid(p.n_inst, (p.n_chunks + cpw - 1) / cpw);
-    switch ((p.n_rows + 15) / 16) {
-        case 1: chunk_mfma_kernel<1><<<grid, 128, 0, s>>>(p, cpw); break;
-        case 2: chunk_mfma_kernel<2><<<grid, 192, 0, s>>>(p, cpw); break;
-        case 3: chunk_mfma_kernel<3><<<grid, 256, 0, s>>>(p, cpw); break;
-        default: chunk_mfma_kernel<4><<<grid, 320, 0, s>>>(p, cpw); break;
-    }
+    // A grid of at most one workgroup per CU is latency-bound: split the V
+    // accumulation of each 16-row group over two waves while that still
+    // leaves about one compute wave per SIMD (up to 32 rows).
+    if (items <= kLatencyWorkgroups && p.n_rows <= 32)
+        launch_rb<2>(p, grid, cpw, s);
+    else
+        launch_rb<1>(p, grid, cpw, s);
     return hipGetLastError();
 }
 

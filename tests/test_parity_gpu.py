@@ -129,20 +129,26 @@ def test_edge_counts_large_grid(n_q):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
-def test_batch_size_independence():
+@pytest.mark.parametrize("n_q", [2, 4])
+def test_batch_size_independence(n_q):
     """Instance data does not depend on the batch size, so the same instances
-    run once in a small grid and once in a large one; every instance is
-    computed by its own workgroups with the same arithmetic in the same
-    order, so outputs and gather indices must agree bit for bit."""
-    say("case: batch-size independence")
-    spec = dict(n_q=4, pool_cells=2048, n_sel=600, sel="uniform", chunk=64)
+    run once in a small grid and once in a large one (which the library
+    launches differently: the V accumulation split over two waves per row
+    group for up to 32 rows in small grids, several chunks per workgroup in
+    large ones); every instance gets the same arithmetic in the same order,
+    so outputs and gather indices must agree bit for bit."""
+    say(f"case: batch-size independence, n_q={n_q}")
+    spec = dict(n_q=n_q, pool_cells=2048, n_sel=600, sel="uniform", chunk=64)
     small = gen.make(None, seed=123, n_inst=20, **spec)   # 20 x 10 chunks
     large = gen.make(None, seed=123, n_inst=30, **spec)   # 30 x 10 chunks
+    huge = gen.make(None, seed=123, n_inst=120, **spec)   # 120 x 10: two chunks per workgroup
     assert np.array_equal(small.sel, large.sel[:20]) and np.array_equal(small.q, large.q[:20])
     o1, l1, g1, _ = run_batch(small)
     o2, l2, g2, _ = run_batch(large)
-    assert np.array_equal(o1, o2[:20]) and np.array_equal(l1, l2[:20])
-    assert np.array_equal(g1, g2[:20])
+    o3, l3, g3, _ = run_batch(huge)
+    for o, l, g_ in ((o2, l2, g2), (o3, l3, g3)):
+        assert np.array_equal(o1, o[:20]) and np.array_equal(l1, l[:20])
+        assert np.array_equal(g1, g_[:20])
     check(large, o2, l2, g2, inst_ids=[0, 19, 29], what="batch of 30")
 
 
@@ -170,6 +176,21 @@ def test_several_chunks_per_workgroup():
         assert_close(l[i, :nch], rl[k, :nch], 0, 1e-3, f"partial l inst {i}")
         assert_close(acc[i, :nch] / l[i, :nch, :, None], racc[k, :nch] / rl[k, :nch, :, None],
                      OUT_ATOL, OUT_RTOL, f"partial acc/l inst {i}")
+
+
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_small_grid_large_page_table(n_q):
+    """A small (latency-bound) grid whose page table is too large to be read
+    into LDS (8,192 pages), with masked and out-of-range entries."""
+    say(f"case: small grid, 8,192-page table, n_q={n_q}")
+    x = gen.make(None, seed=41 + n_q, n_inst=2, n_q=n_q, pool_cells=131072, n_sel=700,
+                 sel="uniform", chunk=256)
+    pt = x.page_table.copy()
+    pt[0, ::5] = -1
+    pt[1, 7] = 10**8
+    x = dataclasses.replace(x, page_table=pt)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what=f"large table nq{n_q}")
 
 
 def test_masking():
