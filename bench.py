@@ -44,8 +44,8 @@ PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary with the commands is in
 # profiles/chunk_mfma_kernel__hbm_bytes__pages_point_and_batched.md.  The
 # figures hold only for the kernel source they were taken on.
-CHUNK_TRAFFIC = {"sources_sha256": "c93cc9a12fcd229352435f89c9a598002591413924920e70621e324d2e333b3d",
-                 "fetch_bytes": 2_010_563, "write_bytes": 445_824}
+CHUNK_TRAFFIC = {"sources_sha256": "7071f9f4bfaef7de808b35f336680c827d5749b04923a189b45d3a20d22be5d3",
+                 "fetch_bytes": 1_878_764, "write_bytes": 445_824}
 TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                    "decode_attention_sparse_amd/csrc/sda_internal.h")
 
@@ -205,6 +205,23 @@ def summarize(case, samples):
     }
 
 
+def gather_ceiling():
+    """Run probes/gather_ceiling (built with the library): cold-cache GB/s for
+    random 256-byte rows, random 4 KB pages, sequential rows and a plain
+    sequential read on this GPU.  None if the probe is not built."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "decode_attention_sparse_amd",
+                       "probes", "gather_ceiling")
+    if not os.path.exists(exe):
+        print(f"# {exe} not built: no measured ceilings", file=sys.stderr)
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        print(f"# gather_ceiling failed ({r.returncode}): {r.stderr.strip()}", file=sys.stderr)
+        return None
+    return [json.loads(ln) for ln in r.stdout.splitlines() if ln.startswith("{")]
+
+
 def cpu_baseline(xs, budget_s):
     """The fp64 oracle on the step's inputs, repeated for about budget_s."""
     import oracle
@@ -237,6 +254,8 @@ def main(argv=None):
     ap.add_argument("--configs", default="2,3,4", help="batched workloads to run")
     ap.add_argument("--chunk2", type=int, default=None,
                     help="chunk size for the 256-instance batched workload")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured HBM read ceilings (probes/gather_ceiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -245,6 +264,9 @@ def main(argv=None):
         print("bench.py measures one GPU: the path shards across GPUs without communication "
               "(instances are independent); run with --gpus 1", file=sys.stderr)
         return 2
+    # measured read ceilings for the access shapes of the chunk pass; run as a
+    # child process before this process touches the GPU
+    ceiling = None if (a.no_ceiling or a.only_batched) else gather_ceiling()
     import torch
     from decode_attention_sparse_amd import api, inputs
     api.library()
@@ -361,6 +383,7 @@ def main(argv=None):
         "per_query_count": per_q,
         "cold_us_per_call_median": cold_us,
         "cold_note": "eager calls, caches evicted before each by reading a 1 GiB buffer, HIP events around the kernels",
+        "hbm_read_ceiling_measured": ceiling,
         "vs_baseline_ref": "pages' v3 kernel on RTX 2080 Ti, sum over q=1..4 of chunk+merge us (context, other hardware)",
         "wall_s_timed_region": round(wall, 3),
     }

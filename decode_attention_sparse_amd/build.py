@@ -26,6 +26,23 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+PROBE_SRC = os.path.join(PKG, "probes", "gather_ceiling.hip")
+PROBE_BIN = os.path.join(PKG, "probes", "gather_ceiling")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The standalone HBM read-ceiling probe run by `bench.py --gather-ceiling`."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = PROBE_BIN + ".tmp%d" % os.getpid()
+    cmd = [hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    os.replace(tmp, PROBE_BIN)
+    return PROBE_BIN
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp%d" % os.getpid()
@@ -46,3 +63,4 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

@@ -1,0 +1,125 @@
+// Cold-cache HBM read ceilings on this GPU for the access shapes of the
+// chunk pass: 256-byte code rows gathered at random, 4 KB pages (16 rows)
+// gathered at random, and a plain sequential read.  Each measurement reads
+// 268 MB (or 1 GiB sequential) after evicting the caches by reading a
+// separate 1 GiB buffer; the median of 5 launches is printed as one JSON
+// line per shape.  Standalone program (no library code); built next to
+// libsda.so and run by `bench.py --gather-ceiling`.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <random>
+#include <vector>
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+#define CHECK(x)                                                                   \
+    do {                                                                           \
+        hipError_t e_ = (x);                                                       \
+        if (e_ != hipSuccess) {                                                    \
+            fprintf(stderr, "%s: %s\n", #x, hipGetErrorString(e_));                \
+            return 1;                                                              \
+        }                                                                          \
+    } while (0)
+
+// Workgroup w gathers tiles of 64 rows from both pools: each of its 4 waves
+// requests 8 blocks of 4 rows (16 lanes per 256-byte row) before using any.
+__global__ __launch_bounds__(256) void row_gather(const int8_t *kp, const int8_t *vp,
+                                                  const int *rows, int tiles, int *sink) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+    const int *my = rows + (int64_t)blockIdx.x * tiles * 64;
+    v4i acc = {0, 0, 0, 0};
+    for (int t = 0; t < tiles; ++t) {
+        v4i st[8];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int k = wave + 4 * it;  // 32 blocks: 16 of K, 16 of V
+            const int r = my[t * 64 + 4 * (k & 15) + g];
+            st[it] = *reinterpret_cast<const v4i *>((k >= 16 ? vp : kp) + (int64_t)r * 256 + 16 * l16);
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) acc ^= st[it];
+    }
+    if (acc.x == 0x13579bdf) sink[0] = acc.y;
+}
+
+__global__ __launch_bounds__(256) void seq_read(const v4i *src, int64_t n, int *sink) {
+    v4i acc = {0, 0, 0, 0};
+    for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) acc ^= src[e];
+    if (acc.x == 0x13579bdf) sink[0] = acc.y;
+}
+
+int main() {
+    const int64_t inst = 256, cells_per_inst = 32768, cells = inst * cells_per_inst;  // 2 GiB per pool
+    const int wgs = 512, tiles = 16, per = tiles * 64;
+    int8_t *kp, *vp;
+    int *rows, *sink;
+    v4i *flush;
+    const int64_t flush_n = (1ll << 30) / 16;
+    CHECK(hipMalloc(&kp, cells * 256));
+    CHECK(hipMalloc(&vp, cells * 256));
+    CHECK(hipMalloc(&flush, flush_n * 16));
+    CHECK(hipMalloc(&rows, (size_t)wgs * per * sizeof(int)));
+    CHECK(hipMalloc(&sink, 16));
+    CHECK(hipMemset(kp, 1, cells * 256));
+    CHECK(hipMemset(vp, 2, cells * 256));
+    CHECK(hipMemset(flush, 3, flush_n * 16));
+    hipEvent_t e0, e1;
+    CHECK(hipEventCreate(&e0));
+    CHECK(hipEventCreate(&e1));
+    auto evict = [&] { hipLaunchKernelGGL(seq_read, 2048, 256, 0, 0, flush, flush_n, sink); };
+    evict();  // clean lines only from here on
+    CHECK(hipDeviceSynchronize());
+    auto median_us = [&](auto launch) {
+        std::vector<float> v;
+        for (int rep = 0; rep < 6; ++rep) {
+            evict();
+            hipEventRecord(e0);
+            launch();
+            hipEventRecord(e1);
+            hipEventSynchronize(e1);
+            float ms = 0.f;
+            hipEventElapsedTime(&ms, e0, e1);
+            if (rep) v.push_back(ms * 1e3f);
+        }
+        std::sort(v.begin(), v.end());
+        return v[v.size() / 2];
+    };
+    const double gather_bytes = (double)wgs * per * 512;
+    const char *shape[3] = {"random 256-byte rows", "random 4 KB pages of 16 rows", "sequential rows"};
+    std::mt19937_64 rng(7);
+    std::vector<int> host(wgs * per);
+    for (int s = 0; s < 3; ++s) {
+        for (int w = 0; w < wgs; ++w) {
+            const int64_t base = (int64_t)(w / 2) * cells_per_inst;  // two workgroups per instance
+            std::vector<int> c(cells_per_inst);
+            for (int j = 0; j < cells_per_inst; ++j) c[j] = j;
+            if (s == 0) {
+                std::shuffle(c.begin(), c.end(), rng);
+            } else if (s == 1) {
+                std::vector<int> pg(cells_per_inst / 16);
+                for (size_t j = 0; j < pg.size(); ++j) pg[j] = (int)j;
+                std::shuffle(pg.begin(), pg.end(), rng);
+                for (int j = 0; j < per; ++j) c[j] = pg[j / 16] * 16 + (j & 15);
+            } else {
+                for (int j = 0; j < per; ++j) c[j] = (w & 1) * per + j;
+            }
+            for (int j = 0; j < per; ++j) host[(size_t)w * per + j] = (int)(base + c[j]);
+        }
+        for (int r : host)
+            if (r < 0 || r >= cells) { fprintf(stderr, "row out of range\n"); return 1; }
+        CHECK(hipMemcpy(rows, host.data(), host.size() * sizeof(int), hipMemcpyHostToDevice));
+        const float us = median_us([&] { hipLaunchKernelGGL(row_gather, wgs, 256, 0, 0, kp, vp, rows, tiles, sink); });
+        printf("{\"shape\": \"%s\", \"bytes\": %.0f, \"us\": %.2f, \"GBps\": %.1f}\n", shape[s], gather_bytes,
+               us, gather_bytes / (us * 1e-6) / 1e9);
+        fflush(stdout);
+    }
+    const int64_t seq_n = (1ll << 30) / 16;
+    const float us = median_us([&] { hipLaunchKernelGGL(seq_read, 4096, 256, 0, 0, (const v4i *)kp, seq_n, sink); });
+    printf("{\"shape\": \"sequential read\", \"bytes\": %.0f, \"us\": %.2f, \"GBps\": %.1f}\n", (double)seq_n * 16, us,
+           seq_n * 16 / (us * 1e-6) / 1e9);
+    CHECK(hipDeviceSynchronize());
+    return 0;
+}
