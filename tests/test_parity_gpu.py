@@ -241,6 +241,31 @@ def test_full_size_configs_sampled(cfg, ids):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("cfg,n_q", [(1, 4), (2, 4)])
+def test_batch_entry_equals_two_passes(cfg, n_q):
+    """sda_decode_attn_batch equals sda_chunk_batch followed by
+    sda_merge_batch bit for bit (the partials in the workspace included)."""
+    import torch
+    from decode_attention_sparse_amd import api
+    say(f"case: batch entry vs the two passes, config {cfg}, n_q={n_q}")
+    x = gen.make(cfg).with_n_q(n_q)
+    n_inst, _, nh, D = x.q.shape
+    max_sel = int(x.sel.shape[1])
+    out1, lse1, _, ws1 = run_batch(x, gather=False)
+    pool, dev = api.to_device(x)
+    ws2 = api.workspace(n_inst, n_q, nh, max_sel, x.chunk)
+    out2 = torch.empty((n_inst, n_q, nh, D), device="cuda")
+    lse2 = torch.empty((n_inst, n_q, nh), device="cuda")
+    api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
+                    x.softmax_scale, x.chunk, ws2)
+    api.merge_batch(dev["n_sel"], max_sel, x.chunk, ws2, out2, lse2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out1, out2.cpu().numpy()) and np.array_equal(lse1, lse2.cpu().numpy())
+    for a1, a2 in zip(api.partials(ws1, n_inst, n_q, nh, max_sel, x.chunk),
+                      api.partials(ws2, n_inst, n_q, nh, max_sel, x.chunk)):
+        assert torch.equal(a1, a2)
+
+
 def test_workspace_sentinel():
     """Bytes past the contracted workspace size stay untouched."""
     import torch
