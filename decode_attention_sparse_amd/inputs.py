@@ -203,3 +203,36 @@ def make(cfg: int | None = None, seed: int | None = None, *, threads: int | None
     return Inputs(n_sel=np.full((n_inst,), n_sel, np.int32),
                   softmax_scale=SOFTMAX_SCALE, chunk=int(spec["chunk"]),
                   workload=str(spec["workload"]), seed=int(seed), **out)
+
+
+# Prompt (many-query) attention over the same pools: the workload of the
+# prompt attention parity test on the Strata PR #2220 page (an INT8 context
+# of 32K cells and 2,048 queries per prompt chunk).  The chunk's own cells are
+# the last n_q cells of the context, so query t sits at position
+# pos0 + t with pos0 = pool_cells - n_q and sees cells 0..pos0 + t.
+PROMPT_CONFIGS = {
+    "prompt_int8_32k_2048q": dict(n_inst=1, n_q=2048, pool_cells=32768),
+}
+
+
+@dataclasses.dataclass
+class PromptInputs(Inputs):
+    pos0: np.ndarray = None  # int32 [n_inst]: position of query 0
+
+
+def make_prompt(name: str | None = None, seed: int | None = None, pos0=None,
+                **overrides) -> PromptInputs:
+    """Pools, permuted page tables and queries drawn exactly as make() draws
+    them (no selection list); pos0 defaults to pool_cells - n_q."""
+    spec = dict(PROMPT_CONFIGS[name]) if name is not None else {}
+    spec.update(overrides)
+    spec.update(sel="all", n_sel=0, chunk=64)
+    spec.setdefault("workload", name or "custom_prompt")
+    x = make(None, seed=20261300 if seed is None else seed, **spec)
+    n_inst = x.n_inst
+    if pos0 is None:
+        pos0 = np.full((n_inst,), int(spec["pool_cells"]) - x.n_q, np.int32)
+    pos0 = np.broadcast_to(np.asarray(pos0, np.int32), (n_inst,)).copy()
+    fields = {f.name: getattr(x, f.name) for f in dataclasses.fields(x)}  # no copies
+    return PromptInputs(**fields, pos0=pos0)
+

@@ -63,6 +63,10 @@ def _load():
     lib.oracle_chunk_partials.restype = None
     lib.oracle_chunk_partials.argtypes = pool + [C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                                  _f64p, _f64p, _f64p]
+    lib.oracle_prompt_attend.restype = None
+    lib.oracle_prompt_attend.argtypes = [_i8p, _u16p, _i8p, _u16p, C.c_int64, C.c_int64, _i32p,
+                                         C.c_int64, C.c_int64, _f32p, C.c_int64, C.c_int64,
+                                         C.c_double, _i64p, C.c_int64, _f64p, _f64p]
     lib.oracle_merge.restype = None
     lib.oracle_merge.argtypes = [C.c_int64, C.c_int64, C.c_int64, _f64p, _f64p, _f64p, _f64p,
                                  _f64p]
@@ -149,6 +153,28 @@ def chunk_partials(x, chunk: int, n_chunks: int | None = None, inst_ids=None):
     lib.oracle_chunk_partials(*args, chunk, n_chunks, None if ids is None else ids.ctypes.data,
                               k, acc, m, l)
     return acc, m, l
+
+
+def prompt_attend(x, inst: int = 0, t_ids=None):
+    """Prompt attention of instance `inst`: query position t sits at position
+    x.pos0[inst] + t and attends to logical cells 0..that position.  Returns
+    out float64 [k][n_qheads][D] and lse [k][n_qheads] for the positions t in
+    t_ids (all n_q when None)."""
+    lib = _load()
+    q = _c(x.q[inst], np.float32)
+    n_q, n_qheads, D = q.shape
+    t = np.arange(n_q, dtype=np.int64) if t_ids is None else _c(t_ids, np.int64).reshape(-1)
+    if t.size and (t.min() < 0 or t.max() >= n_q):
+        raise ValueError("position index out of range")
+    pt = _c(x.page_table[inst], np.int32)
+    kc = _c(x.k_codes, np.int8)
+    out = np.zeros((t.size, n_qheads, D), np.float64)
+    lse = np.zeros((t.size, n_qheads), np.float64)
+    lib.oracle_prompt_attend(kc, _c(x.k_scales, np.uint16), _c(x.v_codes, np.int8),
+                             _c(x.v_scales, np.uint16), kc.shape[0] // 16, D, pt, pt.shape[0],
+                             int(x.pos0[inst]), q, n_q, n_qheads, float(x.softmax_scale), t,
+                             t.size, out, lse)
+    return out, lse
 
 
 def merge(acc, m, l):

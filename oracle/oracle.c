@@ -184,6 +184,51 @@ void oracle_attend(const int8_t *k_codes, const uint16_t *k_scales, const int8_t
     }
 }
 
+/* Prompt (many-query) attention.  Strata PR #2220 page, closing note: the
+ * prompt attention's parity test takes the decode kernel as its reference.
+ * Reading: query position t of an instance sits at position p = pos0 + t
+ * and attends to the instance's logical cells 0, 1, ..., p (its own cell
+ * included), i.e. row (t, h) is the decode result above with the selection
+ * list 0..p; ids past the page table and masked pages drop out exactly as
+ * in the decode definition, and p < 0 leaves nothing (out = 0, lse = -inf).
+ * For one instance: page_table [n_logical_pages], q float32
+ * [n_q][n_qheads][head_dim]; the positions t listed in t_ids (n_ids of
+ * them) and every head h give out[k][h][head_dim] and lse[k][h]. */
+void oracle_prompt_attend(const int8_t *k_codes, const uint16_t *k_scales,
+                          const int8_t *v_codes, const uint16_t *v_scales,
+                          int64_t n_phys_pages, int64_t head_dim, const int32_t *page_table,
+                          int64_t n_logical_pages, int64_t pos0, const float *q, int64_t n_q,
+                          int64_t n_qheads, double sm_scale, const int64_t *t_ids,
+                          int64_t n_ids, double *out, double *lse) {
+    pool_t P = {k_codes, v_codes, k_scales, v_scales, n_phys_pages, head_dim};
+    const int64_t D = head_dim;
+    (void)n_q; /* q rows are indexed by the listed positions */
+    /* the selection list 0, 1, ..., p of the latest listed position */
+    int64_t p_max = -1;
+    for (int64_t k = 0; k < n_ids; ++k)
+        if (pos0 + t_ids[k] > p_max) p_max = pos0 + t_ids[k];
+    int32_t *list = malloc((size_t)(p_max + 1 > 0 ? p_max + 1 : 1) * sizeof(int32_t));
+    for (int64_t j = 0; j <= p_max; ++j) list[j] = (int32_t)j;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < n_ids * n_qheads; ++u) {
+        int64_t k = u / n_qheads, h = u % n_qheads;
+        int64_t t = t_ids[k];
+        int64_t p = pos0 + t;
+        int64_t n_visible = p + 1 > 0 ? p + 1 : 0;
+        double m, l;
+        double *o = out + u * D;
+        attend_range(&P, q + (t * n_qheads + h) * D, list, 0, n_visible, page_table,
+                     n_logical_pages, sm_scale, o, &m, &l);
+        if (m == -INFINITY) {
+            lse[u] = -INFINITY; /* o already zero */
+        } else {
+            for (int64_t d = 0; d < D; ++d) o[d] /= l;
+            lse[u] = m + log(l);
+        }
+    }
+    free(list);
+}
+
 /* Chunk partials: for each listed instance, chunk c (list positions
  * [c*chunk, min((c+1)*chunk, n_sel))) and row r: acc[k][c][r][D], m, l
  * ([k][c][r]).  Chunks past the instance's last (c >= ceil(n_sel/chunk)) are

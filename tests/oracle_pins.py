@@ -417,8 +417,111 @@ def pin_brute_force_subsets(O):
             _close(lse[i], rl, 1e-12, 1e-14, f"brute lse {sub} masked={masked}")
 
 
+# ------------------------------------------------------------ prompt attention
+def tiny_prompt(seed, pos0=None, **kw):
+    spec = dict(n_inst=1, n_q=6, n_qheads=3, head_dim=8, pool_cells=64)
+    spec.update(kw)
+    return gen.make_prompt(None, seed=seed, pos0=pos0, **spec)
+
+
+def textbook_prompt(x, i):
+    """Causal softmax attention over the dense dequantised logical view built
+    with numpy (as in textbook()): row (t, h) sees the logical cells
+    c <= pos0 + t that lie on unmasked pages; scipy's softmax and logsumexp."""
+    D = x.q.shape[-1]
+    n_pages_phys = x.k_codes.shape[0] // 16
+    Kp = (x.k_codes.astype(np.float64) * f16(x.k_scales)[:, None]).reshape(n_pages_phys, 16, D)
+    Vp = (x.v_codes.astype(np.float64) * f16(x.v_scales)[:, None]).reshape(n_pages_phys, 16, D)
+    pt = np.asarray(x.page_table[i], np.int64)
+    page_ok = (pt >= 0) & (pt < n_pages_phys)
+    safe = np.where(page_ok, pt, 0)
+    Klog = Kp[safe].reshape(-1, D)
+    Vlog = Vp[safe].reshape(-1, D)
+    ok_log = np.repeat(page_ok, 16)
+    n_q, nh = x.q.shape[1], x.q.shape[2]
+    Q = np.asarray(x.q[i], np.float64).reshape(-1, D)
+    pos = int(x.pos0[i]) + np.repeat(np.arange(n_q), nh)
+    visible = (np.arange(Klog.shape[0])[None, :] <= pos[:, None]) & ok_log[None, :]
+    S = np.where(visible, float(x.softmax_scale) * (Q @ Klog.T), -np.inf)
+    out = np.zeros((Q.shape[0], D))
+    lse = np.full((Q.shape[0],), -np.inf)
+    live = visible.any(axis=1)
+    if live.any():
+        out[live] = scipy.special.softmax(S[live], axis=1) @ Vlog
+        lse[live] = scipy.special.logsumexp(S[live], axis=1)
+    return out.reshape(n_q, nh, D), lse.reshape(n_q, nh)
+
+
+def pin_prompt_textbook(O):
+    cases = [
+        tiny_prompt(31),                                               # last 6 cells of the pool
+        tiny_prompt(32, pos0=0, n_q=5),                                # the first positions
+        tiny_prompt(33, pos0=-2, n_q=4),                               # two positions see nothing
+        tiny_prompt(34, pos0=60, n_q=8),                               # positions past the table
+        tiny_prompt(35, n_q=20, n_qheads=12, head_dim=256, pool_cells=256),
+        tiny_prompt(36, n_inst=2, pos0=[10, 40], n_q=7, n_qheads=5),   # instances apart
+    ]
+    x = tiny_prompt(37, n_q=30, pool_cells=128, pos0=70)
+    pt = x.page_table.copy()
+    pt[0, 2] = -1      # cells 32..47 masked
+    pt[0, 4] = 9_999   # cells 64..79 out of the pool
+    cases.append(dataclasses.replace(x, page_table=pt))
+    for x in cases:
+        for i in range(x.n_inst):
+            out, lse = O.prompt_attend(x, i)
+            ro, rl = textbook_prompt(x, i)
+            _close(out, ro, 1e-12, 1e-14, "prompt textbook out")
+            _close(lse, rl, 1e-12, 1e-14, "prompt textbook lse")
+
+
+def pin_prompt_first_cell(O):
+    """Position 0 sees cell 0 alone: out = its dequantised V row, lse = its
+    score (scalar Python arithmetic)."""
+    x = tiny_prompt(38, pos0=0, n_q=1)
+    out, lse = O.prompt_attend(x, 0)
+    ph = int(x.page_table[0, 0]) * 16
+    ks, vs = float(f16(x.k_scales[ph])), float(f16(x.v_scales[ph]))
+    for h in range(x.n_qheads):
+        dot = sum(float(a) * float(b) for a, b in zip(x.q[0, 0, h], x.k_codes[ph]))
+        s0 = float(x.softmax_scale) * ks * dot
+        _close(lse[0, h], s0, 1e-13, 1e-15, "first cell lse")
+        _close(out[0, h], [vs * float(v) for v in x.v_codes[ph]], 1e-15, 0.0, "first cell out")
+
+
+def pin_prompt_is_decode_of_prefix(O):
+    """Row (t, h) equals the decode result for the explicit selection 0..p."""
+    x = tiny_prompt(39, n_q=9, n_qheads=4, pool_cells=96, pos0=50)
+    out, lse = O.prompt_attend(x, 0)
+    for t in range(x.n_q):
+        p = int(x.pos0[0]) + t
+        d = dataclasses.replace(x, sel=np.arange(p + 1, dtype=np.int32)[None, :],
+                                n_sel=np.array([p + 1], np.int32),
+                                q=np.ascontiguousarray(x.q[:, t:t + 1]))
+        ro, rl = O.attend(d)
+        assert np.array_equal(out[t], ro[0, 0]) and np.array_equal(lse[t], rl[0, 0]), t
+
+
+def pin_prompt_causal(O):
+    """Changing the K/V rows of cells after a position leaves every row at or
+    before it bit for bit unchanged and changes the rows after it."""
+    x = tiny_prompt(40, n_q=12, pool_cells=64, pos0=50)
+    out, lse = O.prompt_attend(x, 0)
+    cut = 55  # change logical cells 56..63
+    phys = (x.page_table[0][np.arange(cut + 1, 64) // 16] * 16 + np.arange(cut + 1, 64) % 16)
+    kc, vc = x.k_codes.copy(), x.v_codes.copy()
+    kc[phys] = -kc[phys]
+    vc[phys] = 127 - np.abs(vc[phys])
+    y = dataclasses.replace(x, k_codes=kc, v_codes=vc)
+    out2, lse2 = O.prompt_attend(y, 0)
+    t_cut = cut - int(x.pos0[0])
+    assert np.array_equal(out[: t_cut + 1], out2[: t_cut + 1])
+    assert np.array_equal(lse[: t_cut + 1], lse2[: t_cut + 1])
+    assert all(not np.array_equal(out[t], out2[t]) for t in range(t_cut + 1, x.n_q))
+
+
 ALL_PINS = [pin_half_decode, pin_textbook, pin_gather_exhaustive, pin_one_cell, pin_two_cells,
             pin_zero_query, pin_identical_keys, pin_worked_example, pin_merge_closed_form,
             pin_empty_and_masked, pin_permutation, pin_chunking, pin_score_shift,
             pin_relabel_pages, pin_mask_equals_delete, pin_double_v_scales, pin_duplicates,
-            pin_brute_force_subsets]
+            pin_brute_force_subsets, pin_prompt_textbook, pin_prompt_first_cell,
+            pin_prompt_is_decode_of_prefix, pin_prompt_causal]

@@ -42,7 +42,10 @@ MUTANTS = {
     "exp_sign": ("double p = exp(score(P, qrow, ph, sm_scale) - m);",
                  "double p = exp(m - score(P, qrow, ph, sm_scale));"),
     "lse_without_max": ("lse[k * n_rows + r] = m + log(l);", "lse[k * n_rows + r] = log(l);"),
-    "no_normalisation": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;", "(void)0;"),
+    "no_normalisation": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;\n            lse[k * n_rows + r]",
+                         "(void)0;\n            lse[k * n_rows + r]"),
+    "prompt_no_normalisation": ("for (int64_t d = 0; d < D; ++d) o[d] /= l;\n            lse[u]",
+                                "(void)0;\n            lse[u]"),
     "merge_weight_sign": ("double w = exp(mc - M);", "double w = exp(M - mc);"),
     "merge_l_unweighted": ("L += l[u * n_chunks + c] * w;", "L += l[u * n_chunks + c];"),
     "half_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
@@ -51,6 +54,13 @@ MUTANTS = {
                         "attend_range(&P, q + (i * n_rows + (n_rows - 1 - r)) * D, sel + i * sel_stride, 0, n_sel[i],"),
     "chunk_end_off_by_one": ("int64_t j0 = c * chunk, j1 = j0 + chunk;",
                              "int64_t j0 = c * chunk, j1 = j0 + chunk - 1;"),
+    "prompt_excludes_own_cell": ("int64_t n_visible = p + 1 > 0 ? p + 1 : 0;",
+                                 "int64_t n_visible = p > 0 ? p : 0;"),
+    "prompt_ignores_pos0": ("int64_t p = pos0 + t;", "int64_t p = t;"),
+    "prompt_head_major_rows": ("attend_range(&P, q + (t * n_qheads + h) * D, list,",
+                               "attend_range(&P, q + (h * n_q + t) * D, list,"),
+    "prompt_sees_one_more": ("int64_t n_visible = p + 1 > 0 ? p + 1 : 0;",
+                             "int64_t n_visible = p + 2 > 0 ? p + 2 : 0;"),
 }
 
 
