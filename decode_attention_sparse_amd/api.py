@@ -17,9 +17,10 @@ LIB_PATH = os.path.join(PKG, "libsda.so")
 
 SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_LAUNCH = 0, -1, -2, -3, -4
 PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN, MAX_CHUNKS = 16, 256, 64, 64, 65535
+PROMPT_MAX_ROWS = 65535 * 64
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
-            "sda_chunk_batch", "sda_merge_batch", "sda_status_string")
+            "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_status_string")
 
 
 class SdaError(RuntimeError):
@@ -58,6 +59,9 @@ def library() -> C.CDLL:
         lib.sda_chunk_batch.restype = C.c_int
         lib.sda_merge_batch.argtypes = [i32, i32, i32, vp, i32, i32, vp, sz, vp, vp, vp]
         lib.sda_merge_batch.restype = C.c_int
+        lib.sda_prompt_attn_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, vp, i32, i32,
+                                              f32, vp, vp, vp]
+        lib.sda_prompt_attn_batch.restype = C.c_int
         lib.sda_status_string.argtypes = [C.c_int]
         lib.sda_status_string.restype = C.c_char_p
         _lib = lib
@@ -200,6 +204,22 @@ def merge_batch(n_sel, max_sel: int, chunk_cells: int, ws, out, lse, stream=None
         raise SdaError(st, "sda_merge_batch")
 
 
+def prompt_attn_batch(pool: Pool, page_table, pos0, q, softmax_scale: float, out, lse,
+                      stream=None, n_logical_pages: int | None = None):
+    """Prompt attention: page_table [n_inst][pt_stride], pos0 device int32
+    [n_inst] (position of query 0), q [n_inst][n_q][n_qheads][256] fp32; query
+    t of instance i attends causally to logical cells 0..pos0[i] + t.  out like
+    q, lse [n_inst][n_q][n_qheads]."""
+    n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    ps = pool.c_struct()
+    st = library().sda_prompt_attn_batch(
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.stride(0)), nlp, _ptr(pos0), _ptr(q),
+        n_q, n_qheads, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_prompt_attn_batch")
+
+
 def to_device(x, device="cuda", interleave_scales=False):
     """Upload generated inputs (decode_attention_sparse_amd.inputs.Inputs):
     returns (Pool, dict of device tensors).  With interleave_scales the K and
@@ -213,4 +233,6 @@ def to_device(x, device="cuda", interleave_scales=False):
         pool = Pool(t(x.k_codes), t(x.k_scales.view("int16")), t(x.v_codes),
                     t(x.v_scales.view("int16")))
     dev = dict(page_table=t(x.page_table), sel=t(x.sel), n_sel=t(x.n_sel), q=t(x.q))
+    if getattr(x, "pos0", None) is not None:  # prompt inputs
+        dev["pos0"] = t(x.pos0)
     return pool, dev

@@ -7,12 +7,13 @@
 // cell-major probabilities) are prior art; this kernel is laid out for
 // CDNA4 wave64 matrix cores instead.
 //
-// Workgroup = one (instance, chunk) with RB + 1 waves: compute wave w < RB =
-// ceil(rows / 16) owns query rows [16w, 16w + 16) for the whole chunk, so
-// every softmax statistic of a row lives in one wave; the last wave is the
-// producer: it runs the gather and stages all code rows (the compute waves
-// issue no global loads and hold no staging registers).  Cells are processed
-// in tiles of 64.
+// Workgroup = one (instance, chunk) -- or several consecutive chunks of one
+// instance when the grid is large -- with DS * RB + 1 waves: compute wave w
+// owns query rows [16 (w / DS), 16 (w / DS) + 16) for the whole chunk (and
+// 256 / DS of the head dimensions), so every softmax statistic of a row
+// lives in one wave; the last wave is the producer: it runs the gather and
+// stages all code rows (the compute waves issue no global loads and hold no
+// staging registers).  Cells are processed in tiles of 64.
 //
 // Exactness of the contractions.  The INT8 codes are used as they are; the
 // fp32 operands are split into int8 digits so that the int8 MFMA (exact
@@ -108,13 +109,261 @@ __device__ __forceinline__ float wave_max(float x) {
 // 16 lanes) each touch 8 distinct 16-byte bank groups.
 __device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (4 * (cb & 1))); }
 
+// The state of one compute wave: query digits, per-lane LDS offsets, and the
+// running softmax statistics and accumulator of its 16 query rows (for the
+// head dimensions [256 dh / DS, 256 (dh + 1) / DS) it owns, kDB = 16 / DS
+// blocks of 16).  step() is one tile; both kernels run exactly this sequence
+// per chunk, so a chunk's partial does not depend on the kernel or launch.
+template <int kDB>
+struct RowBlock {
+    v4i qa[4], qb[4], qc[4];  // query digits: B operands of S^T = K Q^T
+    float coef;  // sigma * |scale_log2| / 2^8: S (base 2) = coef * (AB + C / 2^8) * k_scale
+    int k_off0, k_off1, v_off, m_off0, m_off1;
+    float m_run;   // running max of this lane's row (base-2 units)
+    float l_part;  // this lane's share of the row denominator
+    float frame;   // O = frame * o
+    v4f o[kDB];    // O^T[16 (kDB dh + db) + 4g + u][row] / frame
+    v4f su[4];     // scores of the tile the softmax runs on next: u, S = coef * u
+
+    // qrow: this lane's query row (nullptr for a row past the end; its
+    // digits are 0), read at dims 64s + 16g + e (byte e of slab s).  The sign
+    // of the softmax scale is folded into the digits so that coef >= 0 and
+    // max commutes with it.
+    __device__ __forceinline__ void init(const float *qrow, float scale_log2, int g, int l16) {
+        v4f qv[4][4];
+        float mx = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                qv[s][w] = (v4f){0.f, 0.f, 0.f, 0.f};
+                if (qrow) qv[s][w] = *reinterpret_cast<const v4f *>(qrow + 64 * s + 16 * g + 4 * w);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(qv[s][w][u]));
+            }
+        mx = wave_max(mx);
+        const float inv = mx > 0.f ? (scale_log2 < 0.f ? -65536.f : 65536.f) * 127.f / mx : 0.f;
+        // clamped away from 0 so that masked cells (-inf) never meet a zero factor
+        coef = fmaxf((mx / 127.f) * fabsf(scale_log2) * (1.f / 256.f), 1e-30f);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                unsigned pa = 0, pb = 0, pc = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    // X = round(q * 127 * 2^16 / max) = 2^16 a + 2^8 b + c, balanced digits
+                    const int X = (int)rintf(qv[s][w][u] * inv);
+                    const int dc = __builtin_amdgcn_sbfe(X, 0, 8);
+                    const int X1 = (X - dc) >> 8;
+                    const int db = __builtin_amdgcn_sbfe(X1, 0, 8);
+                    const int da = (X1 - db) >> 8;
+                    pa |= ((unsigned)da & 0xffu) << (8 * u);
+                    pb |= ((unsigned)db & 0xffu) << (8 * u);
+                    pc |= ((unsigned)dc & 0xffu) << (8 * u);
+                }
+                qa[s][w] = (int)pa;
+                qb[s][w] = (int)pb;
+                qc[s][w] = (int)pc;
+            }
+        }
+        // per-lane constant LDS offsets (everything else is an immediate):
+        // K operand of cell block cb, slab s: row lds_row(cb, l16), bytes 64s + 16g
+        k_off0 = lds_row(0, l16) * kStride + 16 * g;
+        k_off1 = (lds_row(1, l16) - 16) * kStride + 16 * g;
+        // transposed V read: source role (b, h) = (l16 >> 1, l16 & 1) reads row
+        // lds_row(2r + (b >> 2), 4g + (b & 3)), bytes 16db + 8h
+        const int tb = l16 >> 1, th = l16 & 1;
+        v_off = (16 * (tb >> 2) + 4 * (g ^ (tb >> 2)) + (tb & 3)) * kStride + 8 * th;
+        // this lane's S cells (cb, 4g + u) live in LDS rows 16cb + 4(g ^ (cb & 1)) + u
+        m_off0 = 4 * g;
+        m_off1 = 4 * (g ^ 1);
+        reset();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+
+    __device__ __forceinline__ void reset() {
+        m_run = -INFINITY;
+        l_part = 0.f;
+        frame = 1.f;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+
+    // One tile: the softmax and V accumulation of the tile whose scores are
+    // in su (V rows vb, V scales vs, largest V scale vmax), and the scores of
+    // the next tile (K rows kb, K scales ks, bias 0 or -inf per cell) into su,
+    // or -inf everywhere when next_ok is false.  kCausal: cells of the next
+    // tile past index lim (this lane's row's last visible cell, counted from
+    // the tile's first cell) are masked too.
+    template <bool kCausal = false>
+    __device__ __forceinline__ void step(const int8_t *kb, const float *ks_t, const float *bias_t,
+                                         bool next_ok, const int8_t *vb, const float *vs_t,
+                                         float vmax, int dh, int lim = 0) {
+        // ---------------- softmax statistics of the current tile (scores in su)
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) tmax = fmaxf(tmax, su[cb][u]);
+        tmax = max4(tmax);
+        tmax = (tmax == -INFINITY) ? -INFINITY : tmax * coef;  // base-2 tile max
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+        const float frame_new = (m_run == -INFINITY) ? 1.f : frame * corr;
+        m_run = m_new;
+        // W = 256 / tau; X = rint(p * v_scale * W) lands in the low bits of
+        // fma(p, v_scale * W, 2^23)
+        const bool live = tmax != -INFINITY && vmax > 0.f && (m_use - tmax) < kFarBelow;
+        const float W = live ? (256.f * 127.f) * __builtin_amdgcn_rcpf(vmax) *
+                                   __builtin_amdgcn_exp2f(m_use - tmax)
+                             : 0.f;
+
+        // ---------------- scores of the next tile: u = (AB + C/2^8) * k_scale + bias
+        v4f sn[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
+            v4i ka[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
+            v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                aa = mfma_i8(ka[s], qa[s], aa);
+                bb = mfma_i8(ka[s], qb[s], bb);
+                cc = mfma_i8(ka[s], qc[s], cc);
+            }
+            const v4i ab = (aa << 8) + bb;  // 2^8 A + B, |.| < 2^30
+            const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
+            const v4f ks = *reinterpret_cast<const v4f *>(ks_t + mo);
+            const v4f bs = *reinterpret_cast<const v4f *>(bias_t + mo);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
+                sn[cb][u] = next_ok ? fmaf(tq, ks[u], bs[u]) : -INFINITY;
+            }
+        }
+        if constexpr (kCausal) {
+            if (__any(lim < kTile - 1)) {  // only tiles that reach past some row's position
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (mo + u > lim) sn[cb][u] = -INFINITY;
+                }
+            }
+        }
+
+        // ---------------- probabilities and their digits for the current tile
+        float psum = 0.f;
+        v4i xa, xb;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
+            const v4f vs = *reinterpret_cast<const v4f *>(vs_t + mo);
+            unsigned xs[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -m_use));
+                psum += pr;
+                xs[u] = __float_as_uint(fmaf(pr, vs[u] * W, kRound));
+            }
+            // low digit = byte 0 of X; high digit = byte 1 of X + 128
+            const unsigned lo01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
+            const unsigned lo23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
+            const unsigned hi01 = __builtin_amdgcn_perm(xs[1] + 128u, xs[0] + 128u, 0x0c0c0501u);
+            const unsigned hi23 = __builtin_amdgcn_perm(xs[3] + 128u, xs[2] + 128u, 0x05010c0cu);
+            xa[cb] = (int)(hi01 | hi23);
+            xb[cb] = (int)(lo01 | lo23);
+        }
+        l_part = fmaf(l_part, corr, psum);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
+
+        // rare: fold the frame into the accumulator before it gets too small
+        frame = frame_new;
+        if (__any(frame < kRenorm)) {
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) o[db] *= frame;
+            frame = 1.f;
+        }
+        const float tau2 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 256 / frame
+
+        // ---------------- O^T += V^T P^T for this wave's blocks of 16 dims
+        const int8_t *vp = vb + v_off + 16 * kDB * dh;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+            const v2i h0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)(vp + 16 * db));
+            const v2i h1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (v2i LDS_AS *)(vp + 32 * kStride + 16 * db));
+            const v4i va = {h0[0], h0[1], h1[0], h1[1]};
+            const v4i hi = mfma_i8(va, xa, (v4i){0, 0, 0, 0});
+            const v4i lo = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
+            const v4i acc = (hi << 8) + lo;  // sum of X * v_code, exact
+#pragma unroll
+            for (int u = 0; u < 4; ++u) o[db][u] = fmaf((float)acc[u], tau2, o[db][u]);
+        }
+    }
+
+    // The chunk partial of this lane's row at unit index base (instance,
+    // chunk, row) of the workspace.  Every lane of the wave must call it.
+    __device__ __forceinline__ void emit(const Params &p, int64_t base, int row, int g, int dh) {
+        const float l_row = sum4(l_part);
+        if (row < p.n_rows) {
+            float *dst = p.acc + base * kDim + 16 * kDB * dh + 4 * g;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
+            if (g == 0 && dh == 0) {
+                // base-2 maximum back to natural-log units
+                p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
+                p.l[base] = l_row;
+            }
+        }
+    }
+
+    // The normalised result of this lane's row (out_row nullptr: a row past
+    // the end), with the operations the merge applies to a single partial:
+    // out = acc * (1 / l), lse = m + ln l; no visible cell: out = 0,
+    // lse = -inf.  Every lane of the wave must call it.
+    __device__ __forceinline__ void finish(float *out_row, float *lse_row, int g, int dh) {
+        const float l_row = sum4(l_part);
+        if (!out_row) return;
+        float *dst = out_row + 16 * kDB * dh + 4 * g;
+        if (!(l_row > 0.f)) {
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+                *reinterpret_cast<v4f *>(dst + 16 * db) = (v4f){0.f, 0.f, 0.f, 0.f};
+            if (g == 0 && dh == 0) *lse_row = -INFINITY;
+            return;
+        }
+        const float inv = 1.f / l_row;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+            *reinterpret_cast<v4f *>(dst + 16 * db) = (o[db] * frame) * inv;
+        if (g == 0 && dh == 0) *lse_row = m_run * 0.69314718055994531f + logf(l_row);
+    }
+};
+
 // DS = number of compute waves per 16-row group, each accumulating
 // O^T for 256 / DS of the head dimensions (every one of them scores the
 // whole tile).  DS = 1: two workgroups per CU (LDS-limited; with RB = 1 that
 // is one wave per SIMD), for grids that fill the chip.  DS = 2: half the
 // V accumulation per wave, which shortens each step of a small,
 // latency-bound grid (one workgroup per CU).
-template <int RB, int DS>
+//
+// kPrompt = false: decode.  Workgroup (blockIdx.x, blockIdx.y) = instance i,
+// chunks [cpw * y, cpw * y + cpw) of its list; emits chunk partials.
+// kPrompt = true: prompt attention.  Workgroup (i, y) = the 16 RB query rows
+// starting at row 16 RB y of instance i (rows are position-major, so a
+// workgroup holds a few consecutive positions); the cell list is implicit
+// (logical cells 0, 1, 2, ... up to the workgroup's last position), each
+// row masks the cells past its own position, and the rows are normalised in
+// place of a partial (one chunk spans the whole causal range).
+template <int RB, int DS, bool kPrompt>
 __global__ __launch_bounds__(64 * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu((RB == 1 || DS > 1) ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p, int cpw) {
@@ -134,17 +383,31 @@ void chunk_mfma_kernel(Params p, int cpw) {
     const int g = lane >> 4;    // lane group: k-set of the MFMA operands
     const int l16 = lane & 15;  // this lane's row within the wave's 16 rows
     const int i = blockIdx.x;   // instance (fastest: full chunks are dispatched first)
-    // This workgroup runs chunks [c0, c0 + cpw) of instance i as one stream
-    // of tiles: the gather pipeline runs on across chunk boundaries, and the
-    // compute waves emit a partial at the end of each chunk.
-    const int c0 = blockIdx.y * cpw;
-    const int n = count_of(p, i);
-    const int j_begin = c0 * p.chunk;
-    if (j_begin >= n) return;  // this instance has fewer chunks
-    const int j_end = (int)min((int64_t)j_begin + (int64_t)cpw * p.chunk, (int64_t)n);
-    const int n_tiles = (j_end - j_begin + kTile - 1) / kTile;
-    const int tpc = p.chunk / kTile;  // tiles per chunk
     const int R = p.n_rows;
+    int c0 = 0, j_begin = 0, j_end, tpc, row0 = 0;
+    int64_t pos0 = 0;
+    if constexpr (!kPrompt) {
+        // This workgroup runs chunks [c0, c0 + cpw) of instance i as one
+        // stream of tiles: the gather pipeline runs on across chunk
+        // boundaries, and the compute waves emit a partial at the end of
+        // each chunk.
+        c0 = blockIdx.y * cpw;
+        const int n = count_of(p, i);
+        j_begin = c0 * p.chunk;
+        if (j_begin >= n) return;  // this instance has fewer chunks
+        j_end = (int)min((int64_t)j_begin + (int64_t)cpw * p.chunk, (int64_t)n);
+        tpc = p.chunk / kTile;  // tiles per chunk
+    } else {
+        // rows [row0, row0 + 16 RB) sit at positions pos0 + r / n_qheads; the
+        // cells run to the last of them, clipped to the page table
+        row0 = blockIdx.y * (16 * RB);
+        pos0 = p.pos0[i];
+        const int last_row = min(row0 + 16 * RB, R) - 1;
+        const int64_t last = pos0 + last_row / p.n_qheads;
+        j_end = (int)max((int64_t)0, min(last + 1, (int64_t)p.n_logical_pages * kPage));
+        tpc = 1 << 30;  // one chunk: no partial inside the loop
+    }
+    const int n_tiles = (j_end - j_begin + kTile - 1) / kTile;
 
     // scale slots read before their first write hold finite values
     for (int e = threadIdx.x; e < 4 * kTile; e += 64 * (DS * RB + 1)) {
@@ -182,7 +445,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
             const unsigned kh2 = p.k_scales[sc2];
             const unsigned vh2 = p.v_scales[sc2];
             const int pte3 = pt_or_sel[id_ok ? lp3 : 0];
-            const int sel4 = sel[j4 < j_end ? j4 : j_end - 1];
+            const int sel4 = kPrompt ? j4 : sel[j4 < j_end ? j4 : j_end - 1];
             // then the code rows: load (k, c) covers rows 16k + l16, bytes
             // 64c + 16g, so each lane needs the physical cells of 4 rows only
             // (one 16-byte LDS read) and every load uses an immediate offset
@@ -240,7 +503,8 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 if (id_ok && pte3 >= 0 && (int64_t)pte3 < p.n_phys_pages) ph = (pte3 << 4) | (sel3 & 15);
                 phys_s[(t + 3) & 3][4 * l16 + g] = ph;  // cell 16g + l16
                 const int j3 = j_begin + (t + 3) * kTile + lane;
-                if (p.gather_out && j3 < j_end) p.gather_out[(int64_t)i * p.sel_stride + j3] = ph;
+                if (!kPrompt && p.gather_out && j3 < j_end)
+                    p.gather_out[(int64_t)i * p.sel_stride + j3] = ph;
                 ph2 = ph;
             }
             sel3 = (ld_s && j4 < j_end) ? sel4 : -1;
@@ -252,216 +516,47 @@ void chunk_mfma_kernel(Params p, int cpw) {
     // ======================= compute waves =======================
     const int row = (wave / DS) * 16 + l16;  // this lane's query row
     const int dh = wave % DS;                // its share of the head dimensions
-    // ---- query digits: B operands of S^T = K Q^T for rows 16*wave + l16,
-    // dims 64s + 16g + e (byte e of slab s).  The sign of the softmax scale is
-    // folded into the digits so that coef >= 0 and max commutes with it.
-    v4i qa[4], qb[4], qc[4];
-    float coef;  // sigma * |scale_log2| / 2^8: S (base 2) = coef * (AB + C / 2^8) * k_scale
-    {
-        v4f qv[4][4];
-        float mx = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                qv[s][w] = (v4f){0.f, 0.f, 0.f, 0.f};
-                if (row < R)
-                    qv[s][w] = *reinterpret_cast<const v4f *>(
-                        p.q + ((int64_t)i * R + row) * kDim + 64 * s + 16 * g + 4 * w);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(qv[s][w][u]));
-            }
-        mx = wave_max(mx);
-        const float inv = mx > 0.f ? (p.scale_log2 < 0.f ? -65536.f : 65536.f) * 127.f / mx : 0.f;
-        // clamped away from 0 so that masked cells (-inf) never meet a zero factor
-        coef = fmaxf((mx / 127.f) * fabsf(p.scale_log2) * (1.f / 256.f), 1e-30f);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                unsigned pa = 0, pb = 0, pc = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    // X = round(q * 127 * 2^16 / max) = 2^16 a + 2^8 b + c, balanced digits
-                    const int X = (int)rintf(qv[s][w][u] * inv);
-                    const int dc = __builtin_amdgcn_sbfe(X, 0, 8);
-                    const int X1 = (X - dc) >> 8;
-                    const int db = __builtin_amdgcn_sbfe(X1, 0, 8);
-                    const int da = (X1 - db) >> 8;
-                    pa |= ((unsigned)da & 0xffu) << (8 * u);
-                    pb |= ((unsigned)db & 0xffu) << (8 * u);
-                    pc |= ((unsigned)dc & 0xffu) << (8 * u);
-                }
-                qa[s][w] = (int)pa;
-                qb[s][w] = (int)pb;
-                qc[s][w] = (int)pc;
-            }
-        }
-    }
-
-    // ---- per-lane constant LDS offsets (everything else is an immediate)
-    // K operand of cell block cb, slab s: row lds_row(cb, l16), bytes 64s + 16g
-    const int k_off0 = lds_row(0, l16) * kStride + 16 * g;
-    const int k_off1 = (lds_row(1, l16) - 16) * kStride + 16 * g;
-    // transposed V read: source role (b, h) = (l16 >> 1, l16 & 1) reads row
-    // lds_row(2r + (b >> 2), 4g + (b & 3)), bytes 16db + 8h
-    const int tb = l16 >> 1, th = l16 & 1;
-    const int v_off = (16 * (tb >> 2) + 4 * (g ^ (tb >> 2)) + (tb & 3)) * kStride + 8 * th;
-    // this lane's S cells (cb, 4g + u) live in LDS rows 16cb + 4(g ^ (cb & 1)) + u
-    const int m_off0 = 4 * g, m_off1 = 4 * (g ^ 1);
-
-    float m_run = -INFINITY;  // running max of this lane's row (base-2 units)
-    float l_part = 0.f;       // this lane's share of the row denominator
-    float frame = 1.f;        // O = frame * o
-    v4f o[kDB];               // O^T[16 (kDB dh + db) + 4g + u][row] / frame
-#pragma unroll
-    for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
-    v4f su[4];  // scores of the tile the softmax runs on next: u, S = coef * u
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-
+    RowBlock<kDB> rb;
+    const int64_t grow = (int64_t)i * R + row0 + row;  // row in [n_inst][n_rows]
+    const bool row_ok = row0 + row < R;
+    rb.init(row_ok ? p.q + grow * kDim : nullptr, p.scale_log2, g, l16);
+    // prompt: this row's last visible cell (its position)
+    const int64_t lim_row = kPrompt ? pos0 + (row0 + row) / p.n_qheads : 0;
     for (int t = -4; t < n_tiles; ++t) {
         if (t >= -1) {
-            // Both halves run every iteration (no validity branches, so the
-            // scheduler can interleave them); a tile outside [0, n_tiles) has
-            // all scores at -inf and changes nothing.
+            // Both halves of a step run every iteration (no validity branches,
+            // so the scheduler can interleave them); a tile outside
+            // [0, n_tiles) has all scores at -inf and changes nothing.
             const bool next_ok = (t + 1 >= 0) && (t + 1 < n_tiles);
             const int b1 = (t + 1) & 1, m1 = (t + 1) & 3;
             const int b0 = t & 1, m0 = t & 3;
-
-            // ---------------- softmax statistics of tile t (scores in su)
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) tmax = fmaxf(tmax, su[cb][u]);
-            tmax = max4(tmax);
-            tmax = (tmax == -INFINITY) ? -INFINITY : tmax * coef;  // base-2 tile max
-            const float m_new = fmaxf(m_run, tmax);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-            const float frame_new = (m_run == -INFINITY) ? 1.f : frame * corr;
-            m_run = m_new;
-            // W = 256 / tau; X = rint(p * v_scale * W) lands in the low bits of
-            // fma(p, v_scale * W, 2^23)
-            const float vmax = vmax_s[m0];
-            const bool live = tmax != -INFINITY && vmax > 0.f && (m_use - tmax) < kFarBelow;
-            const float W = live ? (256.f * 127.f) * __builtin_amdgcn_rcpf(vmax) *
-                                       __builtin_amdgcn_exp2f(m_use - tmax)
-                                 : 0.f;
-
-            // ---------------- scores of tile t+1: u = (AB + C/2^8) * k_scale + bias
-            v4f sn[4];
-            {
-                const int8_t *kb = kbuf[b1];
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
-                    v4i ka[4];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
-                    v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        aa = mfma_i8(ka[s], qa[s], aa);
-                        bb = mfma_i8(ka[s], qb[s], bb);
-                        cc = mfma_i8(ka[s], qc[s], cc);
-                    }
-                    const v4i ab = (aa << 8) + bb;  // 2^8 A + B, |.| < 2^30
-                    const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
-                    const v4f ks = *reinterpret_cast<const v4f *>(&ks_s[m1][mo]);
-                    const v4f bs = *reinterpret_cast<const v4f *>(&bias_s[m1][mo]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
-                        sn[cb][u] = next_ok ? fmaf(tq, ks[u], bs[u]) : -INFINITY;
-                    }
-                }
+            if constexpr (kPrompt) {
+                // the scores of tile t + 1, whose first cell is j_begin + 64 (t + 1)
+                const int64_t lim = lim_row - (j_begin + (int64_t)(t + 1) * kTile);
+                rb.template step<true>(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0],
+                                       vmax_s[m0], dh, (int)max((int64_t)-1, min(lim, (int64_t)kTile)));
+            } else {
+                rb.step(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0], vmax_s[m0], dh);
             }
-
-            // ---------------- probabilities and their digits for tile t
-            float psum = 0.f;
-            v4i xa, xb;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
-                const v4f vs = *reinterpret_cast<const v4f *>(&vs_s[m0][mo]);
-                unsigned xs[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -m_use));
-                    psum += pr;
-                    xs[u] = __float_as_uint(fmaf(pr, vs[u] * W, kRound));
-                }
-                // low digit = byte 0 of X; high digit = byte 1 of X + 128
-                const unsigned lo01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
-                const unsigned lo23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
-                const unsigned hi01 = __builtin_amdgcn_perm(xs[1] + 128u, xs[0] + 128u, 0x0c0c0501u);
-                const unsigned hi23 = __builtin_amdgcn_perm(xs[3] + 128u, xs[2] + 128u, 0x05010c0cu);
-                xa[cb] = (int)(hi01 | hi23);
-                xb[cb] = (int)(lo01 | lo23);
-            }
-            l_part = fmaf(l_part, corr, psum);
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
-
-            // rare: fold the frame into the accumulator before it gets too small
-            frame = frame_new;
-            if (__any(frame < kRenorm)) {
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) o[db] *= frame;
-                frame = 1.f;
-            }
-            const float tau2 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 256 / frame
-
-            // ---------------- O^T += V^T P^T for 16 blocks of 16 dims
-            const int8_t *vp = vbuf[b0] + v_off + 16 * kDB * dh;
-#pragma unroll
-            for (int db = 0; db < kDB; ++db) {
-                const v2i h0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)(vp + 16 * db));
-                const v2i h1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (v2i LDS_AS *)(vp + 32 * kStride + 16 * db));
-                const v4i va = {h0[0], h0[1], h1[0], h1[1]};
-                const v4i hi = mfma_i8(va, xa, (v4i){0, 0, 0, 0});
-                const v4i lo = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
-                const v4i acc = (hi << 8) + lo;  // sum of X * v_code, exact
-#pragma unroll
-                for (int u = 0; u < 4; ++u) o[db][u] = fmaf((float)acc[u], tau2, o[db][u]);
-            }
-
-            // ---------------- end of a chunk: emit its partial, start afresh
-            if (t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
-                const float l_row = sum4(l_part);
-                if (row < R) {
-                    const int64_t base = ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row;
-                    float *dst = p.acc + base * kDim + 16 * kDB * dh + 4 * g;
-#pragma unroll
-                    for (int db = 0; db < kDB; ++db)
-                        *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
-                    if (g == 0 && dh == 0) {
-                        // base-2 maximum back to natural-log units
-                        p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
-                        p.l[base] = l_row;
-                    }
-                }
-                m_run = -INFINITY;
-                l_part = 0.f;
-                frame = 1.f;
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
+            // end of a chunk: emit its partial, start afresh
+            if (!kPrompt && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
+                rb.emit(p, ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row, row, g, dh);
+                rb.reset();
             }
         }
         __syncthreads();
     }
+    if constexpr (kPrompt)
+        rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
 }
 
 template <int DS>
 void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
     switch ((p.n_rows + 15) / 16) {
-        case 1: chunk_mfma_kernel<1, DS><<<grid, 64 * (DS + 1), 0, s>>>(p, cpw); break;
-        case 2: chunk_mfma_kernel<2, DS><<<grid, 64 * (2 * DS + 1), 0, s>>>(p, cpw); break;
-        case 3: chunk_mfma_kernel<3, 1><<<grid, 64 * 4, 0, s>>>(p, cpw); break;
-        default: chunk_mfma_kernel<4, 1><<<grid, 64 * 5, 0, s>>>(p, cpw); break;
+        case 1: chunk_mfma_kernel<1, DS, false><<<grid, 64 * (DS + 1), 0, s>>>(p, cpw); break;
+        case 2: chunk_mfma_kernel<2, DS, false><<<grid, 64 * (2 * DS + 1), 0, s>>>(p, cpw); break;
+        case 3: chunk_mfma_kernel<3, 1, false><<<grid, 64 * 4, 0, s>>>(p, cpw); break;
+        default: chunk_mfma_kernel<4, 1, false><<<grid, 64 * 5, 0, s>>>(p, cpw); break;
     }
 }
 
@@ -483,6 +578,19 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
         launch_rb<2>(p, grid, cpw, s);
     else
         launch_rb<1>(p, grid, cpw, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_prompt(const Params &p, hipStream_t s) {
+    // 64 rows (four 16-row groups) per workgroup; fewer rows use fewer groups
+    const int rb = p.n_rows >= 64 ? 4 : (p.n_rows + 15) / 16;
+    const dim3 grid(p.n_inst, (p.n_rows + 16 * rb - 1) / (16 * rb));
+    switch (rb) {
+        case 1: chunk_mfma_kernel<1, 1, true><<<grid, 64 * 2, 0, s>>>(p, 1); break;
+        case 2: chunk_mfma_kernel<2, 1, true><<<grid, 64 * 3, 0, s>>>(p, 1); break;
+        case 3: chunk_mfma_kernel<3, 1, true><<<grid, 64 * 4, 0, s>>>(p, 1); break;
+        default: chunk_mfma_kernel<4, 1, true><<<grid, 64 * 5, 0, s>>>(p, 1); break;
+    }
     return hipGetLastError();
 }
 

@@ -44,12 +44,7 @@ int layout_of(int64_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim, i
 
 enum Passes { kChunk = 1, kMerge = 2, kBoth = 3 };
 
-int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
-        int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
-        const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
-        int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
-        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream,
-        int passes = kBoth) {
+int check_pool(const sda_pool *pool) {
     if (!pool) return SDA_ERR_INVALID_ARG;
     if (pool->page_size != SDA_PAGE_SIZE || pool->head_dim != SDA_HEAD_DIM)
         return SDA_ERR_UNSUPPORTED;
@@ -62,8 +57,28 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     if (!aligned(pool->k_codes, 16) || !aligned(pool->v_codes, 16) ||
         !aligned(pool->k_scales, 2) || !aligned(pool->v_scales, 2))
         return SDA_ERR_INVALID_ARG;
+    return SDA_OK;
+}
+
+void set_pool(sda::Params *p, const sda_pool *pool) {
+    p->k_codes = pool->k_codes;
+    p->k_scales = pool->k_scales;
+    p->v_codes = pool->v_codes;
+    p->v_scales = pool->v_scales;
+    p->scale_stride = pool->scale_stride;
+    p->n_phys_pages = pool->n_phys_pages;
+}
+
+int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
+        int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
+        const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
+        int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
+        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream,
+        int passes = kBoth) {
+    int st = check_pool(pool);
+    if (st != SDA_OK) return st;
     Layout L;
-    int st = layout_of(n_inst, n_q, n_qheads, pool->head_dim, max_sel, chunk_cells, &L);
+    st = layout_of(n_inst, n_q, n_qheads, pool->head_dim, max_sel, chunk_cells, &L);
     if (st != SDA_OK) return st;
     if (n_logical_pages < 0 || pt_stride < n_logical_pages || sel_stride < max_sel)
         return SDA_ERR_INVALID_ARG;
@@ -79,12 +94,7 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
 
     sda::Params p;
     memset(&p, 0, sizeof p);
-    p.k_codes = pool->k_codes;
-    p.k_scales = pool->k_scales;
-    p.v_codes = pool->v_codes;
-    p.v_scales = pool->v_scales;
-    p.scale_stride = pool->scale_stride;
-    p.n_phys_pages = pool->n_phys_pages;
+    set_pool(&p, pool);
     p.page_table = page_table;
     p.pt_stride = pt_stride;
     p.n_logical_pages = n_logical_pages;
@@ -188,6 +198,40 @@ int sda_merge_batch(int32_t n_inst, int32_t n_q, int32_t n_qheads, const int32_t
     p.lse = lse;
     (void)hipGetLastError();
     if (sda::launch_merge(p, static_cast<hipStream_t>(stream)) != hipSuccess) return SDA_ERR_LAUNCH;
+    return SDA_OK;
+}
+
+int sda_prompt_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                          int64_t pt_stride, int32_t n_logical_pages, const int32_t *pos0,
+                          const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
+                          float *out, float *lse, void *stream) {
+    int st = check_pool(pool);
+    if (st != SDA_OK) return st;
+    if (n_inst < 0 || n_q < 1 || n_qheads < 1) return SDA_ERR_INVALID_ARG;
+    if ((int64_t)n_q * n_qheads > SDA_PROMPT_MAX_ROWS) return SDA_ERR_UNSUPPORTED;
+    if (n_logical_pages < 1 || pt_stride < n_logical_pages) return SDA_ERR_INVALID_ARG;
+    if (!isfinite(softmax_scale)) return SDA_ERR_INVALID_ARG;
+    if (n_inst == 0) return SDA_OK;
+    if (!page_table || !pos0 || !q || !aligned(q, 16) || !out || !aligned(out, 16) || !lse ||
+        !aligned(lse, 4))
+        return SDA_ERR_INVALID_ARG;
+    sda::Params p;
+    memset(&p, 0, sizeof p);
+    set_pool(&p, pool);
+    p.page_table = page_table;
+    p.pt_stride = pt_stride;
+    p.n_logical_pages = n_logical_pages;
+    p.q = q;
+    p.n_inst = n_inst;
+    p.n_rows = n_q * n_qheads;
+    p.n_qheads = n_qheads;
+    p.pos0 = pos0;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.out = out;
+    p.lse = lse;
+    (void)hipGetLastError();
+    if (sda::launch_prompt(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SDA_ERR_LAUNCH;
     return SDA_OK;
 }
 

@@ -43,6 +43,9 @@ struct Params {
     int32_t *gather_out;       // nullable [n_inst][sel_stride]
     float *out;                // [n_inst][n_rows][kDim]
     float *lse;                // [n_inst][n_rows]
+    // prompt attention: rows r = t * n_qheads + h sit at position pos0[i] + t
+    const int32_t *pos0;       // device [n_inst]
+    int32_t n_qheads;
 };
 
 // IEEE binary16 bit pattern -> float (exact).
@@ -59,5 +62,6 @@ __device__ __forceinline__ int count_of(const Params &p, int i) {
 
 hipError_t launch_chunk(const Params &p, hipStream_t s);
 hipError_t launch_merge(const Params &p, hipStream_t s);
+hipError_t launch_prompt(const Params &p, hipStream_t s);
 
 }  // namespace sda

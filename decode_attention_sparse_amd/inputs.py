@@ -224,7 +224,7 @@ def make_prompt(name: str | None = None, seed: int | None = None, pos0=None,
                 **overrides) -> PromptInputs:
     """Pools, permuted page tables and queries drawn exactly as make() draws
     them (no selection list); pos0 defaults to pool_cells - n_q."""
-    spec = dict(PROMPT_CONFIGS[name]) if name is not None else {}
+    spec = dict(PROMPT_CONFIGS[name]) if name is not None else {"n_inst": 1}
     spec.update(overrides)
     spec.update(sel="all", n_sel=0, chunk=64)
     spec.setdefault("workload", name or "custom_prompt")

@@ -60,6 +60,7 @@ extern "C" {
 #define SDA_MAX_ROWS 64  /* n_q * n_qheads limit */
 #define SDA_CHUNK_ALIGN 64 /* chunk_cells must be a positive multiple of this */
 #define SDA_MAX_CHUNKS 65535 /* ceil(max_sel / chunk_cells) limit (one grid dimension) */
+#define SDA_PROMPT_MAX_ROWS 4194240 /* n_q * n_qheads limit of sda_prompt_attn_batch (65535 x 64) */
 
 typedef enum {
     SDA_OK = 0,
@@ -181,6 +182,39 @@ int sda_chunk_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_ta
 int sda_merge_batch(int32_t n_inst, int32_t n_q, int32_t n_qheads, const int32_t *n_sel,
                     int32_t max_sel, int32_t chunk_cells, const void *workspace,
                     size_t workspace_bytes, float *out, float *lse, void *stream);
+
+/* Prompt (many-query) attention over the same pools: a chunk of n_q
+ * consecutive query positions per instance, every position attending
+ * causally to the instance's logical cells up to and including its own.
+ * Strata PR #2220 page, closing note: the prompt attention's parity test
+ * takes the decode kernel as its reference (INT8 32K-cell context, 2,048
+ * queries per prompt chunk).  Each (position, query head) row is therefore
+ * the decode definition at the top of this header with the selection
+ * 0, 1, ..., p, where p = pos0[i] + t is the row's position:
+ *
+ *   out[i][t][h], lse[i][t][h] = decode result of q[i][t][h] over logical
+ *   cells 0..p of instance i (cells at or past 16 * n_logical_pages and cells
+ *   on pages with id -1 or outside [0, n_phys_pages) are masked; a row with
+ *   no unmasked cell, e.g. p < 0, gets out = 0, lse = -inf).
+ *
+ *   pool          host pointer to the pool descriptor (as above)
+ *   n_inst        host, >= 0 (0: nothing is launched)
+ *   page_table    int32 [n_inst][pt_stride], n_logical_pages >= 1 used per row
+ *   pos0          DEVICE int32 [n_inst]: position of query 0 of each instance
+ *                 (read on the device, so a captured graph replays with new
+ *                 positions)
+ *   q             float [n_inst][n_q][n_qheads][head_dim], 16-byte aligned
+ *   n_q, n_qheads host; >= 1, n_q * n_qheads <= SDA_PROMPT_MAX_ROWS
+ *   softmax_scale host, finite
+ *   out           float [n_inst][n_q][n_qheads][head_dim], 16-byte aligned
+ *   lse           float [n_inst][n_q][n_qheads]
+ *   stream        hipStream_t (NULL = default stream)
+ * No workspace: one kernel computes each row over its whole causal range.
+ * Returns SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED or SDA_ERR_LAUNCH. */
+int sda_prompt_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                          int64_t pt_stride, int32_t n_logical_pages, const int32_t *pos0,
+                          const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
+                          float *out, float *lse, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *sda_status_string(int status);

@@ -50,3 +50,16 @@ def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda", interleave=Fa
                                dev["q"], x.softmax_scale, chunk, out, lse, gather_out=g)
     torch.cuda.synchronize()
     return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)
+
+
+def run_prompt(x, device="cuda", interleave=False):
+    """Upload prompt inputs and run sda_prompt_attn_batch; returns numpy out
+    [n_inst][n_q][n_qheads][D] and lse [n_inst][n_q][n_qheads]."""
+    import torch
+    from decode_attention_sparse_amd import api
+    pool, dev = api.to_device(x, device, interleave_scales=interleave)
+    out = torch.full(x.q.shape, float("nan"), device=device)
+    lse = torch.full(x.q.shape[:3], float("nan"), device=device)
+    api.prompt_attn_batch(pool, dev["page_table"], dev["pos0"], dev["q"], x.softmax_scale, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()

@@ -47,7 +47,8 @@ def test_header_constants_match_binding():
     defs = dict(re.findall(r"#define SDA_(\w+) (\d+)", text))
     assert {k: int(v) for k, v in defs.items()} == {
         "PAGE_SIZE": api.PAGE_SIZE, "HEAD_DIM": api.HEAD_DIM, "MAX_ROWS": api.MAX_ROWS,
-        "CHUNK_ALIGN": api.CHUNK_ALIGN, "MAX_CHUNKS": api.MAX_CHUNKS}
+        "CHUNK_ALIGN": api.CHUNK_ALIGN, "MAX_CHUNKS": api.MAX_CHUNKS,
+        "PROMPT_MAX_ROWS": api.PROMPT_MAX_ROWS}
 
 
 def test_status_strings():
@@ -169,3 +170,32 @@ def test_batch_rejects_before_launch():
     assert call(n_inst=-1) == api.SDA_ERR_INVALID_ARG
     assert call(wsb=100) == api.SDA_ERR_WORKSPACE
     assert call(n_inst=0) == api.SDA_OK                  # nothing to do, nothing launched
+
+
+def test_prompt_rejects_before_launch():
+    lib = api.library()
+    p = _pool()
+    def call(pool=p, **kw):
+        a = dict(n_inst=2, pt=FAKE, pts=8, nlp=8, pos0=FAKE, q=FAKE, n_q=5, nh=12, scale=0.0625,
+                 out=FAKE, lse=FAKE)
+        a.update(kw)
+        return lib.sda_prompt_attn_batch(C.byref(pool) if pool is not None else None,
+                                         a["n_inst"], a["pt"], a["pts"], a["nlp"], a["pos0"],
+                                         a["q"], a["n_q"], a["nh"], a["scale"], a["out"],
+                                         a["lse"], None)
+    assert call(pool=None) == api.SDA_ERR_INVALID_ARG
+    assert call(pool=_pool(head_dim=128)) == api.SDA_ERR_UNSUPPORTED
+    assert call(pool=_pool(scale_stride=0)) == api.SDA_ERR_INVALID_ARG
+    assert call(n_inst=-1) == api.SDA_ERR_INVALID_ARG
+    assert call(n_q=0) == api.SDA_ERR_INVALID_ARG
+    assert call(nh=0) == api.SDA_ERR_INVALID_ARG
+    assert call(n_q=65535, nh=65) == api.SDA_ERR_UNSUPPORTED      # more rows than the grid holds
+    assert call(nlp=0) == api.SDA_ERR_INVALID_ARG                 # a prompt has cells
+    assert call(pts=7) == api.SDA_ERR_INVALID_ARG                 # pt_stride < n_logical_pages
+    assert call(scale=float("inf")) == api.SDA_ERR_INVALID_ARG
+    assert call(pt=None) == api.SDA_ERR_INVALID_ARG
+    assert call(pos0=None) == api.SDA_ERR_INVALID_ARG
+    assert call(q=FAKE + 4) == api.SDA_ERR_INVALID_ARG
+    assert call(out=FAKE + 8) == api.SDA_ERR_INVALID_ARG
+    assert call(lse=None) == api.SDA_ERR_INVALID_ARG
+    assert call(n_inst=0) == api.SDA_OK                           # nothing to do, nothing launched
