@@ -20,7 +20,9 @@ timed with HIP events on the launch stream; cpu_baseline = the
 fp64 CPU oracle on the same workload; "batched" = the three batched
 workloads (256 x 2,051 cells x 4 q, 64 x 16,384 x 2 q, 32 x 131,072 x 4 q)
 measured the same way with a cache flush between calls; the two passes are
-also timed as separate calls for reference.
+also timed as separate calls for reference; "prompt_attention" = the prompt
+workload of the same pages (32K-cell INT8 context, 2,048 causal queries x 12
+heads) through sda_prompt_attn_batch, with its matrix-core roofline.
 """
 from __future__ import annotations
 
@@ -274,6 +276,87 @@ def cpu_baseline(xs, budget_s):
                       f"2,051 cells each) in {el:.1f} s, fp64 C, OpenMP over query rows"}
 
 
+# Prompt attention over the same pools (Strata PR #2220 page, closing note:
+# the prompt attention parity test, INT8 32K context, 2,048 queries per
+# prompt chunk, its reference the decode kernel): ms per chunk on the RTX
+# 2080 Ti with the default and the v3 decode kernel (context, other hardware).
+PROMPT_PAGES_MS = {"default": 71.5, "v3": 36.0}
+INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak
+
+
+def prompt_ops(x):
+    """Algorithmic flops of one prompt call, and its (query row, visible
+    cell) pairs: q.k and p.v take 2 * 256 flops each per pair."""
+    limit = x.n_logical_pages * 16
+    p = x.pos0[:, None].astype(np.int64) + np.arange(x.n_q)[None, :]
+    pairs = int(np.clip(p + 1, 0, limit).sum()) * x.n_qheads
+    return 4 * 256 * pairs, pairs
+
+
+def prompt_case():
+    import torch
+    from decode_attention_sparse_amd import api, inputs
+    x = inputs.make_prompt("prompt_int8_32k_2048q")
+    pool, dev = api.to_device(x, interleave_scales=True)
+    out = torch.empty(x.q.shape, device="cuda")
+    lse = torch.empty(x.q.shape[:3], device="cuda")
+
+    def call():
+        api.prompt_attn_batch(pool, dev["page_table"], dev["pos0"], dev["q"], x.softmax_scale,
+                              out, lse)
+    return x, call
+
+
+def prompt_section(reps, cpu_seconds):
+    """The prompt workload: mean ms per call over a graph of `reps` calls
+    (HIP events on the launch stream), its MFMA roofline, and the oracle on a
+    bounded sample of positions."""
+    x, call = prompt_case()
+    for _ in range(3):
+        call()
+    g = graph_of(call, reps)
+    ms = time_graph(g, reps)
+    del g
+    flops, pairs = prompt_ops(x)
+    achieved = flops / (ms * 1e-3) / 1e12
+    d = {
+        "workload": x.workload,
+        "config": {"instances": x.n_inst, "n_q": x.n_q, "n_qheads": x.n_qheads, "head_dim": 256,
+                   "pool_cells": x.n_logical_pages * 16, "pos0": int(x.pos0[0]),
+                   "mask": "causal: query t sees logical cells 0..pos0 + t",
+                   "pool_layout": "int8 code rows; binary16 (K, V) scale pairs interleaved per cell"},
+        "ms_per_call": round(ms, 4),
+        "query_rows_x_visible_cells": pairs,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_MFMA_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4),
+                     "traffic": None, "kernel": "chunk_mfma_kernel (prompt form)",
+                     "algorithmic_flops_per_launch": flops, "launch_ms_mean": round(ms, 4),
+                     "note": "flops of the fp32-accurate products (q.k and p.v, 2 x 256 each per "
+                             "row and visible cell) against the int8 matrix peak that runs them; "
+                             "the digit splits issue 3 int8 products per q.k and 2 per p.v"},
+        "pages_2080ti_ms_per_chunk": PROMPT_PAGES_MS,
+        "speedup_vs_pages_v3": round(PROMPT_PAGES_MS["v3"] / ms, 2),
+        "timing": f"{reps} calls captured in one HIP graph, HIP events around its replay",
+    }
+    if cpu_seconds > 0:
+        import oracle
+        t_ids = np.linspace(0, x.n_q - 1, 64).astype(np.int64)
+        done, t0, k = 0, time.perf_counter(), 0
+        while k < t_ids.size and time.perf_counter() - t0 < cpu_seconds:
+            oracle.prompt_attend(x, 0, t_ids[k:k + 8])
+            done += int(np.sum(np.minimum(int(x.pos0[0]) + t_ids[k:k + 8] + 1,
+                                          x.n_logical_pages * 16))) * x.n_qheads
+            k += 8
+        el = time.perf_counter() - t0
+        d["cpu_baseline"] = {
+            "value": round(done / el, 1), "unit": "query rows x visible cells / s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "ms_per_call_extrapolated": round(pairs / (done / el) * 1e3, 1),
+            "sample": f"{k} of the {x.n_q} positions (12 rows each, evenly spaced) in {el:.1f} s, "
+                      f"fp64 C, OpenMP over rows"}
+    return d
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +373,10 @@ def main(argv=None):
                     help="chunk size for the 256-instance batched workload")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the measured HBM read ceilings (probes/gather_ceiling)")
+    ap.add_argument("--no-prompt", action="store_true",
+                    help="skip the prompt attention workload")
+    ap.add_argument("--only-prompt", action="store_true",
+                    help="only three eager prompt attention calls (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -300,7 +387,7 @@ def main(argv=None):
         return 2
     # measured read ceilings for the access shapes of the chunk pass; run as a
     # child process before this process touches the GPU
-    ceiling = None if (a.no_ceiling or a.only_batched) else gather_ceiling()
+    ceiling = None if (a.no_ceiling or a.only_batched or a.only_prompt) else gather_ceiling()
     import torch
     from decode_attention_sparse_amd import api, inputs
     api.library()
@@ -313,6 +400,14 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if a.only_prompt:
+        x, call = prompt_case()
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": x.workload, "calls": 3}), flush=True)
+        return 0
 
     if a.only_batched:
         flush = make_flush()
@@ -446,6 +541,15 @@ def main(argv=None):
             del c, x
             torch.cuda.empty_cache()
         result["batched"] = batched
+
+    # ---- prompt attention over the same pools (the next workload on the pages)
+    if not a.no_prompt:
+        d = prompt_section(20, 0.0 if a.no_cpu else a.cpu_seconds / 2)
+        result["prompt_attention"] = d
+        print(f"# {d['workload']}: {d['ms_per_call']} ms/call, {d['roofline']['achieved']} "
+              f"TFLOP/s ({d['roofline']['frac']*100:.1f}% of the int8 matrix peak)",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
 
     if not a.no_cpu:
         result["cpu_baseline"] = cpu_baseline(xs, a.cpu_seconds)

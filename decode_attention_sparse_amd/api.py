@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "libsda.so")
 
 SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_LAUNCH = 0, -1, -2, -3, -4
 PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN, MAX_CHUNKS = 16, 256, 64, 64, 65535
-PROMPT_MAX_ROWS = 65535 * 64
+PROMPT_MAX_ROWS = 65535 * 48
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
             "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_status_string")

@@ -582,8 +582,14 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
 }
 
 hipError_t launch_prompt(const Params &p, hipStream_t s) {
-    // 64 rows (four 16-row groups) per workgroup; fewer rows use fewer groups
-    const int rb = p.n_rows >= 64 ? 4 : (p.n_rows + 15) / 16;
+    // A compute wave holds about 250 VGPRs, so a SIMD runs two: a workgroup
+    // of four 16-row groups (five waves) runs alone on its CU, one of three
+    // groups (four waves) runs beside a second one.  Per CU the two forms
+    // have about the same throughput, so 64-row workgroups are used while
+    // they fit one to a CU, 48-row ones when the grid is larger (two to a
+    // CU), and fewer rows use fewer groups.
+    int rb = (p.n_rows + 15) / 16;
+    if (rb > 4) rb = (int64_t)p.n_inst * ((p.n_rows + 63) / 64) <= kLatencyWorkgroups ? 4 : 3;
     const dim3 grid(p.n_inst, (p.n_rows + 16 * rb - 1) / (16 * rb));
     switch (rb) {
         case 1: chunk_mfma_kernel<1, 1, true><<<grid, 64 * 2, 0, s>>>(p, 1); break;

@@ -60,7 +60,7 @@ extern "C" {
 #define SDA_MAX_ROWS 64  /* n_q * n_qheads limit */
 #define SDA_CHUNK_ALIGN 64 /* chunk_cells must be a positive multiple of this */
 #define SDA_MAX_CHUNKS 65535 /* ceil(max_sel / chunk_cells) limit (one grid dimension) */
-#define SDA_PROMPT_MAX_ROWS 4194240 /* n_q * n_qheads limit of sda_prompt_attn_batch (65535 x 64) */
+#define SDA_PROMPT_MAX_ROWS 3145680 /* n_q * n_qheads limit of sda_prompt_attn_batch (65535 x 48) */
 
 typedef enum {
     SDA_OK = 0,

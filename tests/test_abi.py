@@ -190,6 +190,7 @@ def test_prompt_rejects_before_launch():
     assert call(n_q=0) == api.SDA_ERR_INVALID_ARG
     assert call(nh=0) == api.SDA_ERR_INVALID_ARG
     assert call(n_q=65535, nh=65) == api.SDA_ERR_UNSUPPORTED      # more rows than the grid holds
+    assert call(n_q=api.PROMPT_MAX_ROWS + 1, nh=1) == api.SDA_ERR_UNSUPPORTED
     assert call(nlp=0) == api.SDA_ERR_INVALID_ARG                 # a prompt has cells
     assert call(pts=7) == api.SDA_ERR_INVALID_ARG                 # pt_stride < n_logical_pages
     assert call(scale=float("inf")) == api.SDA_ERR_INVALID_ARG

@@ -50,6 +50,9 @@ CASES = {
     "negative_pos0": (dict(n_q=10, pool_cells=256, pos0=-3, seed=9), []),
     "all_masked": (dict(n_q=6, pool_cells=128, seed=10), [(k, -1) for k in range(8)]),
     "three_instances": (dict(n_inst=3, n_q=9, pool_cells=1024, pos0=[100, 0, 700], seed=11), []),
+    # more than 256 workgroups of 64 rows: the launch takes 48-row workgroups
+    "many_instances_48row_groups": (dict(n_inst=300, n_q=6, pool_cells=256,
+                                         pos0=list(range(-5, 295)), seed=14), []),
 }
 
 
