@@ -48,8 +48,8 @@ PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary with the commands is in
 # profiles/chunk_mfma_kernel__hbm_bytes__pages_point_and_batched.md.  The
 # figures hold only for the kernel source they were taken on.
-CHUNK_TRAFFIC = {"sources_sha256": "7071f9f4bfaef7de808b35f336680c827d5749b04923a189b45d3a20d22be5d3",
-                 "fetch_bytes": 1_878_764, "write_bytes": 445_824}
+CHUNK_TRAFFIC = {"sources_sha256": "bed3b842f0efbd130fd4ea48d18f2d3a1f2b96cb8b20b8dcd1513ad8bb9145a9",
+                 "fetch_bytes": 1_883_068, "write_bytes": 445_824}
 TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                    "decode_attention_sparse_amd/csrc/sda_internal.h")
 
