@@ -51,7 +51,8 @@ PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 CHUNK_TRAFFIC = {"sources_sha256": "bed3b842f0efbd130fd4ea48d18f2d3a1f2b96cb8b20b8dcd1513ad8bb9145a9",
                  "fetch_bytes": 1_883_068, "write_bytes": 445_824}
 TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
-                   "decode_attention_sparse_amd/csrc/sda_internal.h")
+                   "decode_attention_sparse_amd/csrc/sda_internal.h",
+                   "decode_attention_sparse_amd/csrc/sda_api.hip")
 
 
 def chunk_traffic():
@@ -103,6 +104,7 @@ class Case:
         self.out = torch.empty((n_inst, n_q, nh, D), device="cuda")
         self.lse = torch.empty((n_inst, n_q, nh), device="cuda")
         self.ws = api.workspace(n_inst, n_q, nh, self.max_sel, chunk)
+        self.fused_chunk = api.fused_chunk_cells(n_inst, self.max_sel, chunk)
         self.chunk_bytes = algorithmic_bytes(x)  # the chunk kernel's
         self.bytes = self.chunk_bytes + out_bytes(x)  # one whole call
         self.cells = int(np.sum(x.n_sel))
@@ -115,14 +117,17 @@ class Case:
                                    d["q"], self.x.softmax_scale, self.chunk, self.out, self.lse,
                                    ws=self.ws)
 
-    def chunk_pass(self):
+    # The two kernels of a call, launched on their own exactly as the call
+    # launches them: at the chunk size the call uses (finer than the
+    # caller's for small grids, see sda_fused_chunk_cells).
+    def chunk_pass(self, chunk=None):
         d = self.dev
         self.api.chunk_batch(self.pool, d["page_table"], d["sel"], d["n_sel"], self.max_sel, d["q"],
-                             self.x.softmax_scale, self.chunk, self.ws)
+                             self.x.softmax_scale, chunk or self.fused_chunk, self.ws)
 
-    def merge_pass(self):
-        self.api.merge_batch(self.dev["n_sel"], self.max_sel, self.chunk, self.ws, self.out,
-                             self.lse)
+    def merge_pass(self, chunk=None):
+        self.api.merge_batch(self.dev["n_sel"], self.max_sel, chunk or self.fused_chunk, self.ws,
+                             self.out, self.lse)
 
 
 def time_calls(cases, iters, flush=None):
@@ -447,8 +452,10 @@ def main(argv=None):
     step_ms = e0.elapsed_time(e1) / a.steps
     del g_steps
     # per-call means, each call alone in a graph of K launches, and the two
-    # kernels of a call (sda_chunk_batch, sda_merge_batch) timed the same way
-    # on their own: the chunk kernel's mean launch duration feeds the roofline.
+    # kernels of a call (sda_chunk_batch, sda_merge_batch at the chunk size
+    # the call uses) timed the same way on their own: the chunk kernel's mean
+    # launch duration feeds the roofline.  The two passes at the caller's
+    # chunk size (256) are timed too, for reference.
     per_q = {}
     call_us_sum, bytes_sum = 0.0, 0
     for nq, c in zip((1, 2, 3, 4), cases):
@@ -461,9 +468,13 @@ def main(argv=None):
         g_m = graph_of(c.merge_pass, a.steps)
         mg_ms = time_graph(g_m, a.steps)
         del g_m
+        g_2 = graph_of(lambda: (c.chunk_pass(c.chunk), c.merge_pass(c.chunk)), a.steps)
+        two_ms = time_graph(g_2, a.steps)
+        del g_2
         per_q[f"q{nq}"] = {
-            "us_per_call": round(call_ms * 1e3, 3),
+            "us_per_call": round(call_ms * 1e3, 3), "call_chunk_cells": c.fused_chunk,
             "chunk_us": round(ch_ms * 1e3, 3), "merge_us": round(mg_ms * 1e3, 3),
+            f"two_passes_at_chunk_{c.chunk}_us": round(two_ms * 1e3, 3),
             "cells_per_s": round(c.cells / (call_ms * 1e-3), 1),
             "GBps_algorithmic": round(c.bytes / (call_ms * 1e-3) / 1e9, 1),
             "pages_2080ti_v3_us": PAGES_V3_US[nq], "pages_2080ti_default_us": PAGES_DEFAULT_US[nq],
@@ -503,10 +514,12 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": chunk_traffic(),
-                     "kernel": "chunk_mfma_kernel, the n_q = 4 call of the step",
+                     "kernel": f"chunk_mfma_kernel, the n_q = 4 call of the step "
+                               f"({c4.fused_chunk}-cell chunks: "
+                               f"{-(-c4.max_sel // c4.fused_chunk)} workgroups)",
                      "algorithmic_bytes_per_launch": c4.chunk_bytes,
                      "launch_us_mean": k4_us,
-                     "note": "latency-bound: one instance, 2,051 cells, 9 workgroups; "
+                     "note": "latency-bound: one instance, 2,051 cells; "
                              "traffic = HBM bytes per launch (cold, counters), null if the "
                              "kernel changed since they were taken",
                      "bytes_per_step": bytes_sum, "call_us_per_step": round(call_us_sum, 3)},

@@ -20,7 +20,8 @@ PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN, MAX_CHUNKS = 16, 256, 64, 64, 65535
 PROMPT_MAX_ROWS = 65535 * 48
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
-            "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_status_string")
+            "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_fused_chunk_cells",
+            "sda_status_string")
 
 
 class SdaError(RuntimeError):
@@ -62,6 +63,8 @@ def library() -> C.CDLL:
         lib.sda_prompt_attn_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, vp, i32, i32,
                                               f32, vp, vp, vp]
         lib.sda_prompt_attn_batch.restype = C.c_int
+        lib.sda_fused_chunk_cells.argtypes = [i32, i32, i32, C.POINTER(i32)]
+        lib.sda_fused_chunk_cells.restype = C.c_int
         lib.sda_status_string.argtypes = [C.c_int]
         lib.sda_status_string.restype = C.c_char_p
         _lib = lib
@@ -118,6 +121,15 @@ def workspace_bytes(n_inst: int, n_q: int, n_qheads: int, max_sel: int, chunk_ce
                                        C.byref(out))
     if st != SDA_OK:
         raise SdaError(st, "sda_workspace_bytes")
+    return int(out.value)
+
+
+def fused_chunk_cells(n_inst: int, max_sel: int, chunk_cells: int) -> int:
+    """Chunk size sda_decode_attn_step/_batch use for this geometry."""
+    out = C.c_int32(0)
+    st = library().sda_fused_chunk_cells(n_inst, max_sel, chunk_cells, C.byref(out))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_fused_chunk_cells")
     return int(out.value)
 
 

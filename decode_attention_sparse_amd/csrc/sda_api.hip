@@ -44,6 +44,24 @@ int layout_of(int64_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim, i
 
 enum Passes { kChunk = 1, kMerge = 2, kBoth = 3 };
 
+// (instance, chunk) pairs up to which a chunk pass is one workgroup per CU.
+constexpr int64_t kLatencyItems = 256;
+
+// Chunk size the fused call (chunk pass + merge in one call) uses: a grid
+// of at most kLatencyItems (instance, chunk) pairs is latency-bound, and a
+// workgroup's time grows with the tiles it runs one after another, so such
+// a call splits the list into the smallest multiple of 64 cells that still
+// keeps the grid within kLatencyItems; the merge then combines the finer
+// partials.  Larger grids keep the caller's chunk.
+int32_t fused_chunk_of(int64_t n_inst, int32_t max_sel, int32_t chunk_cells) {
+    if (n_inst <= 0 || max_sel <= 0 || chunk_cells <= SDA_CHUNK_ALIGN) return chunk_cells;
+    auto items = [&](int32_t c) { return n_inst * (((int64_t)max_sel + c - 1) / c); };
+    if (items(chunk_cells) > kLatencyItems) return chunk_cells;
+    for (int32_t c = SDA_CHUNK_ALIGN; c < chunk_cells; c += SDA_CHUNK_ALIGN)
+        if (items(c) <= kLatencyItems) return c;
+    return chunk_cells;
+}
+
 int check_pool(const sda_pool *pool) {
     if (!pool) return SDA_ERR_INVALID_ARG;
     if (pool->page_size != SDA_PAGE_SIZE || pool->head_dim != SDA_HEAD_DIM)
@@ -80,6 +98,12 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     Layout L;
     st = layout_of(n_inst, n_q, n_qheads, pool->head_dim, max_sel, chunk_cells, &L);
     if (st != SDA_OK) return st;
+    // the fused call may run finer chunks (same layout, smaller chunk size)
+    const int32_t run_chunk =
+        passes == kBoth ? fused_chunk_of(n_inst, max_sel, chunk_cells) : chunk_cells;
+    if (run_chunk != chunk_cells &&
+        layout_of(n_inst, n_q, n_qheads, pool->head_dim, max_sel, run_chunk, &L) != SDA_OK)
+        return SDA_ERR_UNSUPPORTED;
     if (n_logical_pages < 0 || pt_stride < n_logical_pages || sel_stride < max_sel)
         return SDA_ERR_INVALID_ARG;
     if (!isfinite(softmax_scale)) return SDA_ERR_INVALID_ARG;
@@ -107,7 +131,7 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     p.n_inst = n_inst;
     p.n_rows = n_q * n_qheads;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
-    p.chunk = chunk_cells;
+    p.chunk = run_chunk;
     p.n_chunks = L.n_chunks;
     char *ws = static_cast<char *>(workspace);
     p.acc = L.total ? reinterpret_cast<float *>(ws + L.acc_off) : nullptr;
@@ -132,10 +156,23 @@ extern "C" {
 int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim,
                         int32_t max_sel, int32_t chunk_cells, size_t *bytes) {
     if (!bytes) return SDA_ERR_INVALID_ARG;
-    Layout L;
+    Layout L, F;
     int st = layout_of(n_inst, n_q, n_qheads, head_dim, max_sel, chunk_cells, &L);
-    if (st == SDA_OK) *bytes = L.total;
-    return st;
+    if (st != SDA_OK) return st;
+    st = layout_of(n_inst, n_q, n_qheads, head_dim, max_sel,
+                   fused_chunk_of(n_inst, max_sel, chunk_cells), &F);
+    if (st != SDA_OK) return st;
+    *bytes = L.total > F.total ? L.total : F.total;
+    return SDA_OK;
+}
+
+int sda_fused_chunk_cells(int32_t n_inst, int32_t max_sel, int32_t chunk_cells,
+                          int32_t *fused_chunk_cells) {
+    if (!fused_chunk_cells || n_inst < 0 || max_sel < 0 || chunk_cells < 1)
+        return SDA_ERR_INVALID_ARG;
+    if (chunk_cells % SDA_CHUNK_ALIGN) return SDA_ERR_UNSUPPORTED;
+    *fused_chunk_cells = fused_chunk_of(n_inst, max_sel, chunk_cells);
+    return SDA_OK;
 }
 
 int sda_decode_attn_step(const sda_pool *pool, const int32_t *page_table,

@@ -30,7 +30,9 @@
  *
  * Two entry points mirror the pages' step (one sequence) and batch (many
  * instances) entry points; both run the same two kernels (chunk, then merge)
- * on the caller's stream.
+ * on the caller's stream.  The chunk size is a parameter of the method that
+ * changes the result only by rounding; for small grids these fused calls run
+ * finer chunks than the caller's (sda_fused_chunk_cells).
  *
  * Memory and threading contract (all entry points):
  *   - Every array argument is a DEVICE pointer unless marked "host".  The
@@ -94,8 +96,9 @@ typedef struct sda_pool {
 } sda_pool;
 
 /* Workspace needed by one call (host only, no device access).
- * bytes (host out) = size of the chunk partials, laid out from the start of
- * the workspace as
+ * bytes (host out) = size of the chunk partials for chunk_cells or for
+ * sda_fused_chunk_cells(n_inst, max_sel, chunk_cells), whichever is larger.
+ * Partials are laid out from the start of the workspace as
  *     acc  float [n_inst][n_chunks][R][head_dim]
  *     m    float [n_inst][n_chunks][R]   (natural-log units, -inf if empty)
  *     l    float [n_inst][n_chunks][R]
@@ -104,10 +107,24 @@ typedef struct sda_pool {
  * of the three arrays starting at a 256-byte aligned offset (acc at 0, m at
  * align256(sizeof acc), l at m + align256(sizeof m)).  After a call these
  * hold the chunk partials of the chunks that instance actually has
- * (c < ceil(n_sel[i] / chunk_cells)); other entries are unspecified.
+ * (c < ceil(n_sel[i] / C)); other entries are unspecified.  C is
+ * chunk_cells after sda_chunk_batch, and sda_fused_chunk_cells(...) after
+ * sda_decode_attn_step / sda_decode_attn_batch.
  * Returns SDA_OK, SDA_ERR_INVALID_ARG or SDA_ERR_UNSUPPORTED. */
 int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim,
                         int32_t max_sel, int32_t chunk_cells, size_t *bytes);
+
+/* Chunk size the fused entry points (sda_decode_attn_step / _batch) use for
+ * this geometry (host only).  A call of at most 256 (instance, chunk) pairs
+ * is latency-bound: it uses the smallest multiple of SDA_CHUNK_ALIGN cells
+ * that keeps n_inst * ceil(max_sel / C) within 256, so that the work spreads
+ * over more CUs, and the merge combines the finer partials.  Otherwise, and
+ * always for chunk_cells = SDA_CHUNK_ALIGN, C = chunk_cells.
+ *   fused_chunk_cells (host out)
+ * Returns SDA_OK, SDA_ERR_INVALID_ARG (negative sizes, null output) or
+ * SDA_ERR_UNSUPPORTED (chunk_cells not a multiple of SDA_CHUNK_ALIGN). */
+int sda_fused_chunk_cells(int32_t n_inst, int32_t max_sel, int32_t chunk_cells,
+                          int32_t *fused_chunk_cells);
 
 /* One sequence (one KV head), the pages' single-step entry point.
  *   pool          host pointer to the pool descriptor
@@ -171,8 +188,10 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
  * (16-byte aligned),
  * lse float [n_inst][n_q][n_qheads].
  *
- * Running sda_chunk_batch then sda_merge_batch on one stream gives exactly
- * the result of sda_decode_attn_batch. */
+ * Running sda_chunk_batch then sda_merge_batch on one stream with chunk size
+ * sda_fused_chunk_cells(n_inst, max_sel, chunk_cells) gives exactly the
+ * result (and workspace partials) of sda_decode_attn_batch with chunk_cells;
+ * with chunk_cells itself the result agrees up to rounding. */
 int sda_chunk_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
                     int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
                     int64_t sel_stride, const int32_t *n_sel, int32_t max_sel, const float *q,

@@ -61,14 +61,47 @@ def _al(x):
     return (x + 255) // 256 * 256
 
 
+def fused_chunk(n_inst, max_sel, chunk):
+    """The documented choice, restated: a grid of at most 256 (instance,
+    chunk) pairs takes the smallest multiple of 64 keeping it within 256."""
+    if n_inst <= 0 or max_sel <= 0 or chunk <= 64:
+        return chunk
+    pairs = lambda c: n_inst * -(-max_sel // c)
+    if pairs(chunk) > 256:
+        return chunk
+    return next(c for c in range(64, chunk + 1, 64) if pairs(c) <= 256)
+
+
+@pytest.mark.parametrize("n_inst,max_sel,chunk,expect", [
+    (1, 2051, 256, 64), (1, 600, 256, 64), (8, 2051, 256, 128), (8, 1500, 256, 64),
+    (256, 2051, 1024, 1024), (64, 16384, 512, 512), (1, 16384, 512, 64), (1, 16385, 512, 128),
+    (3, 1, 64, 64), (1, 0, 256, 256), (0, 100, 256, 256), (29, 2051, 256, 256),
+    (28, 2051, 256, 256), (7, 2051, 1024, 64), (20, 2051, 1024, 192)])
+def test_fused_chunk_cells(n_inst, max_sel, chunk, expect):
+    assert api.fused_chunk_cells(n_inst, max_sel, chunk) == expect == fused_chunk(n_inst, max_sel, chunk)
+
+
+def test_fused_chunk_cells_sweep():
+    for n_inst in (1, 2, 3, 5, 8, 13, 32, 100, 257):
+        for max_sel in (1, 63, 64, 65, 600, 2051, 4096, 16384, 65536):
+            for chunk in (64, 128, 192, 256, 512, 1024):
+                assert api.fused_chunk_cells(n_inst, max_sel, chunk) == fused_chunk(n_inst, max_sel, chunk)
+    out = C.c_int32(0)
+    assert api.library().sda_fused_chunk_cells(1, 10, 100, C.byref(out)) == api.SDA_ERR_UNSUPPORTED
+    assert api.library().sda_fused_chunk_cells(-1, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
+    assert api.library().sda_fused_chunk_cells(1, 10, 64, None) == api.SDA_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("n_inst,n_q,nh,max_sel,chunk", [
     (1, 1, 12, 600, 256), (1, 4, 12, 2051, 256), (256, 4, 12, 2051, 1024),
-    (64, 2, 12, 16384, 512), (32, 4, 12, 131072, 1024), (3, 2, 5, 1, 64)])
+    (64, 2, 12, 16384, 512), (32, 4, 12, 131072, 1024), (3, 2, 5, 1, 64), (8, 4, 12, 2051, 256)])
 def test_workspace_layout(n_inst, n_q, nh, max_sel, chunk):
+    """The partials layout for the caller's chunk or the fused call's, whichever is larger."""
     R = n_q * nh
-    nch = -(-max_sel // chunk)
-    units = n_inst * nch * R
-    expect = _al(units * 256 * 4) + 2 * _al(units * 4)
+    def size(c):
+        units = n_inst * -(-max_sel // c) * R
+        return _al(units * 256 * 4) + 2 * _al(units * 4)
+    expect = max(size(chunk), size(fused_chunk(n_inst, max_sel, chunk)))
     assert api.workspace_bytes(n_inst, n_q, nh, max_sel, chunk) == expect
 
 

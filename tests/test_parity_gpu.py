@@ -77,21 +77,37 @@ def test_step_entry_matches_batch(n_q):
     assert np.array_equal(g.cpu().numpy(), g_b[0])
 
 
+def check_partials(x, ws, chunk, what):
+    from decode_attention_sparse_amd import api
+    acc, m, l = (t.cpu().numpy() for t in api.partials(ws, x.n_inst, x.n_q, x.n_qheads,
+                                                       x.sel.shape[1], chunk))
+    racc, rm, rl = oracle.chunk_partials(x, chunk)
+    assert racc.shape[1] == acc.shape[1]
+    assert_close(m, rm, LSE_ATOL, LSE_RTOL, f"{what} partial m")
+    assert_close(l, rl, 0, 1e-3, f"{what} partial l")
+    assert_close(acc / l[..., None], racc / rl[..., None], OUT_ATOL, OUT_RTOL, f"{what} partial acc/l")
+
+
 @pytest.mark.parametrize("cfg,n_q", [(0, 1), (1, 4), (1, 2)])
 def test_chunk_partials(cfg, n_q):
-    """The partials (acc, m, l) left in the workspace against the oracle's."""
+    """The partials (acc, m, l) against the oracle's: those sda_chunk_batch
+    leaves for the caller's chunk size, and those the fused call leaves for
+    the finer chunk it runs (sda_fused_chunk_cells)."""
+    import torch
     from decode_attention_sparse_amd import api
     say(f"case: partials, config {cfg}, n_q={n_q}")
     x = gen.make(cfg).with_n_q(n_q)
-    _, _, _, ws = run_batch(x)
-    acc, m, l = (t.cpu().numpy() for t in api.partials(ws, x.n_inst, n_q, x.n_qheads,
-                                                       x.sel.shape[1], x.chunk))
-    racc, rm, rl = oracle.chunk_partials(x, x.chunk)
-    nch = racc.shape[1]
-    assert_close(m, rm, LSE_ATOL, LSE_RTOL, "partial m")
-    assert_close(l, rl, 0, 1e-3, "partial l")
-    assert_close(acc / l[..., None], racc / rl[..., None], OUT_ATOL, OUT_RTOL, "partial acc/l")
-    assert nch == acc.shape[1]
+    max_sel = int(x.sel.shape[1])
+    pool, dev = api.to_device(x)
+    ws = api.workspace(x.n_inst, n_q, x.n_qheads, max_sel, x.chunk)
+    api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
+                    x.softmax_scale, x.chunk, ws)
+    torch.cuda.synchronize()
+    check_partials(x, ws, x.chunk, "chunk pass")
+    fc = api.fused_chunk_cells(x.n_inst, max_sel, x.chunk)
+    assert fc == 64  # one instance: the fused call runs 64-cell chunks
+    _, _, _, ws2 = run_batch(x)
+    check_partials(x, ws2, fc, "fused call")
 
 
 EDGE_COUNTS = [0, 1, 2, 3, 63, 64, 65, 127, 128, 129, 255, 256, 257]
@@ -241,29 +257,42 @@ def test_full_size_configs_sampled(cfg, ids):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
-@pytest.mark.parametrize("cfg,n_q", [(1, 4), (2, 4)])
-def test_batch_entry_equals_two_passes(cfg, n_q):
+@pytest.mark.parametrize("cfg,n_q,n_inst", [(1, 4, None), (1, 1, 8), (2, 4, None)])
+def test_batch_entry_equals_two_passes(cfg, n_q, n_inst):
     """sda_decode_attn_batch equals sda_chunk_batch followed by
-    sda_merge_batch bit for bit (the partials in the workspace included)."""
+    sda_merge_batch at the chunk size the fused call uses, bit for bit (the
+    partials in the workspace included), and the two passes at the caller's
+    chunk size up to rounding."""
     import torch
     from decode_attention_sparse_amd import api
-    say(f"case: batch entry vs the two passes, config {cfg}, n_q={n_q}")
-    x = gen.make(cfg).with_n_q(n_q)
+    say(f"case: batch entry vs the two passes, config {cfg}, n_q={n_q}, n_inst={n_inst}")
+    x = gen.make(cfg, **({} if n_inst is None else {"n_inst": n_inst})).with_n_q(n_q)
     n_inst, _, nh, D = x.q.shape
     max_sel = int(x.sel.shape[1])
+    fc = api.fused_chunk_cells(n_inst, max_sel, x.chunk)
+    say(f"  fused chunk {fc} (caller's {x.chunk})")
     out1, lse1, _, ws1 = run_batch(x, gather=False)
     pool, dev = api.to_device(x)
-    ws2 = api.workspace(n_inst, n_q, nh, max_sel, x.chunk)
-    out2 = torch.empty((n_inst, n_q, nh, D), device="cuda")
-    lse2 = torch.empty((n_inst, n_q, nh), device="cuda")
-    api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
-                    x.softmax_scale, x.chunk, ws2)
-    api.merge_batch(dev["n_sel"], max_sel, x.chunk, ws2, out2, lse2)
-    torch.cuda.synchronize()
-    assert np.array_equal(out1, out2.cpu().numpy()) and np.array_equal(lse1, lse2.cpu().numpy())
-    for a1, a2 in zip(api.partials(ws1, n_inst, n_q, nh, max_sel, x.chunk),
-                      api.partials(ws2, n_inst, n_q, nh, max_sel, x.chunk)):
+
+    def two_pass(chunk):
+        ws2 = api.workspace(n_inst, n_q, nh, max_sel, x.chunk)
+        out2 = torch.empty((n_inst, n_q, nh, D), device="cuda")
+        lse2 = torch.empty((n_inst, n_q, nh), device="cuda")
+        api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
+                        x.softmax_scale, chunk, ws2)
+        api.merge_batch(dev["n_sel"], max_sel, chunk, ws2, out2, lse2)
+        torch.cuda.synchronize()
+        return out2.cpu().numpy(), lse2.cpu().numpy(), ws2
+
+    out2, lse2, ws2 = two_pass(fc)
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+    for a1, a2 in zip(api.partials(ws1, n_inst, n_q, nh, max_sel, fc),
+                      api.partials(ws2, n_inst, n_q, nh, max_sel, fc)):
         assert torch.equal(a1, a2)
+    if fc != x.chunk:
+        out3, lse3, _ = two_pass(x.chunk)
+        assert_close(out1, out3, OUT_ATOL, OUT_RTOL, "fused vs caller's chunk out")
+        assert_close(lse1, lse3, LSE_ATOL, LSE_RTOL, "fused vs caller's chunk lse")
 
 
 def test_workspace_sentinel():
