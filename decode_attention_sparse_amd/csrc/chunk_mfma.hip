@@ -550,6 +550,105 @@ void chunk_mfma_kernel(Params p, int cpw) {
         rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
 }
 
+// One producer wave stages tile cells [j0, j0 + 64) of instance i (entries
+// from j_end on are masked) in three round trips: the list entries, the
+// page-table entries, then the scales and the K and V code rows together.
+// LDS layout as in the pipelined kernel (row r = tile cell r, padded rows;
+// scales, bias and the tile's largest V scale by cell).
+__device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j_end, int lane,
+                                           int8_t *kb, int8_t *vb, float *ks, float *vs,
+                                           float *bias, float *vmax) {
+    const int g = lane >> 4, l16 = lane & 15;
+    const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
+    const int32_t *sel = p.sel + (int64_t)i * p.sel_stride;
+    const int32_t *pt_or_sel = p.n_logical_pages > 0 ? pt : sel;
+    const int j = j0 + lane;
+    const int c = j < j_end ? sel[j] : -1;
+    const int lp = c >> 4;
+    const bool id_ok = c >= 0 && lp < p.n_logical_pages;
+    const int pte = pt_or_sel[id_ok ? lp : 0];
+    int ph = -1;
+    if (id_ok && pte >= 0 && (int64_t)pte < p.n_phys_pages) ph = (pte << 4) | (c & 15);
+    if (p.gather_out && j < j_end) p.gather_out[(int64_t)i * p.sel_stride + j] = ph;
+    const int64_t sc = (int64_t)(ph < 0 ? 0 : ph) * p.scale_stride;
+    const unsigned kh = p.k_scales[sc];
+    const unsigned vh = p.v_scales[sc];
+    // load (k, cc) covers row 16k + l16, bytes 64cc + 16g; a masked cell
+    // reads cell 0 (its score is -inf)
+    v4i kst[kRows], vst[kRows];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int pr = __shfl(ph, 16 * k + l16);
+        const int64_t off = (int64_t)(pr < 0 ? 0 : pr) * kDim + 16 * g;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            kst[4 * k + cc] = *reinterpret_cast<const v4i *>(p.k_codes + off + 64 * cc);
+            vst[4 * k + cc] = *reinterpret_cast<const v4i *>(p.v_codes + off + 64 * cc);
+        }
+    }
+    const bool ok = ph >= 0;
+    const float ksf = ok ? half_bits_to_float((uint16_t)kh) : 0.f;
+    const float vsf = ok ? half_bits_to_float((uint16_t)vh) : 0.f;
+    ks[lane] = ksf;
+    vs[lane] = vsf;
+    bias[lane] = ok ? 0.f : -INFINITY;
+    const float vm = wave_max(vsf);
+    if (lane == 0) *vmax = vm;
+    int8_t *kd = kb + l16 * kStride + 16 * g;
+    int8_t *vd = vb + l16 * kStride + 16 * g;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            *reinterpret_cast<v4i *>(kd + 16 * k * kStride + 64 * cc) = kst[4 * k + cc];
+            *reinterpret_cast<v4i *>(vd + 16 * k * kStride + 64 * cc) = vst[4 * k + cc];
+        }
+}
+
+// Chunks of one tile (64 cells) in a latency-bound grid: workgroup = one
+// (instance, chunk), DS * RB compute waves and one producer wave that stages
+// the tile in three round trips (the pipelined kernel takes five steps for
+// one tile).  The compute waves then run the same two steps the pipelined
+// kernel runs for a one-tile chunk (the scores, then the softmax and V
+// accumulation), so the partial is bit for bit the same.
+template <int RB, int DS>
+__global__ __launch_bounds__(64 * (DS * RB + 1))
+void chunk_tile_kernel(Params p) {
+    constexpr int kProducer = DS * RB;
+    constexpr int kDB = 16 / DS;
+    __shared__ __attribute__((aligned(1024))) int8_t kbuf[kBuf];
+    __shared__ __attribute__((aligned(1024))) int8_t vbuf[kBuf];
+    __shared__ __attribute__((aligned(16))) float ks_s[kTile];
+    __shared__ __attribute__((aligned(16))) float vs_s[kTile];
+    __shared__ __attribute__((aligned(16))) float bias_s[kTile];
+    __shared__ float vmax_s;
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x;  // instance
+    const int c = blockIdx.y;  // chunk = tile
+    const int n = count_of(p, i);
+    const int j_begin = c * kTile;
+    if (j_begin >= n) return;  // this instance has fewer chunks
+    const int j_end = min(j_begin + kTile, n);
+
+    if (wave == kProducer) {
+        stage_tile(p, i, j_begin, j_end, lane, kbuf, vbuf, ks_s, vs_s, bias_s, &vmax_s);
+        __syncthreads();
+        return;
+    }
+    const int g = lane >> 4, l16 = lane & 15;
+    const int row = (wave / DS) * 16 + l16;
+    const int dh = wave % DS;
+    const int R = p.n_rows;
+    RowBlock<kDB> rb;
+    rb.init(row < R ? p.q + ((int64_t)i * R + row) * kDim : nullptr, p.scale_log2, g, l16);
+    __syncthreads();
+    rb.step(kbuf, ks_s, bias_s, true, vbuf, vs_s, vmax_s, dh);   // scores of the tile
+    rb.step(kbuf, ks_s, bias_s, false, vbuf, vs_s, vmax_s, dh);  // its softmax and V
+    rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
+}
+
 template <int DS>
 void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
     switch ((p.n_rows + 15) / 16) {
@@ -563,11 +662,24 @@ void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_chunk(const Params &p, hipStream_t s) {
+    const int64_t items = (int64_t)p.n_inst * p.n_chunks;
+    // one-tile chunks in a grid of at most one workgroup per CU: stage the
+    // tile at once (the V accumulation split over two waves per row group up
+    // to 32 rows, as below)
+    if (p.chunk == kTile && items <= kLatencyWorkgroups) {
+        const dim3 grid(p.n_inst, p.n_chunks);
+        switch ((p.n_rows + 15) / 16) {
+            case 1: chunk_tile_kernel<1, 2><<<grid, 64 * 3, 0, s>>>(p); break;
+            case 2: chunk_tile_kernel<2, 2><<<grid, 64 * 5, 0, s>>>(p); break;
+            case 3: chunk_tile_kernel<3, 1><<<grid, 64 * 4, 0, s>>>(p); break;
+            default: chunk_tile_kernel<4, 1><<<grid, 64 * 5, 0, s>>>(p); break;
+        }
+        return hipGetLastError();
+    }
     // Chunks per workgroup: enough that the grid stays at about two
     // workgroups per CU (256 CUs), so that no pipeline refills between the
     // chunks a workgroup would otherwise have left to a later wave of
     // workgroups; a small grid keeps one chunk per workgroup.
-    const int64_t items = (int64_t)p.n_inst * p.n_chunks;
     int cpw = (int)(items / kResidentWorkgroups);
     cpw = cpw < 1 ? 1 : (cpw > p.n_chunks ? p.n_chunks : cpw);
     dim3 grid(p.n_inst, (p.n_chunks + cpw - 1) / cpw);
