@@ -613,6 +613,7 @@ __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j
 // accumulation), so the partial is bit for bit the same.
 template <int RB, int DS>
 __global__ __launch_bounds__(64 * (DS * RB + 1))
+__attribute__((amdgpu_waves_per_eu(2, 2)))  // at most 256 registers: no AGPR copies
 void chunk_tile_kernel(Params p) {
     constexpr int kProducer = DS * RB;
     constexpr int kDB = 16 / DS;
