@@ -125,19 +125,25 @@ struct RowBlock {
     v4f o[kDB];    // O^T[16 (kDB dh + db) + 4g + u][row] / frame
     v4f su[4];     // scores of the tile the softmax runs on next: u, S = coef * u
 
-    // qrow: this lane's query row (nullptr for a row past the end; its
-    // digits are 0), read at dims 64s + 16g + e (byte e of slab s).  The sign
-    // of the softmax scale is folded into the digits so that coef >= 0 and
-    // max commutes with it.
-    __device__ __forceinline__ void init(const float *qrow, float scale_log2, int g, int l16) {
+    // qrow: this lane's query row, read at dims 64s + 16g + e (byte e of
+    // slab s); a row past the end (valid false) passes any readable row and
+    // gets digits 0.  The loads are unconditional, so all sixteen are in
+    // flight at once.  The sign of the softmax scale is folded into the
+    // digits so that coef >= 0 and max commutes with it.
+    __device__ __forceinline__ void init(const float *qrow, bool valid, float scale_log2, int g,
+                                         int l16) {
         v4f qv[4][4];
         float mx = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
+            for (int w = 0; w < 4; ++w)
+                qv[s][w] = *reinterpret_cast<const v4f *>(qrow + 64 * s + 16 * g + 4 * w);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
             for (int w = 0; w < 4; ++w) {
-                qv[s][w] = (v4f){0.f, 0.f, 0.f, 0.f};
-                if (qrow) qv[s][w] = *reinterpret_cast<const v4f *>(qrow + 64 * s + 16 * g + 4 * w);
+                if (!valid) qv[s][w] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(qv[s][w][u]));
             }
@@ -519,7 +525,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     RowBlock<kDB> rb;
     const int64_t grow = (int64_t)i * R + row0 + row;  // row in [n_inst][n_rows]
     const bool row_ok = row0 + row < R;
-    rb.init(row_ok ? p.q + grow * kDim : nullptr, p.scale_log2, g, l16);
+    rb.init(p.q + (row_ok ? grow : (int64_t)i * R + row0) * kDim, row_ok, p.scale_log2, g, l16);
     // prompt: this row's last visible cell (its position)
     const int64_t lim_row = kPrompt ? pos0 + (row0 + row) / p.n_qheads : 0;
     for (int t = -4; t < n_tiles; ++t) {
@@ -550,14 +556,19 @@ void chunk_mfma_kernel(Params p, int cpw) {
         rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
 }
 
+constexpr int kPtLdsPages = 2048;  // page tables up to this size are staged whole (8 KB)
+
 // One producer wave stages tile cells [j0, j0 + 64) of instance i (entries
-// from j_end on are masked) in three round trips: the list entries, the
-// page-table entries, then the scales and the K and V code rows together.
-// LDS layout as in the pipelined kernel (row r = tile cell r, padded rows;
+// from j_end on are masked): the list entries and the page-table entries,
+// then the scales and the K and V code rows together.  With pt_s (a page
+// table of at most kPtLdsPages entries) the whole page-table row is loaded
+// into LDS in the same round trip as the list entries, so the lookup is an
+// LDS read: two dependent round trips to memory instead of three.  LDS
+// layout as in the pipelined kernel (row r = tile cell r, padded rows;
 // scales, bias and the tile's largest V scale by cell).
 __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j_end, int lane,
                                            int8_t *kb, int8_t *vb, float *ks, float *vs,
-                                           float *bias, float *vmax) {
+                                           float *bias, float *vmax, int *pt_s) {
     const int g = lane >> 4, l16 = lane & 15;
     const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
     const int32_t *sel = p.sel + (int64_t)i * p.sel_stride;
@@ -566,7 +577,47 @@ __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j
     const int c = j < j_end ? sel[j] : -1;
     const int lp = c >> 4;
     const bool id_ok = c >= 0 && lp < p.n_logical_pages;
-    const int pte = pt_or_sel[id_ok ? lp : 0];
+    int pte;
+    if (pt_s) {
+        // the whole row, every load issued before the first LDS write (one
+        // round trip): 16-byte pieces when the row is 16-byte aligned, else
+        // single entries
+        const int nlp = p.n_logical_pages;
+        if ((reinterpret_cast<uintptr_t>(pt) & 15) == 0) {
+            v4i t[kPtLdsPages / 256];
+#pragma unroll
+            for (int k = 0; k < kPtLdsPages / 256; ++k) {
+                const int e = 4 * lane + 256 * k;
+                if (e + 4 <= nlp) t[k] = *reinterpret_cast<const v4i *>(pt + e);
+            }
+#pragma unroll
+            for (int k = 0; k < kPtLdsPages / 256; ++k) {
+                const int e = 4 * lane + 256 * k;
+                if (e + 4 <= nlp) *reinterpret_cast<v4i *>(pt_s + e) = t[k];
+            }
+            const int e = (nlp & ~3) + lane;  // the last nlp % 4 entries
+            if (e < nlp) pt_s[e] = pt[e];
+        } else {
+            int t[kPtLdsPages / 64];
+#pragma unroll
+            for (int k = 0; k < kPtLdsPages / 64; ++k) {
+                const int e = lane + 64 * k;
+                if (e < nlp) t[k] = pt[e];
+            }
+#pragma unroll
+            for (int k = 0; k < kPtLdsPages / 64; ++k) {
+                const int e = lane + 64 * k;
+                if (e < nlp) pt_s[e] = t[k];
+            }
+        }
+        // the wave's own LDS writes, read back by other lanes of the wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        pte = id_ok ? pt_s[lp] : 0;
+    } else {
+        pte = pt_or_sel[id_ok ? lp : 0];
+    }
     int ph = -1;
     if (id_ok && pte >= 0 && (int64_t)pte < p.n_phys_pages) ph = (pte << 4) | (c & 15);
     if (p.gather_out && j < j_end) p.gather_out[(int64_t)i * p.sel_stride + j] = ph;
@@ -623,6 +674,7 @@ void chunk_tile_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) float vs_s[kTile];
     __shared__ __attribute__((aligned(16))) float bias_s[kTile];
     __shared__ float vmax_s;
+    __shared__ __attribute__((aligned(16))) int pt_s[kPtLdsPages];
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -634,7 +686,8 @@ void chunk_tile_kernel(Params p) {
     const int j_end = min(j_begin + kTile, n);
 
     if (wave == kProducer) {
-        stage_tile(p, i, j_begin, j_end, lane, kbuf, vbuf, ks_s, vs_s, bias_s, &vmax_s);
+        stage_tile(p, i, j_begin, j_end, lane, kbuf, vbuf, ks_s, vs_s, bias_s, &vmax_s,
+                   p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
         __syncthreads();
         return;
     }
@@ -643,7 +696,7 @@ void chunk_tile_kernel(Params p) {
     const int dh = wave % DS;
     const int R = p.n_rows;
     RowBlock<kDB> rb;
-    rb.init(row < R ? p.q + ((int64_t)i * R + row) * kDim : nullptr, p.scale_log2, g, l16);
+    rb.init(p.q + ((int64_t)i * R + (row < R ? row : 0)) * kDim, row < R, p.scale_log2, g, l16);
     __syncthreads();
     rb.step(kbuf, ks_s, bias_s, true, vbuf, vs_s, vmax_s, dh);   // scores of the tile
     rb.step(kbuf, ks_s, bias_s, false, vbuf, vs_s, vmax_s, dh);  // its softmax and V
