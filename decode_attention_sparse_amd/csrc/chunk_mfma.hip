@@ -718,13 +718,13 @@ void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
 hipError_t launch_chunk(const Params &p, hipStream_t s) {
     const int64_t items = (int64_t)p.n_inst * p.n_chunks;
     // one-tile chunks in a grid of at most one workgroup per CU: stage the
-    // tile at once (the V accumulation split over two waves per row group up
-    // to 32 rows, as below)
+    // tile at once (a single 16-row group splits its V accumulation over two
+    // waves; with more groups that measured slower)
     if (p.chunk == kTile && items <= kLatencyWorkgroups) {
         const dim3 grid(p.n_inst, p.n_chunks);
         switch ((p.n_rows + 15) / 16) {
             case 1: chunk_tile_kernel<1, 2><<<grid, 64 * 3, 0, s>>>(p); break;
-            case 2: chunk_tile_kernel<2, 2><<<grid, 64 * 5, 0, s>>>(p); break;
+            case 2: chunk_tile_kernel<2, 1><<<grid, 64 * 3, 0, s>>>(p); break;
             case 3: chunk_tile_kernel<3, 1><<<grid, 64 * 4, 0, s>>>(p); break;
             default: chunk_tile_kernel<4, 1><<<grid, 64 * 5, 0, s>>>(p); break;
         }
