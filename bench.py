@@ -48,8 +48,8 @@ PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary with the commands is in
 # profiles/chunk_mfma_kernel__hbm_bytes__pages_point_and_batched.md.  The
 # figures hold only for the kernel source they were taken on.
-CHUNK_TRAFFIC = {"sources_sha256": "bed3b842f0efbd130fd4ea48d18f2d3a1f2b96cb8b20b8dcd1513ad8bb9145a9",
-                 "fetch_bytes": 1_883_068, "write_bytes": 445_824}
+CHUNK_TRAFFIC = {"sources_sha256": "2ec70f106da75b6626ce857239cbcd13c906f5b0b61d8cf01b3bd426f01c13dd",
+                 "fetch_bytes": 1_972_304, "write_bytes": 1_634_688}
 TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                    "decode_attention_sparse_amd/csrc/sda_internal.h",
                    "decode_attention_sparse_amd/csrc/sda_api.hip")
@@ -514,7 +514,8 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": chunk_traffic(),
-                     "kernel": f"chunk_mfma_kernel, the n_q = 4 call of the step "
+                     "kernel": f"{'chunk_tile_kernel' if c4.fused_chunk == 64 else 'chunk_mfma_kernel'}"
+                               f", the n_q = 4 call of the step "
                                f"({c4.fused_chunk}-cell chunks: "
                                f"{-(-c4.max_sel // c4.fused_chunk)} workgroups)",
                      "algorithmic_bytes_per_launch": c4.chunk_bytes,
