@@ -44,21 +44,38 @@ int layout_of(int64_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim, i
 
 enum Passes { kChunk = 1, kMerge = 2, kBoth = 3 };
 
-// (instance, chunk) pairs up to which a chunk pass is one workgroup per CU.
+// (instance, chunk) pairs up to which a chunk pass is one workgroup per CU,
+// and the workgroups the chunk kernel keeps resident (two per CU).
 constexpr int64_t kLatencyItems = 256;
+constexpr int64_t kResidentItems = 512;
 
-// Chunk size the fused call (chunk pass + merge in one call) uses: a grid
-// of at most kLatencyItems (instance, chunk) pairs is latency-bound, and a
-// workgroup's time grows with the tiles it runs one after another, so such
-// a call splits the list into the smallest multiple of 64 cells that still
-// keeps the grid within kLatencyItems; the merge then combines the finer
-// partials.  Larger grids keep the caller's chunk.
+// Chunk size the fused call (chunk pass + merge in one call) uses.
+//  - A grid of at most kLatencyItems (instance, chunk) pairs is
+//    latency-bound, and a workgroup's time grows with the tiles it runs one
+//    after another: the call splits the list into the smallest multiple of
+//    64 cells that still keeps the grid within kLatencyItems.
+//  - A grid of more than kResidentItems pairs runs k = pairs / kResidentItems
+//    consecutive chunks per workgroup; the call then takes chunks k times
+//    the caller's, so that each workgroup leaves one partial instead of k
+//    (less partial traffic, a shorter merge).
+//  - Otherwise the caller's chunk.
+// The merge combines whatever partials the chunk pass leaves.
 int32_t fused_chunk_of(int64_t n_inst, int32_t max_sel, int32_t chunk_cells) {
-    if (n_inst <= 0 || max_sel <= 0 || chunk_cells <= SDA_CHUNK_ALIGN) return chunk_cells;
-    auto items = [&](int32_t c) { return n_inst * (((int64_t)max_sel + c - 1) / c); };
-    if (items(chunk_cells) > kLatencyItems) return chunk_cells;
-    for (int32_t c = SDA_CHUNK_ALIGN; c < chunk_cells; c += SDA_CHUNK_ALIGN)
-        if (items(c) <= kLatencyItems) return c;
+    if (n_inst <= 0 || max_sel <= 0) return chunk_cells;
+    auto items = [&](int64_t c) { return n_inst * (((int64_t)max_sel + c - 1) / c); };
+    const int64_t pairs = items(chunk_cells);
+    if (pairs <= kLatencyItems) {
+        for (int32_t c = SDA_CHUNK_ALIGN; c < chunk_cells; c += SDA_CHUNK_ALIGN)
+            if (items(c) <= kLatencyItems) return c;
+        return chunk_cells;
+    }
+    if (pairs > kResidentItems) {
+        const int64_t per_inst = ((int64_t)max_sel + chunk_cells - 1) / chunk_cells;
+        int64_t k = pairs / kResidentItems;
+        if (k > per_inst) k = per_inst;
+        const int64_t c = (int64_t)chunk_cells * k;
+        return c > INT32_MAX ? chunk_cells : (int32_t)c;
+    }
     return chunk_cells;
 }
 

@@ -115,11 +115,15 @@ int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t h
                         int32_t max_sel, int32_t chunk_cells, size_t *bytes);
 
 /* Chunk size the fused entry points (sda_decode_attn_step / _batch) use for
- * this geometry (host only).  A call of at most 256 (instance, chunk) pairs
- * is latency-bound: it uses the smallest multiple of SDA_CHUNK_ALIGN cells
- * that keeps n_inst * ceil(max_sel / C) within 256, so that the work spreads
- * over more CUs, and the merge combines the finer partials.  Otherwise, and
- * always for chunk_cells = SDA_CHUNK_ALIGN, C = chunk_cells.
+ * this geometry (host only), with P = n_inst * ceil(max_sel / chunk_cells)
+ * (instance, chunk) pairs:
+ *   P <= 256: the call is latency-bound; C is the smallest multiple of
+ *     SDA_CHUNK_ALIGN cells that keeps n_inst * ceil(max_sel / C) within 256
+ *     (the work spreads over more CUs; the merge combines finer partials);
+ *   P > 512: each workgroup of the chunk pass runs k = min(P / 512,
+ *     ceil(max_sel / chunk_cells)) consecutive chunks; C = k * chunk_cells,
+ *     so that it leaves one partial instead of k;
+ *   otherwise C = chunk_cells.
  *   fused_chunk_cells (host out)
  * Returns SDA_OK, SDA_ERR_INVALID_ARG (negative sizes, null output) or
  * SDA_ERR_UNSUPPORTED (chunk_cells not a multiple of SDA_CHUNK_ALIGN). */

@@ -63,18 +63,23 @@ def _al(x):
 
 def fused_chunk(n_inst, max_sel, chunk):
     """The documented choice, restated: a grid of at most 256 (instance,
-    chunk) pairs takes the smallest multiple of 64 keeping it within 256."""
-    if n_inst <= 0 or max_sel <= 0 or chunk <= 64:
+    chunk) pairs takes the smallest multiple of 64 keeping it within 256; one
+    of more than 512 pairs takes k = min(pairs // 512, chunks per instance)
+    times the chunk."""
+    if n_inst <= 0 or max_sel <= 0:
         return chunk
     pairs = lambda c: n_inst * -(-max_sel // c)
-    if pairs(chunk) > 256:
-        return chunk
-    return next(c for c in range(64, chunk + 1, 64) if pairs(c) <= 256)
+    if pairs(chunk) <= 256:
+        return next(c for c in range(64, chunk + 1, 64) if pairs(c) <= 256)
+    if pairs(chunk) > 512:
+        return chunk * min(pairs(chunk) // 512, -(-max_sel // chunk))
+    return chunk
 
 
 @pytest.mark.parametrize("n_inst,max_sel,chunk,expect", [
     (1, 2051, 256, 64), (1, 600, 256, 64), (8, 2051, 256, 128), (8, 1500, 256, 64),
-    (256, 2051, 1024, 1024), (64, 16384, 512, 512), (1, 16384, 512, 64), (1, 16385, 512, 128),
+    (256, 2051, 1024, 1024), (64, 16384, 512, 2048), (32, 131072, 1024, 8192),
+    (256, 2051, 256, 1024), (1, 16384, 512, 64), (1, 16385, 512, 128), (200, 512, 64, 192),
     (3, 1, 64, 64), (1, 0, 256, 256), (0, 100, 256, 256), (29, 2051, 256, 256),
     (28, 2051, 256, 256), (7, 2051, 1024, 64), (20, 2051, 1024, 192)])
 def test_fused_chunk_cells(n_inst, max_sel, chunk, expect):

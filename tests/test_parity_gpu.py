@@ -145,27 +145,49 @@ def test_edge_counts_large_grid(n_q):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
 
 
+def two_pass(x, chunk, gather=True):
+    """sda_chunk_batch then sda_merge_batch at the given chunk size."""
+    import torch
+    from decode_attention_sparse_amd import api
+    n_inst, n_q, nh, D = x.q.shape
+    max_sel = int(x.sel.shape[1])
+    pool, dev = api.to_device(x)
+    ws = api.workspace(n_inst, n_q, nh, max_sel, chunk)
+    out = torch.full((n_inst, n_q, nh, D), float("nan"), device="cuda")
+    lse = torch.full((n_inst, n_q, nh), float("nan"), device="cuda")
+    g = torch.full(x.sel.shape, -7, dtype=torch.int32, device="cuda") if gather else None
+    api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
+                    x.softmax_scale, chunk, ws, gather_out=g)
+    api.merge_batch(dev["n_sel"], max_sel, chunk, ws, out, lse)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)
+
+
 @pytest.mark.parametrize("n_q", [2, 4])
 def test_batch_size_independence(n_q):
-    """Instance data does not depend on the batch size, so the same instances
-    run once in a small grid and once in a large one (which the library
-    launches differently: the V accumulation split over two waves per row
-    group for up to 32 rows in small grids, several chunks per workgroup in
-    large ones); every instance gets the same arithmetic in the same order,
-    so outputs and gather indices must agree bit for bit."""
+    """The chunk pass and merge at a given chunk size do not depend on the
+    batch: the same instances run in a small grid and in larger ones (which
+    the library launches differently: one-tile workgroups and the V
+    accumulation split over two waves per row group in small grids, several
+    chunks per workgroup in large ones); every instance gets the same
+    arithmetic in the same order, so outputs and gather indices agree bit
+    for bit.  The fused call chooses its chunk size from the grid
+    (sda_fused_chunk_cells), so it is checked against the oracle."""
     say(f"case: batch-size independence, n_q={n_q}")
     spec = dict(n_q=n_q, pool_cells=2048, n_sel=600, sel="uniform", chunk=64)
     small = gen.make(None, seed=123, n_inst=20, **spec)   # 20 x 10 chunks
     large = gen.make(None, seed=123, n_inst=30, **spec)   # 30 x 10 chunks
     huge = gen.make(None, seed=123, n_inst=120, **spec)   # 120 x 10: two chunks per workgroup
     assert np.array_equal(small.sel, large.sel[:20]) and np.array_equal(small.q, large.q[:20])
-    o1, l1, g1, _ = run_batch(small)
-    o2, l2, g2, _ = run_batch(large)
-    o3, l3, g3, _ = run_batch(huge)
+    o1, l1, g1, _ = two_pass(small, 64)
+    o2, l2, g2, _ = two_pass(large, 64)
+    o3, l3, g3, _ = two_pass(huge, 64)
     for o, l, g_ in ((o2, l2, g2), (o3, l3, g3)):
         assert np.array_equal(o1, o[:20]) and np.array_equal(l1, l[:20])
         assert np.array_equal(g1, g_[:20])
     check(large, o2, l2, g2, inst_ids=[0, 19, 29], what="batch of 30")
+    o4, l4, g4, _ = run_batch(huge)
+    check(huge, o4, l4, g4, inst_ids=[0, 19, 77, 119], what="fused call, batch of 120")
 
 
 def test_several_chunks_per_workgroup():
@@ -182,7 +204,7 @@ def test_several_chunks_per_workgroup():
     counts[[0, 1, 2, 3]] = [512, 0, 65, 449]
     x = dataclasses.replace(x, n_sel=counts)
     ids = [0, 1, 2, 3, 57, 128, 199]
-    out, lse, g, ws = run_batch(x)
+    out, lse, g, ws = two_pass(x, 64)  # the caller's chunk: three chunks per workgroup
     check(x, out, lse, g, inst_ids=ids, what="chunks per workgroup")
     acc, m, l = (t.cpu().numpy() for t in api.partials(ws, 200, 2, 12, 512, 64))
     racc, rm, rl = oracle.chunk_partials(x, 64, 8, inst_ids=ids)
