@@ -54,10 +54,14 @@ constexpr int64_t kResidentItems = 512;
 //    latency-bound, and a workgroup's time grows with the tiles it runs one
 //    after another: the call splits the list into the smallest multiple of
 //    64 cells that still keeps the grid within kLatencyItems.
-//  - A grid of more than kResidentItems pairs runs k = pairs / kResidentItems
-//    consecutive chunks per workgroup; the call then takes chunks k times
-//    the caller's, so that each workgroup leaves one partial instead of k
-//    (less partial traffic, a shorter merge).
+//  - Otherwise, with at most kLatencyItems instances: m = kResidentItems /
+//    n_inst (at least 2) balanced chunks per instance, at most the caller's
+//    number, so the grid fills the two resident workgroups per CU in one
+//    round and no workgroup holds a short tail chunk.
+//  - Otherwise, a grid of more than kResidentItems pairs would run
+//    k = pairs / kResidentItems consecutive chunks per workgroup; the call
+//    takes chunks k times the caller's, so that each workgroup leaves one
+//    partial instead of k (less partial traffic, a shorter merge).
 //  - Otherwise the caller's chunk.
 // The merge combines whatever partials the chunk pass leaves.
 int32_t fused_chunk_of(int64_t n_inst, int32_t max_sel, int32_t chunk_cells) {
@@ -69,8 +73,14 @@ int32_t fused_chunk_of(int64_t n_inst, int32_t max_sel, int32_t chunk_cells) {
             if (items(c) <= kLatencyItems) return c;
         return chunk_cells;
     }
+    const int64_t per_inst = ((int64_t)max_sel + chunk_cells - 1) / chunk_cells;
+    if (n_inst <= kLatencyItems) {
+        int64_t m = kResidentItems / n_inst;
+        if (m > per_inst) m = per_inst;
+        const int64_t len = ((int64_t)max_sel + m - 1) / m;  // balanced
+        return (int32_t)((len + SDA_CHUNK_ALIGN - 1) / SDA_CHUNK_ALIGN * SDA_CHUNK_ALIGN);
+    }
     if (pairs > kResidentItems) {
-        const int64_t per_inst = ((int64_t)max_sel + chunk_cells - 1) / chunk_cells;
         int64_t k = pairs / kResidentItems;
         if (k > per_inst) k = per_inst;
         const int64_t c = (int64_t)chunk_cells * k;

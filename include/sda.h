@@ -120,7 +120,11 @@ int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t h
  *   P <= 256: the call is latency-bound; C is the smallest multiple of
  *     SDA_CHUNK_ALIGN cells that keeps n_inst * ceil(max_sel / C) within 256
  *     (the work spreads over more CUs; the merge combines finer partials);
- *   P > 512: each workgroup of the chunk pass runs k = min(P / 512,
+ *   else n_inst <= 256: m = min(512 / n_inst, ceil(max_sel / chunk_cells))
+ *     balanced chunks per instance, C = ceil(max_sel / m) rounded up to a
+ *     multiple of SDA_CHUNK_ALIGN (one round of two workgroups per CU, no
+ *     short tail chunks);
+ *   else P > 512: each workgroup of the chunk pass would run k = min(P / 512,
  *     ceil(max_sel / chunk_cells)) consecutive chunks; C = k * chunk_cells,
  *     so that it leaves one partial instead of k;
  *   otherwise C = chunk_cells.

@@ -71,6 +71,9 @@ def fused_chunk(n_inst, max_sel, chunk):
     pairs = lambda c: n_inst * -(-max_sel // c)
     if pairs(chunk) <= 256:
         return next(c for c in range(64, chunk + 1, 64) if pairs(c) <= 256)
+    if n_inst <= 256:
+        m = min(512 // n_inst, -(-max_sel // chunk))
+        return -(-(-(-max_sel // m)) // 64) * 64
     if pairs(chunk) > 512:
         return chunk * min(pairs(chunk) // 512, -(-max_sel // chunk))
     return chunk
@@ -78,10 +81,11 @@ def fused_chunk(n_inst, max_sel, chunk):
 
 @pytest.mark.parametrize("n_inst,max_sel,chunk,expect", [
     (1, 2051, 256, 64), (1, 600, 256, 64), (8, 2051, 256, 128), (8, 1500, 256, 64),
-    (256, 2051, 1024, 1024), (64, 16384, 512, 2048), (32, 131072, 1024, 8192),
-    (256, 2051, 256, 1024), (1, 16384, 512, 64), (1, 16385, 512, 128), (200, 512, 64, 192),
+    (256, 2051, 1024, 1088), (64, 16384, 512, 2048), (32, 131072, 1024, 8192),
+    (256, 2051, 256, 1088), (1, 16384, 512, 64), (1, 16385, 512, 128), (200, 512, 64, 256),
+    (300, 2051, 1024, 1024), (1000, 2051, 256, 2304), (400, 600, 256, 512),
     (3, 1, 64, 64), (1, 0, 256, 256), (0, 100, 256, 256), (29, 2051, 256, 256),
-    (28, 2051, 256, 256), (7, 2051, 1024, 64), (20, 2051, 1024, 192)])
+    (28, 2051, 256, 256), (7, 2051, 1024, 64), (20, 2051, 1024, 192), (100, 2051, 512, 448)])
 def test_fused_chunk_cells(n_inst, max_sel, chunk, expect):
     assert api.fused_chunk_cells(n_inst, max_sel, chunk) == expect == fused_chunk(n_inst, max_sel, chunk)
 
