@@ -78,7 +78,8 @@ int32_t fused_chunk_of(int64_t n_inst, int32_t max_sel, int32_t chunk_cells) {
         int64_t m = kResidentItems / n_inst;
         if (m > per_inst) m = per_inst;
         const int64_t len = ((int64_t)max_sel + m - 1) / m;  // balanced
-        return (int32_t)((len + SDA_CHUNK_ALIGN - 1) / SDA_CHUNK_ALIGN * SDA_CHUNK_ALIGN);
+        const int64_t c = (len + SDA_CHUNK_ALIGN - 1) / SDA_CHUNK_ALIGN * SDA_CHUNK_ALIGN;
+        return c > INT32_MAX ? chunk_cells : (int32_t)c;
     }
     if (pairs > kResidentItems) {
         int64_t k = pairs / kResidentItems;

@@ -95,6 +95,10 @@ def test_fused_chunk_cells_sweep():
         for max_sel in (1, 63, 64, 65, 600, 2051, 4096, 16384, 65536):
             for chunk in (64, 128, 192, 256, 512, 1024):
                 assert api.fused_chunk_cells(n_inst, max_sel, chunk) == fused_chunk(n_inst, max_sel, chunk)
+    # near the int32 limit the choice stays a valid positive multiple of 64
+    for n_inst, max_sel in ((2, 2**31 - 1), (200, 2**31 - 1), (1, 2**31 - 1)):
+        c = api.fused_chunk_cells(n_inst, max_sel, 64 * 2**20)
+        assert 0 < c and c % 64 == 0
     out = C.c_int32(0)
     assert api.library().sda_fused_chunk_cells(1, 10, 100, C.byref(out)) == api.SDA_ERR_UNSUPPORTED
     assert api.library().sda_fused_chunk_cells(-1, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
