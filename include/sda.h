@@ -29,8 +29,8 @@
  *   entries count once each.
  *
  * Two entry points mirror the pages' step (one sequence) and batch (many
- * instances) entry points; both run the same two kernels (chunk, then merge)
- * on the caller's stream.  The chunk size is a parameter of the method that
+ * instances) entry points; both run the chunk pass, then the merge, on the
+ * caller's stream.  The chunk size is a parameter of the method that
  * changes the result only by rounding; for small grids these fused calls run
  * finer chunks than the caller's (sda_fused_chunk_cells).
  *
