@@ -107,9 +107,77 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p) {
     if (lane == 0) p.lse[(int64_t)i * R + r] = M + logf(L);
 }
 
+// Rows of at most NC chunks: each wave merges kRowsPerWave rows (workgroup =
+// 4 waves = 16 rows of one instance) and issues every load of its rows at
+// once, so a merge of a few partials per row is one round trip for a quarter
+// of the waves.  Per row the arithmetic is merge_kernel<1>'s, chunk by chunk.
+constexpr int kRowsPerWave = 4;
+
+template <int NC>
+__global__ __launch_bounds__(256) void merge_few_kernel(Params p) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x;
+    const int R = p.n_rows;
+    const int r0 = (4 * blockIdx.y + wave) * kRowsPerWave;
+    if (r0 >= R) return;
+    const int n = count_of(p, i);
+    const int nch = (n + p.chunk - 1) / p.chunk;  // at most NC here
+    v4f a[kRowsPerWave][NC];
+    float mc[kRowsPerWave][NC], lc[kRowsPerWave][NC];
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+        const int r = r0 + q < R ? r0 + q : R - 1;  // rows past the end: loaded, not stored
+        const int64_t row0 = (int64_t)i * p.n_chunks * R + r;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c < nch) {  // uniform across the workgroup
+                a[q][c] = *reinterpret_cast<const v4f *>(p.acc + (row0 + (int64_t)c * R) * kDim +
+                                                         4 * lane);
+                mc[q][c] = p.m[row0 + (int64_t)c * R];
+                lc[q][c] = p.l[row0 + (int64_t)c * R];
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kRowsPerWave; ++q) {
+        if (r0 + q >= R) break;
+        float M = -INFINITY, L = 0.f;
+        v4f o = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (c < nch) M = fmaxf(M, mc[q][c]);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (c < nch) {
+                const float w = mc[q][c] == -INFINITY ? 0.f : expf(mc[q][c] - M);
+                L = fmaf(lc[q][c], w, L);
+                o += w * a[q][c];
+            }
+        }
+        const int64_t u = (int64_t)i * R + r0 + q;
+        v4f *out = reinterpret_cast<v4f *>(p.out + u * kDim) + lane;
+        if (!(L > 0.f)) {  // no unmasked cell in any chunk
+            *out = (v4f){0.f, 0.f, 0.f, 0.f};
+            if (lane == 0) p.lse[u] = -INFINITY;
+        } else {
+            *out = o * (1.f / L);
+            if (lane == 0) p.lse[u] = M + logf(L);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_merge(const Params &p, hipStream_t s) {
+    if (p.n_chunks <= 2) {
+        merge_few_kernel<2><<<dim3(p.n_inst, (p.n_rows + 15) / 16), dim3(256), 0, s>>>(p);
+        return hipGetLastError();
+    }
+    if (p.n_chunks <= 4) {
+        merge_few_kernel<4><<<dim3(p.n_inst, (p.n_rows + 15) / 16), dim3(256), 0, s>>>(p);
+        return hipGetLastError();
+    }
     // rows with more chunks than one batch split them over four waves
     if (p.n_chunks > kBatch) {
         merge_kernel<4><<<dim3(p.n_inst, p.n_rows), dim3(256), 0, s>>>(p);
