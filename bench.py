@@ -263,6 +263,17 @@ def gather_ceiling():
     return [json.loads(ln) for ln in r.stdout.splitlines() if ln.startswith("{")]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(xs, budget_s):
     """The fp64 oracle on the step's inputs, repeated for about budget_s."""
     import oracle
@@ -276,7 +287,7 @@ def cpu_baseline(xs, budget_s):
         if el >= budget_s:
             break
     return {"value": round(cells / el, 1), "unit": "selected cells/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{reps} full steps of the headline workload (4 calls, n_q=1..4, "
                       f"2,051 cells each) in {el:.1f} s, fp64 C, OpenMP over query rows"}
 
