@@ -63,6 +63,11 @@ def _load():
     lib.oracle_chunk_partials.restype = None
     lib.oracle_chunk_partials.argtypes = pool + [C.c_int64, C.c_int64, C.c_void_p, C.c_int64,
                                                  _f64p, _f64p, _f64p]
+    lib.oracle_float_to_half.restype = C.c_uint16
+    lib.oracle_float_to_half.argtypes = [C.c_float]
+    lib.oracle_kv_append.restype = None
+    lib.oracle_kv_append.argtypes = [_i8p, _u16p, _i8p, _u16p, C.c_int64, C.c_int64, C.c_int64,
+                                     _i32p, C.c_int64, C.c_int64, _f32p, _f32p, C.c_int64]
     lib.oracle_prompt_attend.restype = None
     lib.oracle_prompt_attend.argtypes = [_i8p, _u16p, _i8p, _u16p, C.c_int64, C.c_int64, _i32p,
                                          C.c_int64, C.c_int64, _f32p, C.c_int64, C.c_int64,
@@ -153,6 +158,31 @@ def chunk_partials(x, chunk: int, n_chunks: int | None = None, inst_ids=None):
     lib.oracle_chunk_partials(*args, chunk, n_chunks, None if ids is None else ids.ctypes.data,
                               k, acc, m, l)
     return acc, m, l
+
+
+def float_to_half(x) -> np.ndarray:
+    """binary16 bit patterns (uint16) of float32 values, round to nearest even."""
+    lib = _load()
+    a = np.asarray(x, np.float32).reshape(-1)
+    return np.array([lib.oracle_float_to_half(float(v)) for v in a], np.uint16)
+
+
+def kv_append(pool, page_table, n_logical_pages, pos0, k_new, v_new, scale_stride=1):
+    """The KV append of one instance on copies of the pool arrays.  pool =
+    (k_codes int8 [cells][D], k_scales uint16, v_codes, v_scales), the scales
+    as flat arrays indexed by cell * scale_stride; page_table int32 row;
+    k_new, v_new float32 [n_new][D].  Returns the four updated copies."""
+    lib = _load()
+    kc, ks, vc, vs = (np.array(a, copy=True) for a in pool)
+    for a, dt in ((kc, np.int8), (ks, np.uint16), (vc, np.int8), (vs, np.uint16)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError("pool arrays: int8 codes and uint16 scales, C-contiguous")
+    kn, vn = _c(k_new, np.float32), _c(v_new, np.float32)
+    D = kc.shape[1]
+    lib.oracle_kv_append(kc, ks.reshape(-1), vc, vs.reshape(-1), int(scale_stride),
+                         kc.shape[0] // 16, D, _c(page_table, np.int32), int(n_logical_pages),
+                         int(pos0), kn, vn, kn.shape[0])
+    return kc, ks, vc, vs
 
 
 def prompt_attend(x, inst: int = 0, t_ids=None):

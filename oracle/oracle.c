@@ -184,6 +184,86 @@ void oracle_attend(const int8_t *k_codes, const uint16_t *k_scales, const int8_t
     }
 }
 
+/* IEEE binary16 bit pattern of a finite or infinite float, rounded to
+ * nearest with ties to even, written out from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits; magnitudes below
+ * 2^-14 are subnormal multiples of 2^-24; 65520 and above round to
+ * infinity.  NaN gives the quiet NaN 0x7e00. */
+uint16_t oracle_float_to_half(float x) {
+    if (isnan(x)) return 0x7e00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (a >= 65520.0) return sign | 0x7c00;
+    if (a < ldexp(1.0, -14)) {
+        double q = rint(ldexp(a, 24)); /* units of 2^-24; 1024 is the smallest normal */
+        return sign | (uint16_t)q;
+    }
+    int e;
+    double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+    e -= 1;                  /* a = (2m) * 2^e, 2m in [1, 2) */
+    double q = rint((2.0 * m - 1.0) * 1024.0);
+    if (q == 1024.0) {
+        q = 0.0;
+        e += 1;
+    }
+    return sign | (uint16_t)((e + 15) << 10) | (uint16_t)q;
+}
+
+/* INT8 quantisation of one new K or V row (the KV append step).  The pages
+ * fix only the stored format: int8 codes with one binary16 scale per cell,
+ * value = code * scale.  Reading (symmetric per-cell absmax), every step in
+ * float32 as a GPU computes it, so that both sides take each integer
+ * decision in the same precision:
+ *   amax  = max_d |x[d]|
+ *   s16   = binary16(min(amax / 127, 65504))   (round to nearest even; the
+ *           scale saturates at the largest finite binary16)
+ *   s     = the value of s16
+ *   code  = clamp(rint(x[d] / s), -127, 127)   (ties to even; all 0 if s = 0)
+ * Writes head_dim codes and the scale. */
+static void quantise_row(const float *x, int64_t head_dim, int8_t *codes, uint16_t *scale) {
+    float amax = 0.0f;
+    for (int64_t d = 0; d < head_dim; ++d) {
+        float v = fabsf(x[d]);
+        if (v > amax) amax = v;
+    }
+    float s32 = amax / 127.0f;
+    if (s32 > 65504.0f) s32 = 65504.0f;
+    uint16_t s16 = oracle_float_to_half(s32);
+    float s = (float)oracle_half_to_double(s16);
+    for (int64_t d = 0; d < head_dim; ++d) {
+        float q = 0.0f;
+        if (s > 0.0f) {
+            q = rintf(x[d] / s);
+            if (q > 127.0f) q = 127.0f;
+            if (q < -127.0f) q = -127.0f;
+        }
+        codes[d] = (int8_t)q;
+    }
+    *scale = s16;
+}
+
+/* KV append for one instance: new rows t < n_new go to logical cell
+ * c = pos0 + t, i.e. physical cell page_table[c / 16] * 16 + c % 16 (the
+ * decode gather's page map); a row whose cell is outside the table or on a
+ * masked page (-1 or outside the pool) is not written.  K and V scales of
+ * physical cell ph are k_scales[ph * scale_stride], v_scales[ph * scale_stride].
+ * k_new, v_new: float32 [n_new][head_dim]. */
+void oracle_kv_append(int8_t *k_codes, uint16_t *k_scales, int8_t *v_codes, uint16_t *v_scales,
+                      int64_t scale_stride, int64_t n_phys_pages, int64_t head_dim,
+                      const int32_t *page_table, int64_t n_logical_pages, int64_t pos0,
+                      const float *k_new, const float *v_new, int64_t n_new) {
+    for (int64_t t = 0; t < n_new; ++t) {
+        int64_t c = pos0 + t;
+        if (c < 0 || c > INT32_MAX) continue;
+        int64_t ph = gather_one((int32_t)c, page_table, n_logical_pages, n_phys_pages);
+        if (ph < 0) continue;
+        quantise_row(k_new + t * head_dim, head_dim, k_codes + ph * head_dim,
+                     k_scales + ph * scale_stride);
+        quantise_row(v_new + t * head_dim, head_dim, v_codes + ph * head_dim,
+                     v_scales + ph * scale_stride);
+    }
+}
+
 /* Prompt (many-query) attention.  Strata PR #2220 page, closing note: the
  * prompt attention's parity test takes the decode kernel as its reference.
  * Reading: query position t of an instance sits at position p = pos0 + t

@@ -519,9 +519,160 @@ def pin_prompt_causal(O):
     assert all(not np.array_equal(out[t], out2[t]) for t in range(t_cut + 1, x.n_q))
 
 
+# ------------------------------------------------------------ KV append (INT8 quantisation)
+def pin_half_encode(O):
+    """binary16 rounding against numpy's float32 -> float16 conversion
+    (round to nearest even): log-uniform magnitudes over the whole range,
+    every tie between neighbouring binary16 values, subnormals, overflow."""
+    rng = np.random.default_rng(5)
+    mag = np.exp2(rng.uniform(-30, 17, 20000)).astype(np.float32)
+    x = np.concatenate([mag, -mag])
+    h = np.arange(0, 0x7c00, 7, dtype=np.uint16).view(np.float16).astype(np.float32)
+    ties = (h[:-1].astype(np.float64) + h[1:].astype(np.float64)) / 2  # exact in float32
+    special = np.array([0.0, -0.0, 2.0**-24, 2.0**-25, 3 * 2.0**-26, 2.0**-14, 65504, 65519.99,
+                        65520, 1e30, -1e30, np.inf, -np.inf], np.float32)
+    x = np.concatenate([x, ties.astype(np.float32), special])
+    got = O.float_to_half(x)
+    with np.errstate(over="ignore"):  # values past the binary16 range become inf, on purpose
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:5]
+
+
+def _append_case(seed, n_new=40, D=256, cells=256, pos0=100, scale_stride=1, rows=None):
+    rng = np.random.default_rng(seed)
+    kc = rng.integers(-127, 128, size=(cells, D), dtype=np.int8)
+    vc = rng.integers(-127, 128, size=(cells, D), dtype=np.int8)
+    ks = rng.integers(0, 0x7c00, size=cells * scale_stride).astype(np.uint16)
+    vs = rng.integers(0, 0x7c00, size=cells * scale_stride).astype(np.uint16)
+    pt = rng.permutation(cells // 16).astype(np.int32)
+    k_new = (rng.standard_normal((n_new, D)) * np.exp2(rng.uniform(-8, 8, (n_new, 1)))).astype(np.float32)
+    v_new = (rng.standard_normal((n_new, D)) * np.exp2(rng.uniform(-8, 8, (n_new, 1)))).astype(np.float32)
+    if rows is not None:
+        for t, (k, v) in rows.items():
+            k_new[t], v_new[t] = k, v
+    return (kc, ks, vc, vs), pt, pos0, k_new, v_new
+
+
+def _written(pt, pos0, n_new, n_phys_pages):
+    """physical cell of every new row (-1: not written), from the page view."""
+    out = []
+    for t in range(n_new):
+        c = pos0 + t
+        lp = c // 16
+        ok = 0 <= c and lp < pt.size and 0 <= pt[lp] < n_phys_pages
+        out.append(int(pt[lp]) * 16 + c % 16 if ok else -1)
+    return out
+
+
+def pin_append_quantiser(O):
+    """Per written row: the scale is the binary16 of amax/127 (float32), every
+    code reconstructs its value within half a scale step, the largest |code|
+    is 127; zero rows give scale 0 and zero codes; tiny rows a zero scale;
+    huge rows a saturated scale and clamped codes."""
+    D = 256
+    rows = {0: (np.zeros(D, np.float32), np.zeros(D, np.float32)),
+            1: (np.full(D, 1e-9, np.float32), np.linspace(-1e-7, 1e-7, D).astype(np.float32)),
+            2: (np.linspace(-1e8, 1e8, D).astype(np.float32), np.full(D, 3e7, np.float32))}
+    pool, pt, pos0, kn, vn = _append_case(11, rows=rows)
+    kc, ks, vc, vs = O.kv_append(pool, pt, pt.size, pos0, kn, vn)
+    for t, ph in enumerate(_written(pt, pos0, kn.shape[0], kc.shape[0] // 16)):
+        assert ph >= 0
+        for x, codes, s16 in ((kn[t], kc[ph], ks[ph]), (vn[t], vc[ph], vs[ph])):
+            amax = np.float32(np.max(np.abs(x)))
+            s32 = min(amax / np.float32(127), np.float32(65504))
+            assert s16 == np.float32(s32).astype(np.float16).view(np.uint16), (t, s16)
+            s = float(np.uint16(s16).view(np.float16))
+            if s == 0:
+                assert not codes.any()
+                continue
+            q = codes.astype(np.float64)
+            clipped = np.abs(x.astype(np.float64) / s) > 127.5
+            err = np.abs(x.astype(np.float64) - q * s)
+            assert np.all(err[~clipped] <= s / 2 * (1 + 1e-6)), (t, err.max() / s)
+            assert np.all(np.abs(q[clipped]) == 127)
+            assert np.max(np.abs(q)) == 127, t
+    assert ks[_written(pt, pos0, 3, kc.shape[0] // 16)[2]] == 0x7bff  # saturated
+
+
+def pin_append_exact_rows(O):
+    """Rows that are integer multiples k * s of a binary16 step s with
+    max |k| = 127 come back as exactly k and s."""
+    rng = np.random.default_rng(12)
+    D, n = 256, 24
+    rows = {}
+    for t in range(n):
+        while True:
+            s = np.float16(np.exp2(rng.uniform(-12, 6))).astype(np.float32)
+            if np.float32(np.float32(127) * s / np.float32(127)).astype(np.float16) == s:
+                break
+        k = rng.integers(-127, 128, D)
+        k[rng.integers(D)] = 127 * rng.choice([-1, 1])
+        rows[t] = ((k * s).astype(np.float32), (-k * s).astype(np.float32))
+    pool, pt, pos0, kn, vn = _append_case(13, n_new=n, rows=rows)
+    kc, ks, vc, vs = O.kv_append(pool, pt, pt.size, pos0, kn, vn)
+    for t, ph in enumerate(_written(pt, pos0, n, kc.shape[0] // 16)):
+        s = kn[t][np.argmax(np.abs(kn[t]))] / 127
+        assert np.array_equal(kc[ph].astype(np.float32) * abs(s), kn[t]), t
+        assert np.array_equal(vc[ph], -kc[ph])
+        assert ks[ph] == vs[ph] == np.float32(abs(s)).astype(np.float16).view(np.uint16)
+
+
+def pin_append_placement(O):
+    """Rows land on the page view's physical cells and nowhere else: cells of
+    masked pages, rows past the table and rows before position 0 are not
+    written; with interleaved (K, V) scale pairs (stride 2) the scales go to
+    the pair of their cell."""
+    for pos0, n_new, stride in ((100, 40, 1), (-5, 20, 1), (230, 40, 1), (37, 90, 2)):
+        pool, pt, _, kn, vn = _append_case(14 + pos0 % 7, n_new=n_new, pos0=pos0,
+                                           scale_stride=stride)
+        pt = pt.copy()
+        pt[3] = -1
+        pt[9] = 10_000
+        kc, ks, vc, vs = O.kv_append(pool, pt, pt.size, pos0, kn, vn, scale_stride=stride)
+        dest = _written(pt, pos0, n_new, kc.shape[0] // 16)
+        written = sorted(p for p in dest if p >= 0)
+        changed = np.flatnonzero((kc != pool[0]).any(axis=1) | (vc != pool[2]).any(axis=1))
+        assert set(changed) <= set(written)
+        keep = np.setdiff1d(np.arange(kc.shape[0]), written)
+        assert np.array_equal(kc[keep], pool[0][keep]) and np.array_equal(vc[keep], pool[2][keep])
+        sk = np.setdiff1d(np.arange(ks.size), [p * stride for p in written])
+        assert np.array_equal(ks[sk], pool[1][sk]) and np.array_equal(vs[sk], pool[3][sk])
+        for t, ph in enumerate(dest):
+            if ph < 0:
+                continue
+            amax = np.max(np.abs(kn[t]))
+            assert ks[ph * stride] == np.float32(amax / np.float32(127)).astype(np.float16).view(np.uint16)
+            assert abs(int(kc[ph][np.argmax(np.abs(kn[t]))])) == 127  # this row, not another
+
+
+def pin_append_then_attend(O):
+    """A row appended and then attended to alone: out is its dequantised V
+    row, within half a scale step of the appended values; lse is the score
+    of the dequantised K row, within the error those steps allow."""
+    D = 256
+    pool, pt, pos0, kn, vn = _append_case(15, n_new=1, D=D, pos0=77)
+    kc, ks, vc, vs = O.kv_append(pool, pt, pt.size, pos0, kn, vn)
+    rng = np.random.default_rng(16)
+    q = rng.standard_normal((1, 1, 3, D)).astype(np.float32)
+    x = gen.Inputs(k_codes=kc, v_codes=vc, k_scales=ks, v_scales=vs,
+                   page_table=pt[None, :], sel=np.array([[pos0]], np.int32),
+                   n_sel=np.array([1], np.int32), q=q, softmax_scale=1 / 16, chunk=64,
+                   workload="append_then_attend", seed=0)
+    out, lse = O.attend(x)
+    sv = float(np.uint16(vs[_written(pt, pos0, 1, kc.shape[0] // 16)[0]]).view(np.float16))
+    sk = float(np.uint16(ks[_written(pt, pos0, 1, kc.shape[0] // 16)[0]]).view(np.float16))
+    for h in range(3):
+        assert np.all(np.abs(out[0, 0, h] - vn[0]) <= sv / 2 * (1 + 1e-6))
+        exact = float(q[0, 0, h].astype(np.float64) @ kn[0].astype(np.float64)) / 16
+        bound = np.sum(np.abs(q[0, 0, h].astype(np.float64))) * sk / 2 / 16
+        assert abs(lse[0, 0, h] - exact) <= bound * (1 + 1e-6) + 1e-12
+
+
 ALL_PINS = [pin_half_decode, pin_textbook, pin_gather_exhaustive, pin_one_cell, pin_two_cells,
             pin_zero_query, pin_identical_keys, pin_worked_example, pin_merge_closed_form,
             pin_empty_and_masked, pin_permutation, pin_chunking, pin_score_shift,
             pin_relabel_pages, pin_mask_equals_delete, pin_double_v_scales, pin_duplicates,
             pin_brute_force_subsets, pin_prompt_textbook, pin_prompt_first_cell,
-            pin_prompt_is_decode_of_prefix, pin_prompt_causal]
+            pin_prompt_is_decode_of_prefix, pin_prompt_causal, pin_half_encode,
+            pin_append_quantiser, pin_append_exact_rows, pin_append_placement,
+            pin_append_then_attend]

@@ -61,6 +61,19 @@ MUTANTS = {
                                "attend_range(&P, q + (h * n_q + t) * D, list,"),
     "prompt_sees_one_more": ("int64_t n_visible = p + 1 > 0 ? p + 1 : 0;",
                              "int64_t n_visible = p + 2 > 0 ? p + 2 : 0;"),
+    "half_truncates": ("double q = rint((2.0 * m - 1.0) * 1024.0);",
+                       "double q = floor((2.0 * m - 1.0) * 1024.0);"),
+    "half_bias_off": ("return sign | (uint16_t)((e + 15) << 10) | (uint16_t)q;",
+                      "return sign | (uint16_t)((e + 14) << 10) | (uint16_t)q;"),
+    "quant_truncates": ("q = rintf(x[d] / s);", "q = truncf(x[d] / s);"),
+    "quant_no_clamp": ("if (q > 127.0f) q = 127.0f;", "(void)0;"),
+    "quant_scale_128": ("float s32 = amax / 127.0f;", "float s32 = amax / 128.0f;"),
+    "quant_no_saturation": ("if (s32 > 65504.0f) s32 = 65504.0f;", "(void)0;"),
+    "append_ignores_pos0": ("int64_t c = pos0 + t;\n        if (c < 0 || c > INT32_MAX) continue;",
+                            "int64_t c = t;\n        if (c < 0 || c > INT32_MAX) continue;"),
+    "append_kv_swapped": ("quantise_row(v_new + t * head_dim, head_dim, v_codes + ph * head_dim,",
+                          "quantise_row(k_new + t * head_dim, head_dim, v_codes + ph * head_dim,"),
+    "append_scale_stride_ignored": ("k_scales + ph * scale_stride);", "k_scales + ph);"),
 }
 
 
