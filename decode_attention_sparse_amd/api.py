@@ -21,7 +21,7 @@ PROMPT_MAX_ROWS = 65535 * 48
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
             "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_fused_chunk_cells",
-            "sda_status_string")
+            "sda_kv_append_batch", "sda_status_string")
 
 
 class SdaError(RuntimeError):
@@ -63,6 +63,9 @@ def library() -> C.CDLL:
         lib.sda_prompt_attn_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, vp, i32, i32,
                                               f32, vp, vp, vp]
         lib.sda_prompt_attn_batch.restype = C.c_int
+        # sda_pool_mut has sda_pool's layout (writable pointers)
+        lib.sda_kv_append_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, vp, vp, i32, vp]
+        lib.sda_kv_append_batch.restype = C.c_int
         lib.sda_fused_chunk_cells.argtypes = [i32, i32, i32, C.POINTER(i32)]
         lib.sda_fused_chunk_cells.restype = C.c_int
         lib.sda_status_string.argtypes = [C.c_int]
@@ -230,6 +233,23 @@ def prompt_attn_batch(pool: Pool, page_table, pos0, q, softmax_scale: float, out
         n_q, n_qheads, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream))
     if st != SDA_OK:
         raise SdaError(st, "sda_prompt_attn_batch")
+
+
+def kv_append_batch(pool: Pool, page_table, pos0, k_new, v_new, stream=None,
+                    n_logical_pages: int | None = None):
+    """Quantise new rows k_new, v_new float32 [n_inst][n_new][256] into the
+    pools at logical cells pos0[i] + t (pos0 device int32 [n_inst]) through
+    page_table [n_inst][pt_stride]; writes the pool tensors in place."""
+    n_inst, n_new = int(k_new.shape[0]), int(k_new.shape[1])
+    if tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new and v_new must have the same shape")
+    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    ps = pool.c_struct()
+    st = library().sda_kv_append_batch(C.byref(ps), n_inst, _ptr(page_table),
+                                       int(page_table.stride(0)), nlp, _ptr(pos0), _ptr(k_new),
+                                       _ptr(v_new), n_new, _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_kv_append_batch")
 
 
 def to_device(x, device="cuda", interleave_scales=False):

@@ -32,13 +32,14 @@
 //       MFMA chain; 2^8 A + B is formed in int32 (|.| < 2^30) before the
 //       conversion to fp32.  Score errors are at fp32 level relative to the
 //       wave's largest score.
-//   PV  x = p * v_scale / tau in [0, 127], tau = 2^(tile max - running max)
-//       * (tile max v_scale) / 127 per row and tile; X = rint(256 x) in
-//       [0, 32512] is written as 2^8 hi + lo (hi in [0,127], lo in
-//       [-128,127]); the tile's sum over cells of X * v_code (two MFMAs,
-//       combined as 2^8 HI + LO) is exact in int32 and folded into the fp32
-//       accumulator once per tile.  The probability split keeps 15 bits
-//       relative to the tile's largest weighted probability.
+//   PV  x = p * v_scale / tau in [0, 127], tau = (the row's largest
+//       p * v_scale in the tile) / 127; X = rint(256 x) in [0, 32512] is
+//       written as 2^8 hi + lo (hi in [0,127], lo in [-128,127]); the tile's
+//       sum over cells of X * v_code (two MFMAs, combined as 2^8 HI + LO) is
+//       exact in int32 and folded into the fp32 accumulator once per tile.
+//       The probability split keeps 15 bits relative to the tile's largest
+//       weighted probability p * v_scale, whatever the spread of the V
+//       scales.
 //
 // Pipeline.  Iteration t of the tile loop computes the scores of tile t+1
 // while it runs the softmax and the V accumulation of tile t, so matrix-core
@@ -70,7 +71,7 @@ constexpr int kStride = kDim + 16;   // LDS bytes per code row (padded)
 constexpr int kBuf = kTile * kStride;
 constexpr int kRows = kTile / 4;     // 1 KB staging loads per tile and pool (4 rows each)
 constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^22) to integers in the low bits
-constexpr float kFarBelow = 64.f;    // tiles 2^64 below the running max carry no weight
+constexpr float kWTiny = 7.888609052210118e-31f;  // 2^-100: tiles whose weights stay below carry none
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
 constexpr int64_t kLatencyWorkgroups = 256;         // grids up to one workgroup per CU
@@ -204,7 +205,7 @@ struct RowBlock {
     }
 
     // One tile: the softmax and V accumulation of the tile whose scores are
-    // in su (V rows vb, V scales vs, largest V scale vmax), and the scores of
+    // in su (V rows vb, V scales vs), and the scores of
     // the next tile (K rows kb, K scales ks, bias 0 or -inf per cell) into su,
     // or -inf everywhere when next_ok is false.  kCausal: cells of the next
     // tile past index lim (this lane's row's last visible cell, counted from
@@ -212,7 +213,7 @@ struct RowBlock {
     template <bool kCausal = false>
     __device__ __forceinline__ void step(const int8_t *kb, const float *ks_t, const float *bias_t,
                                          bool next_ok, const int8_t *vb, const float *vs_t,
-                                         float vmax, int dh, int lim = 0) {
+                                         int dh, int lim = 0) {
         // ---------------- softmax statistics of the current tile (scores in su)
         float tmax = -INFINITY;
 #pragma unroll
@@ -226,12 +227,6 @@ struct RowBlock {
         const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
         const float frame_new = (m_run == -INFINITY) ? 1.f : frame * corr;
         m_run = m_new;
-        // W = 256 / tau; X = rint(p * v_scale * W) lands in the low bits of
-        // fma(p, v_scale * W, 2^23)
-        const bool live = tmax != -INFINITY && vmax > 0.f && (m_use - tmax) < kFarBelow;
-        const float W = live ? (256.f * 127.f) * __builtin_amdgcn_rcpf(vmax) *
-                                   __builtin_amdgcn_exp2f(m_use - tmax)
-                             : 0.f;
 
         // ---------------- scores of the next tile: u = (AB + C/2^8) * k_scale + bias
         v4f sn[4];
@@ -271,19 +266,32 @@ struct RowBlock {
         }
 
         // ---------------- probabilities and their digits for the current tile
+        // weights w = p * v_scale; W = 256 / tau = 32512 / (row max of w), and
+        // X = rint(w * W) lands in the low bits of fma(w, W, 2^23)
         float psum = 0.f;
-        v4i xa, xb;
+        float wt[4][4];
+        float wmax = 0.f;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
             const v4f vs = *reinterpret_cast<const v4f *>(vs_t + mo);
-            unsigned xs[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -m_use));
                 psum += pr;
-                xs[u] = __float_as_uint(fmaf(pr, vs[u] * W, kRound));
+                wt[cb][u] = pr * vs[u];
+                wmax = fmaxf(wmax, wt[cb][u]);
             }
+        }
+        wmax = max4(wmax);
+        const bool live = wmax > kWTiny;
+        const float W = live ? (256.f * 127.f) * __builtin_amdgcn_rcpf(wmax) : 0.f;
+        v4i xa, xb;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            unsigned xs[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xs[u] = __float_as_uint(fmaf(wt[cb][u], W, kRound));
             // low digit = byte 0 of X; high digit = byte 1 of X + 128
             const unsigned lo01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
             const unsigned lo23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
@@ -388,7 +396,6 @@ void chunk_mfma_kernel(Params p, int cpw) {
     __shared__ __attribute__((aligned(16))) float ks_s[4][kTile];
     __shared__ __attribute__((aligned(16))) float vs_s[4][kTile];
     __shared__ __attribute__((aligned(16))) float bias_s[4][kTile];
-    __shared__ float vmax_s[4];
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -427,7 +434,6 @@ void chunk_mfma_kernel(Params p, int cpw) {
         (&vs_s[0][0])[e] = 0.f;
         (&bias_s[0][0])[e] = -INFINITY;
     }
-    if (threadIdx.x < 4) vmax_s[threadIdx.x] = 0.f;
     __syncthreads();
 
     // Both roles run n_tiles + 4 iterations with one barrier each.  Iteration
@@ -507,8 +513,6 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 ks_s[m2][lane] = ksf;
                 vs_s[m2][lane] = vsf;
                 bias_s[m2][lane] = ok ? 0.f : -INFINITY;
-                const float vm = wave_max(vsf);
-                if (lane == 0) vmax_s[m2] = vm;
             }
             if (t + 3 >= 0 && t + 3 < n_tiles) {
                 int ph = -1;
@@ -546,9 +550,9 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 // the scores of tile t + 1, whose first cell is j_begin + 64 (t + 1)
                 const int64_t lim = lim_row - (j_begin + (int64_t)(t + 1) * kTile);
                 rb.template step<true>(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0],
-                                       vmax_s[m0], dh, (int)max((int64_t)-1, min(lim, (int64_t)kTile)));
+                                       dh, (int)max((int64_t)-1, min(lim, (int64_t)kTile)));
             } else {
-                rb.step(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0], vmax_s[m0], dh);
+                rb.step(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0], dh);
             }
             // end of a chunk: emit its partial, start afresh
             if (!kPrompt && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
@@ -571,10 +575,10 @@ constexpr int kPtLdsPages = 2048;  // page tables up to this size are staged who
 // into LDS in the same round trip as the list entries, so the lookup is an
 // LDS read: two dependent round trips to memory instead of three.  LDS
 // layout as in the pipelined kernel (row r = tile cell r, padded rows;
-// scales, bias and the tile's largest V scale by cell).
+// scales and bias by cell).
 __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j_end, int lane,
                                            int8_t *kb, int8_t *vb, float *ks, float *vs,
-                                           float *bias, float *vmax, int *pt_s) {
+                                           float *bias, int *pt_s) {
     const int g = lane >> 4, l16 = lane & 15;
     const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
     const int32_t *sel = p.sel + (int64_t)i * p.sel_stride;
@@ -649,8 +653,6 @@ __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j
     ks[lane] = ksf;
     vs[lane] = vsf;
     bias[lane] = ok ? 0.f : -INFINITY;
-    const float vm = wave_max(vsf);
-    if (lane == 0) *vmax = vm;
     int8_t *kd = kb + l16 * kStride + 16 * g;
     int8_t *vd = vb + l16 * kStride + 16 * g;
 #pragma unroll
@@ -679,7 +681,6 @@ void chunk_tile_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) float ks_s[kTile];
     __shared__ __attribute__((aligned(16))) float vs_s[kTile];
     __shared__ __attribute__((aligned(16))) float bias_s[kTile];
-    __shared__ float vmax_s;
     __shared__ __attribute__((aligned(16))) int pt_s[kPtLdsPages];
 
     const int wave = threadIdx.x >> 6;
@@ -692,7 +693,7 @@ void chunk_tile_kernel(Params p) {
     const int j_end = min(j_begin + kTile, n);
 
     if (wave == kProducer) {
-        stage_tile(p, i, j_begin, j_end, lane, kbuf, vbuf, ks_s, vs_s, bias_s, &vmax_s,
+        stage_tile(p, i, j_begin, j_end, lane, kbuf, vbuf, ks_s, vs_s, bias_s,
                    p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
         __syncthreads();
         return;
@@ -704,8 +705,8 @@ void chunk_tile_kernel(Params p) {
     RowBlock<kDB> rb;
     rb.init(p.q + ((int64_t)i * R + (row < R ? row : 0)) * kDim, row < R, p.scale_log2, g, l16);
     __syncthreads();
-    rb.step(kbuf, ks_s, bias_s, true, vbuf, vs_s, vmax_s, dh);   // scores of the tile
-    rb.step(kbuf, ks_s, bias_s, false, vbuf, vs_s, vmax_s, dh);  // its softmax and V
+    rb.step(kbuf, ks_s, bias_s, true, vbuf, vs_s, dh);   // scores of the tile
+    rb.step(kbuf, ks_s, bias_s, false, vbuf, vs_s, dh);  // its softmax and V
     rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
 }
 

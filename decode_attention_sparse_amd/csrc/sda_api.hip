@@ -300,6 +300,44 @@ int sda_prompt_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
     return SDA_OK;
 }
 
+int sda_kv_append_batch(const sda_pool_mut *pool, int32_t n_inst, const int32_t *page_table,
+                        int64_t pt_stride, int32_t n_logical_pages, const int32_t *pos0,
+                        const float *k_new, const float *v_new, int32_t n_new, void *stream) {
+    if (!pool) return SDA_ERR_INVALID_ARG;
+    const sda_pool view = {pool->k_codes, pool->k_scales, pool->v_codes, pool->v_scales,
+                           pool->n_phys_pages, pool->page_size, pool->head_dim,
+                           pool->scale_stride, pool->reserved};
+    int st = check_pool(&view);
+    if (st != SDA_OK) return st;
+    if (n_inst < 0 || n_new < 0 || n_logical_pages < 0 || pt_stride < n_logical_pages)
+        return SDA_ERR_INVALID_ARG;
+    if (n_inst > 65535) return SDA_ERR_UNSUPPORTED;
+    if (n_inst == 0 || n_new == 0) return SDA_OK;
+    if (!pos0 || !k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))
+        return SDA_ERR_INVALID_ARG;
+    if (n_logical_pages > 0 && !page_table) return SDA_ERR_INVALID_ARG;
+    sda::AppendParams p;
+    memset(&p, 0, sizeof p);
+    p.k_codes = pool->k_codes;
+    p.k_scales = pool->k_scales;
+    p.v_codes = pool->v_codes;
+    p.v_scales = pool->v_scales;
+    p.scale_stride = pool->scale_stride;
+    p.n_phys_pages = pool->n_phys_pages;
+    p.page_table = page_table;
+    p.pt_stride = pt_stride;
+    p.n_logical_pages = n_logical_pages;
+    p.pos0 = pos0;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.n_inst = n_inst;
+    p.n_new = n_new;
+    (void)hipGetLastError();
+    if (sda::launch_kv_append(p, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SDA_ERR_LAUNCH;
+    return SDA_OK;
+}
+
 const char *sda_status_string(int status) {
     switch (status) {
         case SDA_OK: return "SDA_OK";

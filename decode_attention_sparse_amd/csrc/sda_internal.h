@@ -60,7 +60,26 @@ __device__ __forceinline__ int count_of(const Params &p, int i) {
     return n > p.max_sel ? p.max_sel : n;
 }
 
+// KV append: new rows [n_inst][n_new][kDim] into the pools (already validated).
+struct AppendParams {
+    int8_t *k_codes;
+    uint16_t *k_scales;
+    int8_t *v_codes;
+    uint16_t *v_scales;
+    int64_t scale_stride;
+    int64_t n_phys_pages;
+    const int32_t *page_table;  // [n_inst][pt_stride]
+    int64_t pt_stride;
+    int32_t n_logical_pages;
+    const int32_t *pos0;        // device [n_inst]: position of new row 0
+    const float *k_new;         // [n_inst][n_new][kDim]
+    const float *v_new;
+    int32_t n_inst;
+    int32_t n_new;
+};
+
 hipError_t launch_chunk(const Params &p, hipStream_t s);
+hipError_t launch_kv_append(const AppendParams &p, hipStream_t s);
 hipError_t launch_merge(const Params &p, hipStream_t s);
 hipError_t launch_prompt(const Params &p, hipStream_t s);
 

@@ -236,3 +236,60 @@ def make_prompt(name: str | None = None, seed: int | None = None, pos0=None,
     fields = {f.name: getattr(x, f.name) for f in dataclasses.fields(x)}  # no copies
     return PromptInputs(**fields, pos0=pos0)
 
+
+# KV append (new K/V rows quantised into the pools).  The pages give no
+# append workload; this one appends a prompt chunk of 2,048 rows to each of
+# 64 (sequence, KV head) instances whose pools hold 32K cells, the new rows
+# at the end of each context (pos0 = pool_cells - n_new).
+APPEND_CONFIGS = {
+    "kv_append_64inst_2048rows": dict(n_inst=64, n_new=2048, pool_cells=32768),
+}
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    page_table: np.ndarray  # int32 [n_inst][pages]: a permutation of the instance's own pages
+    pos0: np.ndarray        # int32 [n_inst]: logical cell of new row 0
+    k_new: np.ndarray       # float32 [n_inst][n_new][head_dim]
+    v_new: np.ndarray
+    pool_cells: int         # cells per instance (pool = n_inst * pool_cells cells)
+    workload: str
+    seed: int
+
+    @property
+    def n_inst(self) -> int:
+        return int(self.k_new.shape[0])
+
+    @property
+    def n_new(self) -> int:
+        return int(self.k_new.shape[1])
+
+
+def make_append(name: str | None = None, seed: int | None = None, pos0=None, spread: float = 8.0,
+                **overrides) -> AppendInputs:
+    """Page tables drawn as make() draws them, new rows N(0, 1) scaled per row
+    by 2^U(-spread, spread) (rows of very different magnitudes)."""
+    spec = dict(APPEND_CONFIGS[name]) if name is not None else {"n_inst": 1}
+    spec.update(overrides)
+    n_inst, n_new, cells = int(spec["n_inst"]), int(spec["n_new"]), int(spec["pool_cells"])
+    D = int(spec.get("head_dim", HEAD_DIM))
+    pages = cells // PAGE_SIZE
+    seed = 20261400 if seed is None else seed
+    children = np.random.SeedSequence(seed).spawn(n_inst)
+    pt = np.empty((n_inst, pages), np.int32)
+    k_new = np.empty((n_inst, n_new, D), np.float32)
+    v_new = np.empty((n_inst, n_new, D), np.float32)
+    def fill(i):
+        rng = np.random.Generator(np.random.PCG64(children[i]))
+        pt[i] = rng.permutation(pages) + i * pages
+        for a in (k_new, v_new):
+            a[i] = rng.standard_normal((n_new, D), dtype=np.float32)
+            a[i] *= np.exp2(rng.uniform(-spread, spread, (n_new, 1))).astype(np.float32)
+
+    with _cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(n_inst)))
+    if pos0 is None:
+        pos0 = cells - n_new
+    pos0 = np.broadcast_to(np.asarray(pos0, np.int32), (n_inst,)).copy()
+    return AppendInputs(page_table=pt, pos0=pos0, k_new=k_new, v_new=v_new, pool_cells=cells,
+                        workload=str(spec.get("workload", name or "custom_append")), seed=seed)

@@ -243,6 +243,50 @@ int sda_prompt_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
                           const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
                           float *out, float *lse, void *stream);
 
+/* The pools as the KV append writes them: the same layout and rules as
+ * sda_pool, with writable pointers. */
+typedef struct sda_pool_mut {
+    int8_t *k_codes;
+    uint16_t *k_scales;
+    int8_t *v_codes;
+    uint16_t *v_scales;
+    int64_t n_phys_pages;
+    int32_t page_size;    /* must be SDA_PAGE_SIZE */
+    int32_t head_dim;     /* must be SDA_HEAD_DIM */
+    int32_t scale_stride; /* elements between the scales of consecutive cells, in [1, 64] */
+    int32_t reserved;     /* must be 0 */
+} sda_pool_mut;
+
+/* KV append: quantise new K and V rows to INT8 and write them into the
+ * pools, the step that produces what the attention reads.  The pages fix
+ * the stored format (INT8 codes, one binary16 scale per cell for K and one
+ * for V; Strata PR #2220 page) and list the KV append after the K/V
+ * projection (Strata round-9 page, section "R9-gpu-8: one exact launch for
+ * QSA K and V"), not the quantiser.  This one is symmetric per-cell absmax,
+ * every step in float32:
+ *   amax = max_d |x[d]|;  scale = binary16(min(amax / 127, 65504)), rounded
+ *   to nearest even;  code[d] = clamp(rint(x[d] / scale), -127, 127) with
+ *   ties to even and correctly rounded division; all codes 0 when the scale
+ *   is 0 (amax below about 127 * 2^-25).
+ * New row t of instance i goes to logical cell c = pos0[i] + t, i.e.
+ * physical cell page_table[i][c / 16] * 16 + c % 16 (the attention's page
+ * map).  A row whose cell is outside [0, 16 * n_logical_pages) or on a page
+ * with id -1 or outside [0, n_phys_pages) is not written.
+ *   pool          host pointer, writable pools (as sda_pool)
+ *   n_inst        host, in [0, 65535] (0: nothing is launched)
+ *   page_table    int32 [n_inst][pt_stride] (may be NULL if n_logical_pages == 0)
+ *   pos0          DEVICE int32 [n_inst]
+ *   k_new, v_new  float [n_inst][n_new][head_dim], 16-byte aligned, finite
+ *                 (non-finite values give unspecified codes)
+ *   n_new         host, >= 0
+ *   stream        hipStream_t (NULL = default stream)
+ * Two new rows that map to the same physical cell (in one call) race: the
+ * cell ends up holding one of them.  Returns SDA_OK, SDA_ERR_INVALID_ARG,
+ * SDA_ERR_UNSUPPORTED or SDA_ERR_LAUNCH. */
+int sda_kv_append_batch(const sda_pool_mut *pool, int32_t n_inst, const int32_t *page_table,
+                        int64_t pt_stride, int32_t n_logical_pages, const int32_t *pos0,
+                        const float *k_new, const float *v_new, int32_t n_new, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *sda_status_string(int status);
 

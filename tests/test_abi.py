@@ -246,3 +246,29 @@ def test_prompt_rejects_before_launch():
     assert call(out=FAKE + 8) == api.SDA_ERR_INVALID_ARG
     assert call(lse=None) == api.SDA_ERR_INVALID_ARG
     assert call(n_inst=0) == api.SDA_OK                           # nothing to do, nothing launched
+
+
+def test_append_rejects_before_launch():
+    lib = api.library()
+    def call(pool=None, **kw):
+        pool = _pool() if pool is None else pool
+        a = dict(n_inst=2, pt=FAKE, pts=8, nlp=8, pos0=FAKE, k=FAKE, v=FAKE, n_new=5)
+        a.update(kw)
+        return lib.sda_kv_append_batch(C.byref(pool), a["n_inst"], a["pt"], a["pts"], a["nlp"],
+                                       a["pos0"], a["k"], a["v"], a["n_new"], None)
+    assert lib.sda_kv_append_batch(None, 1, FAKE, 8, 8, FAKE, FAKE, FAKE, 1, None) == api.SDA_ERR_INVALID_ARG
+    assert call(pool=_pool(head_dim=128)) == api.SDA_ERR_UNSUPPORTED
+    assert call(pool=_pool(page_size=8)) == api.SDA_ERR_UNSUPPORTED
+    assert call(pool=_pool(v_codes=None)) == api.SDA_ERR_INVALID_ARG
+    assert call(pool=_pool(k_codes=FAKE + 8)) == api.SDA_ERR_INVALID_ARG
+    assert call(pool=_pool(scale_stride=0)) == api.SDA_ERR_INVALID_ARG
+    assert call(n_inst=-1) == api.SDA_ERR_INVALID_ARG
+    assert call(n_new=-1) == api.SDA_ERR_INVALID_ARG
+    assert call(nlp=-1) == api.SDA_ERR_INVALID_ARG
+    assert call(pts=7) == api.SDA_ERR_INVALID_ARG
+    assert call(n_inst=65536) == api.SDA_ERR_UNSUPPORTED
+    assert call(pos0=None) == api.SDA_ERR_INVALID_ARG
+    assert call(k=None) == api.SDA_ERR_INVALID_ARG
+    assert call(v=FAKE + 4) == api.SDA_ERR_INVALID_ARG
+    assert call(pt=None) == api.SDA_ERR_INVALID_ARG
+    assert call(n_inst=0) == api.SDA_OK and call(n_new=0) == api.SDA_OK  # nothing launched

@@ -1,0 +1,151 @@
+"""GPU parity of the INT8 KV append (sda_kv_append_batch through the C ABI)
+against the CPU oracle's kv_append: the whole pools after the call (codes and
+scales of every cell, written or not) must be identical bit for bit, since
+every code is an integer decision both sides take in float32."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_sparse_amd import inputs as gen
+from tests.gpu_util import (LSE_ATOL, LSE_RTOL, OUT_ATOL, OUT_RTOL, assert_close, run_prompt,
+                            say)
+
+pytestmark = pytest.mark.gpu
+
+
+def random_pools(seed, n_inst, cells, scale_stride=1):
+    rng = np.random.default_rng(seed)
+    total = n_inst * cells
+    kc = rng.integers(-127, 128, size=(total, 256), dtype=np.int8)
+    vc = rng.integers(-127, 128, size=(total, 256), dtype=np.int8)
+    scales = rng.integers(0, 0x7c00, size=(2, total * scale_stride)).astype(np.uint16)
+    return kc, scales[0].copy(), vc, scales[1].copy()
+
+
+def run_append(pools, x, scale_stride=1):
+    """Upload pools and rows, append on the GPU, return the four arrays."""
+    import torch
+    from decode_attention_sparse_amd import api
+    kc, ks, vc, vs = pools
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    if scale_stride == 2:
+        # one [cells][2] array of (K, V) pairs; the oracle's K and V scale
+        # arrays hold them at the even indices (cell * 2)
+        pairs = t(np.stack([ks[0::2], vs[0::2]], axis=1).view(np.int16))
+        pool = api.Pool(t(kc), None, t(vc), None, scales=pairs)
+    else:
+        pool = api.Pool(t(kc), t(ks.view(np.int16)), t(vc), t(vs.view(np.int16)))
+    api.kv_append_batch(pool, t(x.page_table), t(x.pos0), t(x.k_new), t(x.v_new))
+    torch.cuda.synchronize()
+    if scale_stride == 2:
+        pr = pool.scales.cpu().numpy().view(np.uint16)
+        ks2, vs2 = ks.copy(), vs.copy()
+        ks2[0::2], vs2[0::2] = pr[:, 0], pr[:, 1]
+        return pool.k_codes.cpu().numpy(), ks2, pool.v_codes.cpu().numpy(), vs2
+    return (pool.k_codes.cpu().numpy(), pool.k_scales.cpu().numpy().view(np.uint16),
+            pool.v_codes.cpu().numpy(), pool.v_scales.cpu().numpy().view(np.uint16))
+
+
+def oracle_append(pools, x, scale_stride=1):
+    cur = tuple(np.array(a, copy=True) for a in pools)
+    for i in range(x.n_inst):
+        cur = oracle.kv_append(cur, x.page_table[i], x.page_table.shape[1], int(x.pos0[i]),
+                               x.k_new[i], x.v_new[i], scale_stride=scale_stride)
+    return cur
+
+
+def check_equal(got, ref, what):
+    names = ("k codes", "k scales", "v codes", "v scales")
+    for g, r, nm in zip(got, ref, names):
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)
+            raise AssertionError(f"{what}: {nm} differ at {len(bad)} places, first {bad[:3].tolist()}")
+    say(f"  {what}: pools identical")
+
+
+def special_rows(x):
+    """Zero, tiny (subnormal binary16 scale), huge (saturated scale) rows and
+    rows of exact ties (x / scale = k + 1/2) as the first new rows (as many
+    as there are)."""
+    k, v = x.k_new.copy(), x.v_new.copy()
+    D = k.shape[-1]
+    s = np.float32(2.0 ** -3)  # the tie rows' amax is exactly 127 s
+    ties = (np.arange(D) % 120 - 60 + 0.5).astype(np.float32) * s
+    ties[0] = 127 * s
+    rows = [(np.zeros(D), np.zeros(D)),
+            (np.linspace(-1e-5, 1e-5, D), np.full(D, 3e-6)),       # scale 7.9e-8: subnormal
+            (np.linspace(-1e9, 1e9, D), np.full(D, -5e7)),         # saturated, clamped
+            (ties, -ties)]
+    for t, (rk, rv) in enumerate(rows[: x.n_new]):
+        k[0, t], v[0, t] = rk, rv
+    return dataclasses.replace(x, k_new=k, v_new=v)
+
+
+CASES = {
+    # name: (make_append overrides, pos0, page-table edits, scale_stride)
+    "tail_37_rows": (dict(n_inst=1, n_new=37, pool_cells=1024, seed=1), None, [], 1),
+    "three_instances": (dict(n_inst=3, n_new=100, pool_cells=1024, seed=2), [0, 500, 924], [], 1),
+    "masked_and_past_table": (dict(n_inst=2, n_new=60, pool_cells=512, seed=3), [470, 10],
+                              [(1, -1), (30, 99_999)], 1),
+    "negative_pos0": (dict(n_inst=1, n_new=20, pool_cells=256, seed=4), [-7], [], 1),
+    "interleaved_scales": (dict(n_inst=2, n_new=45, pool_cells=512, seed=5), [3, 200], [], 2),
+    "one_row": (dict(n_inst=1, n_new=1, pool_cells=256, seed=6), [255], [], 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_append_cases(name):
+    kw, pos0, edits, stride = CASES[name]
+    kw = dict(kw)
+    seed = kw.pop("seed")
+    say(f"case: kv append {name} {kw} pos0={pos0} edits={edits} stride={stride}")
+    x = special_rows(gen.make_append(None, seed=seed, pos0=pos0, **kw))
+    pt = x.page_table.copy()
+    for lp, val in edits:
+        pt[:, lp] = val
+    x = dataclasses.replace(x, page_table=pt)
+    pools = random_pools(seed + 100, x.n_inst, x.pool_cells, stride)
+    check_equal(run_append(pools, x, stride), oracle_append(pools, x, stride), name)
+
+
+def test_append_full_size_sampled():
+    """The bench workload (64 instances x 2,048 rows into 32K-cell pools); the
+    oracle recomputes sampled instances on their own pool slices."""
+    x = gen.make_append("kv_append_64inst_2048rows")
+    say("case: kv append 64 x 2,048 rows, oracle on instances [0, 17, 63]")
+    cells = x.pool_cells
+    pools = tuple(np.zeros(s, dt) for s, dt in (((64 * cells, 256), np.int8), (64 * cells, np.uint16),
+                                                ((64 * cells, 256), np.int8), (64 * cells, np.uint16)))
+    got = run_append(pools, x)
+    for i in (0, 17, 63):
+        sl = slice(i * cells, (i + 1) * cells)
+        sub = (pools[0][sl], pools[1][sl], pools[2][sl], pools[3][sl])
+        pt = x.page_table[i] - i * (cells // 16)  # the instance's pages, counted from its slice
+        ref = oracle.kv_append(sub, pt, pt.size, int(x.pos0[i]), x.k_new[i], x.v_new[i])
+        check_equal(tuple(g[sl] for g in got), ref, f"instance {i}")
+
+
+def test_append_then_prompt_attention():
+    """A prompt chunk's K and V appended into the pool, then attended to by
+    the chunk's queries: GPU append + GPU prompt attention against the
+    oracle's append + prompt attention.  The appended rows spread over 2^+-2
+    (scores of order 10); with rows over 2^+-8 the scores reach the
+    thousands, where a plain float32 attention already misses 1e-3."""
+    say("case: append a 300-row prompt chunk, then prompt attention over the pool")
+    base = gen.make_prompt(None, seed=21, n_q=300, pool_cells=2048)
+    app = gen.make_append(None, seed=22, n_inst=1, n_new=300, pool_cells=2048,
+                          pos0=int(base.pos0[0]), spread=2.0)
+    app = dataclasses.replace(app, page_table=base.page_table)
+    pools = (base.k_codes, base.k_scales, base.v_codes, base.v_scales)
+    gpu_pools = run_append(pools, app)
+    ref_pools = oracle_append(pools, app)
+    check_equal(gpu_pools, ref_pools, "appended pools")
+    x = dataclasses.replace(base, k_codes=gpu_pools[0], k_scales=gpu_pools[1],
+                            v_codes=gpu_pools[2], v_scales=gpu_pools[3])
+    out, lse = run_prompt(x)
+    ro, rl = oracle.prompt_attend(x, 0)
+    e1 = assert_close(out[0], ro, OUT_ATOL, OUT_RTOL, "append+prompt out")
+    e2 = assert_close(lse[0], rl, LSE_ATOL, LSE_RTOL, "append+prompt lse")
+    say(f"  append + prompt: max|dout| {e1:.2e} max|dlse| {e2:.2e}")

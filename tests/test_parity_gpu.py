@@ -45,6 +45,30 @@ def test_config1_pages_kernel_point(n_q):
     check(x, out, lse, g, what=f"cfg1 nq{n_q}")
 
 
+def wide_scales(x, seed, octaves=8):
+    """K and V scales spread over 2^-octaves .. 2^octaves times their drawn
+    values, independently per cell (rows of very different magnitudes)."""
+    rng = np.random.default_rng(seed)
+    def spread(bits):
+        v = bits.view(np.float16).astype(np.float32)
+        v = v * np.exp2(rng.uniform(-octaves, octaves, v.shape)).astype(np.float32)
+        return v.astype(np.float16).view(np.uint16)
+    return dataclasses.replace(x, k_scales=spread(x.k_scales), v_scales=spread(x.v_scales))
+
+
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_wide_scale_range(n_q):
+    """K and V scales spanning 2^16: each tile's probability digits are
+    scaled by the row's largest p * v_scale, so the accuracy does not depend
+    on how far apart the largest probability and the largest V scale are."""
+    say(f"case: scales over 2^16, config 1, n_q={n_q}")
+    x = wide_scales(gen.make(1).with_n_q(n_q), 40 + n_q)
+    out, lse, g, _ = run_batch(x)
+    check(x, out, lse, g, what=f"wide scales nq{n_q}")
+    o2, l2, g2, _ = two_pass(x, 256)
+    check(x, o2, l2, g2, what=f"wide scales nq{n_q}, two passes at chunk 256")
+
+
 @pytest.mark.parametrize("cfg", [0, 1])
 def test_interleaved_scales(cfg):
     """(K, V) scale pairs interleaved per cell (scale_stride 2) give the

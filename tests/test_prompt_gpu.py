@@ -70,6 +70,20 @@ def test_prompt_cases(name):
         assert np.all(out == 0) and np.all(np.isneginf(lse))
 
 
+def test_prompt_wide_scale_range():
+    """K and V scales spread over 2^16 per cell (see the decode test)."""
+    say("case: prompt, scales over 2^16")
+    x = gen.make_prompt(None, seed=15, n_q=50, pool_cells=2048)
+    rng = np.random.default_rng(16)
+    def spread(bits):
+        v = bits.view(np.float16).astype(np.float32)
+        return (v * np.exp2(rng.uniform(-8, 8, v.shape)).astype(np.float32)).astype(
+            np.float16).view(np.uint16)
+    x = dataclasses.replace(x, k_scales=spread(x.k_scales), v_scales=spread(x.v_scales))
+    out, lse = run_prompt(x)
+    check(x, out, lse, "prompt wide scales")
+
+
 def test_prompt_interleaved_scales():
     say("case: prompt, interleaved (K, V) scale pairs")
     x = gen.make_prompt(None, seed=12, n_q=21, pool_cells=1024)
