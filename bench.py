@@ -22,7 +22,9 @@ workloads (256 x 2,051 cells x 4 q, 64 x 16,384 x 2 q, 32 x 131,072 x 4 q)
 measured the same way with a cache flush between calls; the two passes are
 also timed as separate calls for reference; "prompt_attention" = the prompt
 workload of the same pages (32K-cell INT8 context, 2,048 causal queries x 12
-heads) through sda_prompt_attn_batch, with its matrix-core roofline.
+heads) through sda_prompt_attn_batch, with its matrix-core roofline;
+"kv_append" = the INT8 KV append of 64 x 2,048 new rows into 32K-cell pools
+through sda_kv_append_batch, cold, with its HBM roofline.
 """
 from __future__ import annotations
 
@@ -373,6 +375,72 @@ def prompt_section(reps, cpu_seconds):
     return d
 
 
+def append_bytes(x) -> int:
+    """Algorithmic bytes of one KV append: per new row the K and V values
+    read (2 x 256 x 4 B) and the codes and scales written (2 x (256 + 2) B);
+    4 B per touched page-table entry and per instance's pos0."""
+    pages = 0
+    for i in range(x.n_inst):
+        c = int(x.pos0[i]) + np.arange(x.n_new)
+        c = c[(c >= 0) & (c < x.page_table.shape[1] * 16)]
+        pages += int(np.unique(c >> 4).size)
+    return x.n_inst * x.n_new * (2 * 256 * 4 + 2 * 258) + pages * 4 + x.n_inst * 4
+
+
+def append_case():
+    import torch
+    from decode_attention_sparse_amd import api, inputs
+    x = inputs.make_append("kv_append_64inst_2048rows")
+    cells = x.n_inst * x.pool_cells
+    pool = api.Pool(torch.zeros((cells, 256), dtype=torch.int8, device="cuda"), None,
+                    torch.zeros((cells, 256), dtype=torch.int8, device="cuda"), None,
+                    scales=torch.zeros((cells, 2), dtype=torch.int16, device="cuda"))
+    t = lambda a: torch.from_numpy(a).cuda()
+    pt, pos0, kn, vn = t(x.page_table), t(x.pos0), t(x.k_new), t(x.v_new)
+
+    def call():
+        api.kv_append_batch(pool, pt, pos0, kn, vn)
+    return x, call
+
+
+def append_section(iters, flush):
+    """The KV append workload: eager calls, caches evicted before each by the
+    read flush, HIP events around the call on the launch stream."""
+    import torch
+    x, call = append_case()
+    for _ in range(3):
+        call()
+    evs = []
+    for _ in range(iters):
+        flush()
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        call()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    med = float(np.median(us))
+    nbytes = append_bytes(x)
+    gbs = nbytes / (med * 1e-6) / 1e9
+    return {
+        "workload": x.workload,
+        "config": {"instances": x.n_inst, "new_rows_per_instance": x.n_new,
+                   "pool_cells_per_instance": x.pool_cells, "pos0": int(x.pos0[0]),
+                   "rows": "float32 K and V rows, N(0, 1) x 2^U(-8, 8) per row",
+                   "pool_layout": "int8 code rows; binary16 (K, V) scale pairs interleaved per cell"},
+        "us_per_call_median": round(med, 3),
+        "us_per_call_p10": round(float(np.percentile(us, 10)), 3),
+        "us_per_call_p90": round(float(np.percentile(us, 90)), 3),
+        "rows_per_s": round(x.n_inst * x.n_new / (med * 1e-6), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kv_append_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "launch_us_median": round(med, 3)},
+        "timing": f"{iters} eager calls, caches evicted before each by reading a 1 GiB buffer",
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +461,9 @@ def main(argv=None):
                     help="skip the prompt attention workload")
     ap.add_argument("--only-prompt", action="store_true",
                     help="only three eager prompt attention calls (for profiling)")
+    ap.add_argument("--no-append", action="store_true", help="skip the KV append workload")
+    ap.add_argument("--only-append", action="store_true",
+                    help="only three eager KV append calls (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -403,7 +474,8 @@ def main(argv=None):
         return 2
     # measured read ceilings for the access shapes of the chunk pass; run as a
     # child process before this process touches the GPU
-    ceiling = None if (a.no_ceiling or a.only_batched or a.only_prompt) else gather_ceiling()
+    ceiling = (None if (a.no_ceiling or a.only_batched or a.only_prompt or a.only_append)
+               else gather_ceiling())
     import torch
     from decode_attention_sparse_amd import api, inputs
     api.library()
@@ -416,6 +488,14 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if a.only_append:
+        x, call = append_case()
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": x.workload, "calls": 3}), flush=True)
+        return 0
 
     if a.only_prompt:
         x, call = prompt_case()
@@ -574,6 +654,14 @@ def main(argv=None):
         print(f"# {d['workload']}: {d['ms_per_call']} ms/call, {d['roofline']['achieved']} "
               f"TFLOP/s ({d['roofline']['frac']*100:.1f}% of the int8 matrix peak)",
               file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    # ---- INT8 KV append into the same pool layout
+    if not a.no_append:
+        d = append_section(a.batched_iters, flush)
+        result["kv_append"] = d
+        print(f"# {d['workload']}: {d['us_per_call_median']} us/call, {d['roofline']['achieved']} "
+              f"GB/s ({d['roofline']['frac']*100:.1f}% of HBM peak)", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     if not a.no_cpu:
