@@ -50,8 +50,8 @@ PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary with the commands is in
 # profiles/chunk_mfma_kernel__hbm_bytes__pages_point_and_batched.md.  The
 # figures hold only for the kernel source they were taken on.
-CHUNK_TRAFFIC = {"sources_sha256": "da767aa833d07134a8d6d50a6b24194c75c273c113fb4f54841c0fe2e43b8f6c",
-                 "fetch_bytes": 1_972_254, "write_bytes": 1_634_688}
+CHUNK_TRAFFIC = {"sources_sha256": "02c192545447183a3a5bb876832aa1b9fafe78ede0bb8a73e2da1b39a051899d",
+                 "fetch_bytes": 1_972_326, "write_bytes": 1_634_688}
 TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                    "decode_attention_sparse_amd/csrc/sda_internal.h",
                    "decode_attention_sparse_amd/csrc/sda_api.hip")
