@@ -160,7 +160,8 @@ def partials(ws: torch.Tensor, n_inst, n_q, n_qheads, max_sel, chunk_cells):
 
 def decode_attn_step(pool: Pool, page_table, sel, q, softmax_scale: float, chunk_cells: int,
                      out, lse, gather_out=None, ws=None, stream=None, n_sel: int | None = None):
-    """One sequence: q [n_q][n_qheads][256] fp32; out like q; lse [n_q][n_qheads]."""
+    """One sequence: q [n_q][n_qheads][256] fp32; out like q; lse [n_q][n_qheads].
+    Chunks of fused_chunk_cells(1, n_sel, chunk_cells) cells, as the batch call."""
     n_q, n_qheads = int(q.shape[0]), int(q.shape[1])
     n = int(sel.numel()) if n_sel is None else int(n_sel)
     if ws is None:
@@ -179,7 +180,9 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
                       chunk_cells: int, out, lse, gather_out=None, ws=None, stream=None,
                       n_logical_pages: int | None = None):
     """Many instances: page_table [n_inst][pt_stride], sel [n_inst][sel_stride],
-    n_sel device int32 [n_inst], q [n_inst][n_q][n_qheads][256]."""
+    n_sel device int32 [n_inst], q [n_inst][n_q][n_qheads][256].  The call
+    runs chunks of fused_chunk_cells(n_inst, max_sel, chunk_cells) cells; the
+    workspace then holds those partials (partials(..., that chunk size))."""
     n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     if ws is None:
         ws = workspace(n_inst, n_q, n_qheads, max_sel, chunk_cells, q.device)
@@ -197,7 +200,7 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
 
 def chunk_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softmax_scale: float,
                 chunk_cells: int, ws, gather_out=None, stream=None):
-    """Chunk pass only: partials into ws (see partials())."""
+    """Chunk pass only, at exactly chunk_cells: partials into ws (see partials())."""
     n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     ps = pool.c_struct()
     st = library().sda_chunk_batch(

@@ -6,12 +6,13 @@
 // denominators are the partials; the softmax merge order is fixed).
 //
 // Lane l owns head dimensions [4l, 4l + 4): one 16-byte load per chunk and
-// lane, a 1 KB coalesced row per wave.  Rows with many chunks are split over
-// the four waves of a workgroup, rows with few get one wave each (see
-// merge_kernel).  The first batch of accumulator rows is requested before
-// the maximum over the chunk maxima is known, so a short merge costs one
-// round trip to memory.  Wave sums are added in a fixed order through LDS,
-// which keeps the result deterministic.
+// lane, a 1 KB coalesced row per wave.  Rows with at most four chunks are
+// merged four rows per wave with every load in flight (merge_few_kernel);
+// rows with up to eight get one wave each and rows with more are split over
+// the four waves of a workgroup (merge_kernel).  The first batch of
+// accumulator rows is requested before the maximum over the chunk maxima is
+// known, so a short merge costs one round trip to memory.  Wave sums are
+// added in a fixed order through LDS, which keeps the result deterministic.
 #include "sda_internal.h"
 
 namespace sda {
