@@ -214,6 +214,28 @@ def test_batch_size_independence(n_q):
     check(huge, o4, l4, g4, inst_ids=[0, 19, 77, 119], what="fused call, batch of 120")
 
 
+def test_many_instances_coarse_chunks():
+    """More than 256 instances and 512 (instance, chunk) pairs: the fused
+    call takes chunks k times the caller's (300 x 600 cells at chunk 64:
+    3,000 pairs, k = 5, 320-cell chunks).  Against the oracle on sampled
+    instances, and bit for bit against the two passes at that chunk size."""
+    from decode_attention_sparse_amd import api
+    say("case: 300 instances, coarse fused chunks")
+    x = gen.make(None, seed=61, n_inst=300, n_q=2, pool_cells=1024, n_sel=600, sel="uniform",
+                 chunk=64)
+    rng = np.random.default_rng(62)
+    counts = rng.integers(0, 601, size=300).astype(np.int32)
+    counts[[0, 1, 2]] = [600, 0, 321]
+    x = dataclasses.replace(x, n_sel=counts)
+    fc = api.fused_chunk_cells(300, 600, 64)
+    assert fc == 320
+    out, lse, g, _ = run_batch(x)
+    ids = [0, 1, 2, 150, 299]
+    check(x, out, lse, g, inst_ids=ids, what="coarse fused chunks")
+    o2, l2, g2, _ = two_pass(x, fc)
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2) and np.array_equal(g, g2)
+
+
 def test_several_chunks_per_workgroup():
     """A grid of 1,600 chunks, so that each workgroup streams several
     consecutive chunks of one instance; ragged per-instance counts put chunk
