@@ -107,6 +107,8 @@ class Case:
         self.lse = torch.empty((n_inst, n_q, nh), device="cuda")
         self.ws = api.workspace(n_inst, n_q, nh, self.max_sel, chunk)
         self.fused_chunk = api.fused_chunk_cells(n_inst, self.max_sel, chunk)
+        # whether the call is one chunk-kernel launch that writes the outputs
+        self.single_launch = api.fused_single_launch(n_inst, n_q, nh, self.max_sel, chunk)
         self.chunk_bytes = algorithmic_bytes(x)  # the chunk kernel's
         self.bytes = self.chunk_bytes + out_bytes(x)  # one whole call
         self.cells = int(np.sum(x.n_sel))
@@ -635,10 +637,18 @@ def main(argv=None):
             time_calls([c], 3)
             d = summarize(c, time_calls([c], a.batched_iters, flush=flush)[0],
                           time_passes([c], a.batched_iters, flush=flush)[0])
+            nch = -(-int(x.sel.shape[1]) // c.fused_chunk)
             d.update({"instances": x.n_inst, "n_q": x.n_q, "selected_cells_per_instance":
-                      int(x.sel.shape[1]), "chunk": x.chunk,
+                      int(x.sel.shape[1]), "chunk": x.chunk, "call_chunk_cells": c.fused_chunk,
+                      "call_launches": ("one chunk_mfma_kernel launch: " +
+                                        ("two gather pipelines per workgroup, " if nch == 2 else "")
+                                        + "outputs merged and written in place")
+                                       if c.single_launch else "chunk_mfma_kernel, then merge kernel",
+                      "two_pass_note": "chunk_us_mean / merge_us_mean: sda_chunk_batch and "
+                                       "sda_merge_batch at the call's chunk size, timed as "
+                                       "separate calls",
                       "bytes_algorithmic": c.bytes, "partials_bytes_written":
-                      int(x.n_inst * -(-x.sel.shape[1] // x.chunk) * x.n_q * 12 * 258 * 4)})
+                      0 if c.single_launch else int(x.n_inst * nch * x.n_q * 12 * 258 * 4)})
             batched[x.workload] = d
             print(f"# {x.workload}: {d['us_per_call_median']} us/call, "
                   f"{d['GBps_algorithmic']} GB/s ({d['frac_hbm_peak']*100:.1f}% of HBM peak)",

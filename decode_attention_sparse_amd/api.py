@@ -21,7 +21,7 @@ PROMPT_MAX_ROWS = 65535 * 48
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
             "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_fused_chunk_cells",
-            "sda_kv_append_batch", "sda_status_string")
+            "sda_fused_single_launch", "sda_kv_append_batch", "sda_status_string")
 
 
 class SdaError(RuntimeError):
@@ -68,6 +68,8 @@ def library() -> C.CDLL:
         lib.sda_kv_append_batch.restype = C.c_int
         lib.sda_fused_chunk_cells.argtypes = [i32, i32, i32, C.POINTER(i32)]
         lib.sda_fused_chunk_cells.restype = C.c_int
+        lib.sda_fused_single_launch.argtypes = [i32, i32, i32, i32, i32, C.POINTER(i32)]
+        lib.sda_fused_single_launch.restype = C.c_int
         lib.sda_status_string.argtypes = [C.c_int]
         lib.sda_status_string.restype = C.c_char_p
         _lib = lib
@@ -134,6 +136,18 @@ def fused_chunk_cells(n_inst: int, max_sel: int, chunk_cells: int) -> int:
     if st != SDA_OK:
         raise SdaError(st, "sda_fused_chunk_cells")
     return int(out.value)
+
+
+def fused_single_launch(n_inst: int, n_q: int, n_qheads: int, max_sel: int,
+                        chunk_cells: int) -> bool:
+    """Whether sda_decode_attn_step/_batch run this geometry as one chunk-kernel
+    launch that writes the outputs (the workspace is then left untouched)."""
+    out = C.c_int32(0)
+    st = library().sda_fused_single_launch(n_inst, n_q, n_qheads, max_sel, chunk_cells,
+                                           C.byref(out))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_fused_single_launch")
+    return bool(out.value)
 
 
 def workspace(n_inst, n_q, n_qheads, max_sel, chunk_cells, device="cuda") -> torch.Tensor:

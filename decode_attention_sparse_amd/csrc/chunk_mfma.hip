@@ -196,6 +196,17 @@ struct RowBlock {
         for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
 
+    // Moves this lane's LDS offsets to another pipeline's buffers: code rows
+    // kv bytes on, scale and bias slots sc elements on.  (Not for the causal
+    // form, whose mask compares the slot offsets with cell indices.)
+    __device__ __forceinline__ void shift(int kv, int sc) {
+        k_off0 += kv;
+        k_off1 += kv;
+        v_off += kv;
+        m_off0 += sc;
+        m_off1 += sc;
+    }
+
     __device__ __forceinline__ void reset() {
         m_run = -INFINITY;
         l_part = 0.f;
@@ -329,6 +340,12 @@ struct RowBlock {
         }
     }
 
+    // The partial's maximum: the base-2 running maximum back in natural-log
+    // units.
+    __device__ __forceinline__ float m_nat() const {
+        return (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
+    }
+
     // The chunk partial of this lane's row at unit index base (instance,
     // chunk, row) of the workspace.  Every lane of the wave must call it.
     __device__ __forceinline__ void emit(const Params &p, int64_t base, int row, int g, int dh) {
@@ -338,8 +355,7 @@ struct RowBlock {
 #pragma unroll
             for (int db = 0; db < kDB; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
             if (g == 0 && dh == 0) {
-                // base-2 maximum back to natural-log units
-                p.m[base] = (m_run == -INFINITY) ? -INFINITY : m_run * 0.69314718055994531f;
+                p.m[base] = m_nat();
                 p.l[base] = l_row;
             }
         }
@@ -377,35 +393,69 @@ struct RowBlock {
 //
 // kPrompt = false: decode.  Workgroup (blockIdx.x, blockIdx.y) = instance i,
 // chunks [cpw * y, cpw * y + cpw) of its list; emits chunk partials.
+// kFinal (decode calls whose every instance has at most SP chunks): the
+// workgroup runs all of instance i's chunks, SP = 2 pipelines side by side
+// (pipeline h: chunk h, its own producer wave, compute waves and LDS), and
+// writes the head outputs itself: the partials are merged in LDS with the
+// merge pass's arithmetic (merge_weight, merge_acc), so the result is the
+// two passes' bit for bit, without the partials' round trip through memory
+// or a second launch.
 // kPrompt = true: prompt attention.  Workgroup (i, y) = the 16 RB query rows
 // starting at row 16 RB y of instance i (rows are position-major, so a
 // workgroup holds a few consecutive positions); the cell list is implicit
 // (logical cells 0, 1, 2, ... up to the workgroup's last position), each
 // row masks the cells past its own position, and the rows are normalised in
 // place of a partial (one chunk spans the whole causal range).
-template <int RB, int DS, bool kPrompt>
-__global__ __launch_bounds__(64 * (DS * RB + 1))
+template <int RB, int DS, bool kPrompt, int SP = 1, bool kFinal = false>
+__global__ __launch_bounds__(64 * SP * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu((RB == 1 || DS > 1) ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p, int cpw) {
-    constexpr int kProducer = DS * RB;  // the last wave
+    static_assert(SP == 1 || (SP == 2 && kFinal && DS == 1 && RB >= 2 && RB <= 3),
+                  "two pipelines: final decode output, 2 or 3 row groups");
+    static_assert(!(kPrompt && kFinal), "the prompt form always writes its rows");
+    static_assert(SP == 1 || RB * 8 * 64 * 16 <= 2 * kBuf,
+                  "the hand-over fits a pipeline's K (and V) buffers");
+    constexpr int kPipe = DS * RB + 1;  // waves per pipeline
+    constexpr int kProducer = DS * RB;  // a pipeline's last wave
     constexpr int kDB = 16 / DS;        // 16-dim blocks of O^T per compute wave
-    __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kBuf];
-    __shared__ __attribute__((aligned(1024))) int8_t vbuf[2][kBuf];
+    __shared__ __attribute__((aligned(1024))) int8_t kbuf_p[SP][2][kBuf];
+    __shared__ __attribute__((aligned(1024))) int8_t vbuf_p[SP][2][kBuf];
     // physical cell of tile cell 16k + r at [slot][4r + k]
-    __shared__ __attribute__((aligned(16))) int phys_s[4][kTile];
-    __shared__ __attribute__((aligned(16))) float ks_s[4][kTile];
-    __shared__ __attribute__((aligned(16))) float vs_s[4][kTile];
-    __shared__ __attribute__((aligned(16))) float bias_s[4][kTile];
+    __shared__ __attribute__((aligned(16))) int phys_p[SP][4][kTile];
+    __shared__ __attribute__((aligned(16))) float ks_p[SP][4][kTile];
+    __shared__ __attribute__((aligned(16))) float vs_p[SP][4][kTile];
+    __shared__ __attribute__((aligned(16))) float bias_p[SP][4][kTile];
 
-    const int wave = threadIdx.x >> 6;
+    // wave index: uniform, so that the role and pipeline branches are scalar
+    const int wv = SP == 1 ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pipe = SP == 1 ? 0 : wv / kPipe;
+    const int wave = wv - pipe * kPipe;  // within the pipeline
     const int lane = threadIdx.x & 63;
+    int8_t (&kbuf)[2][kBuf] = kbuf_p[pipe];
+    int8_t (&vbuf)[2][kBuf] = vbuf_p[pipe];
+    int (&phys_s)[4][kTile] = phys_p[pipe];
+    float (&ks_s)[4][kTile] = ks_p[pipe];
+    float (&vs_s)[4][kTile] = vs_p[pipe];
+    float (&bias_s)[4][kTile] = bias_p[pipe];
     const int g = lane >> 4;    // lane group: k-set of the MFMA operands
     const int l16 = lane & 15;  // this lane's row within the wave's 16 rows
     const int i = blockIdx.x;   // instance (fastest: full chunks are dispatched first)
     const int R = p.n_rows;
     int c0 = 0, j_begin = 0, j_end, tpc, row0 = 0;
+    int n_iter = 0;  // pipeline steps (the tile count of the longest pipeline)
     int64_t pos0 = 0;
-    if constexpr (!kPrompt) {
+    if constexpr (kFinal) {
+        // pipeline h runs chunk h (cells [h C, h C + C) clipped to the count);
+        // an instance with fewer chunks leaves a pipeline with no tiles, which
+        // still takes every step (no early exit: the workgroup shares its
+        // barriers) and contributes nothing
+        const int n = count_of(p, i);
+        c0 = pipe;
+        j_begin = pipe * p.chunk;
+        j_end = max(j_begin, min(j_begin + p.chunk, n));
+        tpc = 1 << 30;
+        n_iter = (min(p.chunk, n) + kTile - 1) / kTile;  // pipeline 0's
+    } else if constexpr (!kPrompt) {
         // This workgroup runs chunks [c0, c0 + cpw) of instance i as one
         // stream of tiles: the gather pipeline runs on across chunk
         // boundaries, and the compute waves emit a partial at the end of
@@ -427,16 +477,20 @@ void chunk_mfma_kernel(Params p, int cpw) {
         tpc = 1 << 30;  // one chunk: no partial inside the loop
     }
     const int n_tiles = (j_end - j_begin + kTile - 1) / kTile;
+    if constexpr (!kFinal) n_iter = n_tiles;
+    // the last list entry, the target of the clamped list loads (a pipeline
+    // with no tiles reads a valid entry: a final-output call has max_sel > 0)
+    const int j_last = kFinal ? max(j_end - 1, 0) : j_end - 1;
 
     // scale slots read before their first write hold finite values
-    for (int e = threadIdx.x; e < 4 * kTile; e += 64 * (DS * RB + 1)) {
-        (&ks_s[0][0])[e] = 0.f;
-        (&vs_s[0][0])[e] = 0.f;
-        (&bias_s[0][0])[e] = -INFINITY;
+    for (int e = threadIdx.x; e < SP * 4 * kTile; e += 64 * SP * kPipe) {
+        (&ks_p[0][0][0])[e] = 0.f;
+        (&vs_p[0][0][0])[e] = 0.f;
+        (&bias_p[0][0][0])[e] = -INFINITY;
     }
     __syncthreads();
 
-    // Both roles run n_tiles + 4 iterations with one barrier each.  Iteration
+    // Both roles run n_iter + 4 iterations with one barrier each.  Iteration
     // t: the producer loads the selected ids of tile t+4, the page-table
     // entries of tile t+3, the scales and K rows of tile t+2 and the V rows of
     // tile t+1 and writes them to LDS; the compute waves score tile t+1 and
@@ -449,7 +503,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
         const int32_t *pt_or_sel = p.n_logical_pages > 0 ? pt : sel;
         int sel3 = -1;  // selected id of tile t+3 (this lane's cell)
         int ph2 = -1;   // physical cell of tile t+2
-        for (int t = -4; t < n_tiles; ++t) {
+        for (int t = -4; t < n_iter; ++t) {
             const bool ld_k = (t + 2 >= 0) && (t + 2 < n_tiles);
             const bool ld_v = (t + 1 >= 0) && (t + 1 < n_tiles);
             // gather loads: unconditional, from clamped (always valid) addresses,
@@ -463,7 +517,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
             const unsigned kh2 = p.k_scales[sc2];
             const unsigned vh2 = p.v_scales[sc2];
             const int pte3 = pt_or_sel[id_ok ? lp3 : 0];
-            const int sel4 = kPrompt ? j4 : sel[j4 < j_end ? j4 : j_end - 1];
+            const int sel4 = kPrompt ? j4 : sel[j4 < j_end ? j4 : j_last];
             // then the code rows: load (k, c) covers rows 16k + l16, bytes
             // 64c + 16g, so each lane needs the physical cells of 4 rows only
             // (one 16-byte LDS read) and every load uses an immediate offset
@@ -526,6 +580,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
             sel3 = (ld_s && j4 < j_end) ? sel4 : -1;
             __syncthreads();
         }
+        if constexpr (SP > 1) __syncthreads();  // the compute waves' hand-over
         return;
     }
 
@@ -536,9 +591,12 @@ void chunk_mfma_kernel(Params p, int cpw) {
     const int64_t grow = (int64_t)i * R + row0 + row;  // row in [n_inst][n_rows]
     const bool row_ok = row0 + row < R;
     rb.init(p.q + (row_ok ? grow : (int64_t)i * R + row0) * kDim, row_ok, p.scale_log2, g, l16);
+    // the steps below address pipeline 0's buffers; the lane offsets carry
+    // the pipeline (one add here instead of a base register per buffer)
+    if constexpr (SP > 1) rb.shift(pipe * 2 * kBuf, pipe * 4 * kTile);
     // prompt: this row's last visible cell (its position)
     const int64_t lim_row = kPrompt ? pos0 + (row0 + row) / p.n_qheads : 0;
-    for (int t = -4; t < n_tiles; ++t) {
+    for (int t = -4; t < n_iter; ++t) {
         if (t >= -1) {
             // Both halves of a step run every iteration (no validity branches,
             // so the scheduler can interleave them); a tile outside
@@ -552,10 +610,11 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 rb.template step<true>(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0],
                                        dh, (int)max((int64_t)-1, min(lim, (int64_t)kTile)));
             } else {
-                rb.step(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0], dh);
+                rb.step(kbuf_p[0][b1], ks_p[0][m1], bias_p[0][m1], next_ok, vbuf_p[0][b0],
+                        vs_p[0][m0], dh);
             }
             // end of a chunk: emit its partial, start afresh
-            if (!kPrompt && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
+            if (!kPrompt && !kFinal && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
                 rb.emit(p, ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row, row, g, dh);
                 rb.reset();
             }
@@ -564,6 +623,70 @@ void chunk_mfma_kernel(Params p, int cpw) {
     }
     if constexpr (kPrompt)
         rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
+    if constexpr (kFinal) {
+        // each pipeline's partial as the chunk pass would emit it: acc = o *
+        // frame, m = m_nat(), l = the row sum
+        const float l_row = sum4(rb.l_part);
+        const float m_row = rb.m_nat();
+        // pipeline 1 hands its partial over through its own staging buffers,
+        // idle since the last step's barrier: wave w's accumulator block db
+        // at [w][db % 8][lane] of its K buffers (db < 8) or V buffers (8 KB
+        // per wave in each), m and l by row in its scale slots
+        auto xslot = [&](int db) {
+            float *base = reinterpret_cast<float *>(db < kDB / 2 ? &kbuf_p[SP - 1][0][0]
+                                                                 : &vbuf_p[SP - 1][0][0]);
+            return reinterpret_cast<v4f *>(base) + (wave * (kDB / 2) + db % (kDB / 2)) * 64 + lane;
+        };
+        float *xm = &ks_p[SP - 1][0][0];
+        float *xl = &vs_p[SP - 1][0][0];
+        if constexpr (SP > 1) {
+            if (pipe == 1) {
+#pragma unroll
+                for (int db = 0; db < kDB; ++db) *xslot(db) = rb.o[db] * rb.frame;
+                if (g == 0) {
+                    xm[row] = m_row;
+                    xl[row] = l_row;
+                }
+            }
+            __syncthreads();
+            if (pipe == 1) return;
+        }
+        if (!row_ok) return;
+        // the merge of the instance's nch partials, chunk by chunk
+        const int nch = (count_of(p, i) + p.chunk - 1) / p.chunk;  // at most SP
+        float mc[SP], lc[SP];
+        mc[0] = m_row;
+        lc[0] = l_row;
+        if constexpr (SP > 1) {
+            mc[1] = xm[row];
+            lc[1] = xl[row];
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < SP; ++c)
+            if (c < nch) M = fmaxf(M, mc[c]);
+        float L = 0.f, w[SP];
+#pragma unroll
+        for (int c = 0; c < SP; ++c) {
+            w[c] = 0.f;
+            if (c < nch) {
+                w[c] = merge_weight(mc[c], M);
+                L = fmaf(lc[c], w[c], L);
+            }
+        }
+        float *dst = p.out + grow * kDim + 16 * kDB * dh + 4 * g;
+        const bool any = L > 0.f;
+        const float inv = any ? 1.f / L : 0.f;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+            v4f o = (v4f){0.f, 0.f, 0.f, 0.f};
+            if (0 < nch) o = merge_acc(o, w[0], rb.o[db] * rb.frame);
+            if constexpr (SP > 1)
+                if (1 < nch) o = merge_acc(o, w[1], *xslot(db));
+            *reinterpret_cast<v4f *>(dst + 16 * db) = any ? o * inv : (v4f){0.f, 0.f, 0.f, 0.f};
+        }
+        if (g == 0 && dh == 0) p.lse[grow] = any ? M + logf(L) : -INFINITY;
+    }
 }
 
 constexpr int kPtLdsPages = 2048;  // page tables up to this size are staged whole (8 KB)
@@ -751,6 +874,42 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
         launch_rb<2>(p, grid, cpw, s);
     else
         launch_rb<1>(p, grid, cpw, s);
+    return hipGetLastError();
+}
+
+bool chunk_writes_output(const Params &p) {
+    // multi-tile chunks only: one-tile chunks take the single-tile kernel
+    if (p.n_chunks < 1 || p.n_chunks > 2 || p.chunk <= kTile) return false;
+    // Two pipelines: 2 or 3 row groups (more do not fit two waves per SIMD).
+    // With one row group the pair measured no faster than two workgroups and
+    // the merge launch: the shared barrier makes each step wait for the
+    // slower of two gathers, which costs about what the merge saves.
+    return p.n_chunks == 1 || (p.n_rows > 16 && p.n_rows <= 48);
+}
+
+hipError_t launch_chunk_final(const Params &p, hipStream_t s) {
+    const dim3 grid(p.n_inst, 1);
+    const int rb = (p.n_rows + 15) / 16;
+    if (p.n_chunks == 2) {
+        // two pipelines of RB + 1 waves, one workgroup per CU (LDS)
+        switch (rb) {
+            case 2: chunk_mfma_kernel<2, 1, false, 2, true><<<grid, 64 * 6, 0, s>>>(p, 1); break;
+            default: chunk_mfma_kernel<3, 1, false, 2, true><<<grid, 64 * 8, 0, s>>>(p, 1); break;
+        }
+    } else if (p.n_inst <= kLatencyWorkgroups && p.n_rows <= 32) {
+        // the launch shapes of launch_chunk for the same grid
+        switch (rb) {
+            case 1: chunk_mfma_kernel<1, 2, false, 1, true><<<grid, 64 * 3, 0, s>>>(p, 1); break;
+            default: chunk_mfma_kernel<2, 2, false, 1, true><<<grid, 64 * 5, 0, s>>>(p, 1); break;
+        }
+    } else {
+        switch (rb) {
+            case 1: chunk_mfma_kernel<1, 1, false, 1, true><<<grid, 64 * 2, 0, s>>>(p, 1); break;
+            case 2: chunk_mfma_kernel<2, 1, false, 1, true><<<grid, 64 * 3, 0, s>>>(p, 1); break;
+            case 3: chunk_mfma_kernel<3, 1, false, 1, true><<<grid, 64 * 4, 0, s>>>(p, 1); break;
+            default: chunk_mfma_kernel<4, 1, false, 1, true><<<grid, 64 * 5, 0, s>>>(p, 1); break;
+        }
+    }
     return hipGetLastError();
 }
 

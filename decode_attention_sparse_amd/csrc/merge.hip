@@ -75,9 +75,9 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p) {
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 // a chunk with no unmasked cell (m = -inf) has weight 0
-                const float w = mc[k] == -INFINITY ? 0.f : expf(mc[k] - M);
+                const float w = merge_weight(mc[k], M);
                 L = fmaf(lc[k], w, L);
-                o += w * a[k];
+                o = merge_acc(o, w, a[k]);
             }
             c0 += KW * kBatch;
             if (c0 >= nch) break;
@@ -151,9 +151,9 @@ __global__ __launch_bounds__(256) void merge_few_kernel(Params p) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             if (c < nch) {
-                const float w = mc[q][c] == -INFINITY ? 0.f : expf(mc[q][c] - M);
+                const float w = merge_weight(mc[q][c], M);
                 L = fmaf(lc[q][c], w, L);
-                o += w * a[q][c];
+                o = merge_acc(o, w, a[q][c]);
             }
         }
         const int64_t u = (int64_t)i * R + r0 + q;

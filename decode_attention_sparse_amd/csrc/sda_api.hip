@@ -171,6 +171,8 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so it is not blamed on us
+    if (passes == kBoth && sda::chunk_writes_output(p))
+        return sda::launch_chunk_final(p, s) == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
     if ((passes & kChunk) && p.n_chunks > 0 && sda::launch_chunk(p, s) != hipSuccess)
         return SDA_ERR_LAUNCH;
     if ((passes & kMerge) && sda::launch_merge(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
@@ -200,6 +202,22 @@ int sda_fused_chunk_cells(int32_t n_inst, int32_t max_sel, int32_t chunk_cells,
         return SDA_ERR_INVALID_ARG;
     if (chunk_cells % SDA_CHUNK_ALIGN) return SDA_ERR_UNSUPPORTED;
     *fused_chunk_cells = fused_chunk_of(n_inst, max_sel, chunk_cells);
+    return SDA_OK;
+}
+
+int sda_fused_single_launch(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t max_sel,
+                            int32_t chunk_cells, int32_t *single_launch) {
+    if (!single_launch || n_inst < 0 || max_sel < 0 || chunk_cells < 1 || n_q < 1 ||
+        n_qheads < 1 || (int64_t)n_q * n_qheads > SDA_MAX_ROWS)
+        return SDA_ERR_INVALID_ARG;
+    if (chunk_cells % SDA_CHUNK_ALIGN) return SDA_ERR_UNSUPPORTED;
+    sda::Params p;
+    memset(&p, 0, sizeof p);
+    p.n_inst = n_inst;
+    p.n_rows = n_q * n_qheads;
+    p.chunk = fused_chunk_of(n_inst, max_sel, chunk_cells);
+    p.n_chunks = (int32_t)(((int64_t)max_sel + p.chunk - 1) / p.chunk);
+    *single_launch = sda::chunk_writes_output(p) ? 1 : 0;
     return SDA_OK;
 }
 

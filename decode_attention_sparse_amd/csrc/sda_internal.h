@@ -53,6 +53,24 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// The log-sum-exp merge of a row's chunk partials (m_c, l_c, acc_c), as every
+// merge in the library runs it, chunk by chunk in chunk order:
+//   M = max_c m_c (from -inf),  w_c = e^(m_c - M) (0 for an empty chunk),
+//   L = fma(l_c, w_c, L),  o = fma(w_c, acc_c, o) element by element (from 0),
+//   out = o * (1 / L),  lse = M + ln L  (L = 0: out = 0, lse = -inf).
+// The explicit fmas fix the rounding, so the merge kernels and the chunk
+// kernel's in-place merge give the same bits.
+__device__ __forceinline__ float merge_weight(float mc, float M) {
+    return mc == -INFINITY ? 0.f : expf(mc - M);
+}
+
+typedef float merge_v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ merge_v4f merge_acc(merge_v4f o, float w, merge_v4f a) {
+    return (merge_v4f){__builtin_fmaf(w, a[0], o[0]), __builtin_fmaf(w, a[1], o[1]),
+                       __builtin_fmaf(w, a[2], o[2]), __builtin_fmaf(w, a[3], o[3])};
+}
+
 // Number of selected entries instance i actually uses.
 __device__ __forceinline__ int count_of(const Params &p, int i) {
     int n = p.n_sel_dev ? p.n_sel_dev[i] : p.n_sel_host;
@@ -79,6 +97,11 @@ struct AppendParams {
 };
 
 hipError_t launch_chunk(const Params &p, hipStream_t s);
+// Whether a call with both passes runs as one chunk-kernel launch that writes
+// the head outputs (every instance has at most two multi-tile chunks), and
+// that launch.  The workspace is not touched.
+bool chunk_writes_output(const Params &p);
+hipError_t launch_chunk_final(const Params &p, hipStream_t s);
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t s);
 hipError_t launch_merge(const Params &p, hipStream_t s);
 hipError_t launch_prompt(const Params &p, hipStream_t s);

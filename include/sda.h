@@ -109,7 +109,9 @@ typedef struct sda_pool {
  * hold the chunk partials of the chunks that instance actually has
  * (c < ceil(n_sel[i] / C)); other entries are unspecified.  C is
  * chunk_cells after sda_chunk_batch, and sda_fused_chunk_cells(...) after
- * sda_decode_attn_step / sda_decode_attn_batch.
+ * sda_decode_attn_step / sda_decode_attn_batch, except after a fused call
+ * that runs as a single launch (sda_fused_single_launch), which does not
+ * touch the workspace.
  * Returns SDA_OK, SDA_ERR_INVALID_ARG or SDA_ERR_UNSUPPORTED. */
 int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t head_dim,
                         int32_t max_sel, int32_t chunk_cells, size_t *bytes);
@@ -133,6 +135,20 @@ int sda_workspace_bytes(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t h
  * SDA_ERR_UNSUPPORTED (chunk_cells not a multiple of SDA_CHUNK_ALIGN). */
 int sda_fused_chunk_cells(int32_t n_inst, int32_t max_sel, int32_t chunk_cells,
                           int32_t *fused_chunk_cells);
+
+/* Whether a fused call (sda_decode_attn_step / _batch) of this geometry runs
+ * as a single chunk-kernel launch that merges in place and writes out and
+ * lse itself, leaving the workspace untouched (host only).  That is the case
+ * when C = sda_fused_chunk_cells(n_inst, max_sel, chunk_cells) exceeds
+ * SDA_CHUNK_ALIGN and ceil(max_sel / C) is 1, or 2 with 16 < n_q * n_qheads
+ * <= 48 (one workgroup runs both chunks of an instance, one gather pipeline
+ * each); otherwise the call launches the chunk pass and the merge pass.
+ *   single_launch (host out): 1 or 0
+ * Returns SDA_OK, SDA_ERR_INVALID_ARG (negative sizes, rows outside
+ * [1, SDA_MAX_ROWS], null output) or SDA_ERR_UNSUPPORTED (chunk_cells not a
+ * multiple of SDA_CHUNK_ALIGN). */
+int sda_fused_single_launch(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t max_sel,
+                            int32_t chunk_cells, int32_t *single_launch);
 
 /* One sequence (one KV head), the pages' single-step entry point.
  *   pool          host pointer to the pool descriptor
@@ -198,8 +214,9 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
  *
  * Running sda_chunk_batch then sda_merge_batch on one stream with chunk size
  * sda_fused_chunk_cells(n_inst, max_sel, chunk_cells) gives exactly the
- * result (and workspace partials) of sda_decode_attn_batch with chunk_cells;
- * with chunk_cells itself the result agrees up to rounding. */
+ * result of sda_decode_attn_batch with chunk_cells (and its workspace
+ * partials, where that call writes them); with chunk_cells itself the result
+ * agrees up to rounding. */
 int sda_chunk_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
                     int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
                     int64_t sel_stride, const int32_t *n_sel, int32_t max_sel, const float *q,

@@ -52,6 +52,39 @@ def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda", interleave=Fa
     return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)
 
 
+def check(x, out, lse, g=None, inst_ids=None, what=""):
+    """The outputs (and gather indices) of a decode call against the oracle,
+    on all instances or the sampled inst_ids."""
+    import oracle
+    ro, rl = oracle.attend(x, inst_ids)
+    sl = slice(None) if inst_ids is None else np.asarray(inst_ids)
+    e1 = assert_close(out[sl], ro, OUT_ATOL, OUT_RTOL, f"{what} out")
+    e2 = assert_close(lse[sl], rl, LSE_ATOL, LSE_RTOL, f"{what} lse")
+    if g is not None:
+        rg = oracle.gather(x)
+        valid = np.arange(x.sel.shape[1])[None, :] < x.n_sel[:, None]
+        assert np.array_equal(g[valid], rg[valid]), f"{what}: gather indices differ"
+    say(f"  {what}: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
+
+
+def two_pass(x, chunk, gather=True):
+    """sda_chunk_batch then sda_merge_batch at the given chunk size."""
+    import torch
+    from decode_attention_sparse_amd import api
+    n_inst, n_q, nh, D = x.q.shape
+    max_sel = int(x.sel.shape[1])
+    pool, dev = api.to_device(x)
+    ws = api.workspace(n_inst, n_q, nh, max_sel, chunk)
+    out = torch.full((n_inst, n_q, nh, D), float("nan"), device="cuda")
+    lse = torch.full((n_inst, n_q, nh), float("nan"), device="cuda")
+    g = torch.full(x.sel.shape, -7, dtype=torch.int32, device="cuda") if gather else None
+    api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
+                    x.softmax_scale, chunk, ws, gather_out=g)
+    api.merge_batch(dev["n_sel"], max_sel, chunk, ws, out, lse)
+    torch.cuda.synchronize()
+    return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)
+
+
 def run_prompt(x, device="cuda", interleave=False):
     """Upload prompt inputs and run sda_prompt_attn_batch; returns numpy out
     [n_inst][n_q][n_qheads][D] and lse [n_inst][n_q][n_qheads]."""

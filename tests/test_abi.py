@@ -105,6 +105,47 @@ def test_fused_chunk_cells_sweep():
     assert api.library().sda_fused_chunk_cells(1, 10, 64, None) == api.SDA_ERR_INVALID_ARG
 
 
+def single_launch(n_inst, n_q, nh, max_sel, chunk):
+    """The documented rule, restated: chunks of more than 64 cells, one per
+    instance, or two with 17 to 48 query rows."""
+    c = fused_chunk(n_inst, max_sel, chunk)
+    nch = -(-max_sel // c)
+    return c > 64 and (nch == 1 or (nch == 2 and 16 < n_q * nh <= 48))
+
+
+@pytest.mark.parametrize("n_inst,n_q,nh,max_sel,chunk,expect", [
+    (256, 4, 12, 2051, 1024, True),     # two 1,088-cell chunks, 48 rows
+    (256, 1, 12, 2051, 1024, False),    # two chunks of 12 rows: chunk + merge
+    (256, 4, 16, 2051, 1024, False),    # 64 rows
+    (64, 2, 12, 16384, 512, False),     # eight chunks
+    (1, 4, 12, 2051, 256, False),       # one-tile chunks
+    (200, 2, 12, 250, 256, True),       # one 256-cell chunk
+    (520, 4, 16, 600, 256, True),       # one 768-cell chunk, 64 rows
+    (100, 1, 12, 500, 256, False),
+    (3, 1, 12, 1, 64, False),           # one cell: one-tile chunk
+    (5, 1, 12, 0, 256, False),          # nothing selected: the merge writes the empty rows
+])
+def test_fused_single_launch(n_inst, n_q, nh, max_sel, chunk, expect):
+    got = api.fused_single_launch(n_inst, n_q, nh, max_sel, chunk)
+    assert got == expect == single_launch(n_inst, n_q, nh, max_sel, chunk)
+
+
+def test_fused_single_launch_sweep_and_status():
+    for n_inst in (1, 7, 100, 200, 256, 300, 1000):
+        for max_sel in (1, 64, 65, 500, 2051, 16384):
+            for n_q, nh in ((1, 12), (2, 12), (3, 12), (4, 12), (1, 16), (4, 16)):
+                for chunk in (64, 256, 1024):
+                    assert (api.fused_single_launch(n_inst, n_q, nh, max_sel, chunk)
+                            == single_launch(n_inst, n_q, nh, max_sel, chunk))
+    out = C.c_int32(0)
+    lib = api.library()
+    assert lib.sda_fused_single_launch(1, 1, 12, 10, 100, C.byref(out)) == api.SDA_ERR_UNSUPPORTED
+    assert lib.sda_fused_single_launch(1, 0, 12, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
+    assert lib.sda_fused_single_launch(1, 5, 13, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
+    assert lib.sda_fused_single_launch(-1, 1, 12, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
+    assert lib.sda_fused_single_launch(1, 1, 12, 10, 64, None) == api.SDA_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("n_inst,n_q,nh,max_sel,chunk", [
     (1, 1, 12, 600, 256), (1, 4, 12, 2051, 256), (256, 4, 12, 2051, 1024),
     (64, 2, 12, 16384, 512), (32, 4, 12, 131072, 1024), (3, 2, 5, 1, 64), (8, 4, 12, 2051, 256)])

@@ -11,22 +11,10 @@ import pytest
 
 import oracle
 from decode_attention_sparse_amd import inputs as gen
-from tests.gpu_util import (LSE_ATOL, LSE_RTOL, OUT_ATOL, OUT_RTOL, assert_close, run_batch,
-                            say)
+from tests.gpu_util import (LSE_ATOL, LSE_RTOL, OUT_ATOL, OUT_RTOL, assert_close, check,
+                            run_batch, say, two_pass)
 
 pytestmark = pytest.mark.gpu
-
-
-def check(x, out, lse, g=None, inst_ids=None, what=""):
-    ro, rl = oracle.attend(x, inst_ids)
-    sl = slice(None) if inst_ids is None else np.asarray(inst_ids)
-    e1 = assert_close(out[sl], ro, OUT_ATOL, OUT_RTOL, f"{what} out")
-    e2 = assert_close(lse[sl], rl, LSE_ATOL, LSE_RTOL, f"{what} lse")
-    if g is not None:
-        rg = oracle.gather(x)
-        valid = np.arange(x.sel.shape[1])[None, :] < x.n_sel[:, None]
-        assert np.array_equal(g[valid], rg[valid]), f"{what}: gather indices differ"
-    say(f"  {what}: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
 
 
 @pytest.mark.parametrize("n_q", [1])
@@ -167,24 +155,6 @@ def test_edge_counts_large_grid(n_q):
     out, lse, g, _ = run_batch(x)
     check(x, out, lse, g, what=f"edges large grid nq{n_q}")
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
-
-
-def two_pass(x, chunk, gather=True):
-    """sda_chunk_batch then sda_merge_batch at the given chunk size."""
-    import torch
-    from decode_attention_sparse_amd import api
-    n_inst, n_q, nh, D = x.q.shape
-    max_sel = int(x.sel.shape[1])
-    pool, dev = api.to_device(x)
-    ws = api.workspace(n_inst, n_q, nh, max_sel, chunk)
-    out = torch.full((n_inst, n_q, nh, D), float("nan"), device="cuda")
-    lse = torch.full((n_inst, n_q, nh), float("nan"), device="cuda")
-    g = torch.full(x.sel.shape, -7, dtype=torch.int32, device="cuda") if gather else None
-    api.chunk_batch(pool, dev["page_table"], dev["sel"], dev["n_sel"], max_sel, dev["q"],
-                    x.softmax_scale, chunk, ws, gather_out=g)
-    api.merge_batch(dev["n_sel"], max_sel, chunk, ws, out, lse)
-    torch.cuda.synchronize()
-    return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)
 
 
 @pytest.mark.parametrize("n_q", [2, 4])
@@ -329,8 +299,8 @@ def test_full_size_configs_sampled(cfg, ids):
 def test_batch_entry_equals_two_passes(cfg, n_q, n_inst):
     """sda_decode_attn_batch equals sda_chunk_batch followed by
     sda_merge_batch at the chunk size the fused call uses, bit for bit (the
-    partials in the workspace included), and the two passes at the caller's
-    chunk size up to rounding."""
+    partials in the workspace included, where the call runs the merge pass),
+    and the two passes at the caller's chunk size up to rounding."""
     import torch
     from decode_attention_sparse_amd import api
     say(f"case: batch entry vs the two passes, config {cfg}, n_q={n_q}, n_inst={n_inst}")
@@ -354,9 +324,10 @@ def test_batch_entry_equals_two_passes(cfg, n_q, n_inst):
 
     out2, lse2, ws2 = two_pass(fc)
     assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
-    for a1, a2 in zip(api.partials(ws1, n_inst, n_q, nh, max_sel, fc),
-                      api.partials(ws2, n_inst, n_q, nh, max_sel, fc)):
-        assert torch.equal(a1, a2)
+    if not api.fused_single_launch(n_inst, n_q, nh, max_sel, x.chunk):  # else no partials
+        for a1, a2 in zip(api.partials(ws1, n_inst, n_q, nh, max_sel, fc),
+                          api.partials(ws2, n_inst, n_q, nh, max_sel, fc)):
+            assert torch.equal(a1, a2)
     if fc != x.chunk:
         out3, lse3, _ = two_pass(x.chunk)
         assert_close(out1, out3, OUT_ATOL, OUT_RTOL, "fused vs caller's chunk out")
