@@ -44,31 +44,47 @@ PAGES_V3_US = {1: 34.5, 2: 41.0, 3: 73.0, 4: 84.9}
 PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
 
 
-# HBM bytes per launch of the chunk kernel on the headline workload at n_q = 4
-# (cold caches), from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE),
-# each scaled by what the counter reads for a plain 256 MiB device copy
-# (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary with the commands is in
-# profiles/chunk_mfma_kernel__hbm_bytes__pages_point_and_batched.md.  The
-# figures hold only for the kernel source they were taken on.
-CHUNK_TRAFFIC = {"sources_sha256": "02c192545447183a3a5bb876832aa1b9fafe78ede0bb8a73e2da1b39a051899d",
-                 "fetch_bytes": 1_972_326, "write_bytes": 1_634_688}
-TRAFFIC_SOURCES = ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
-                   "decode_attention_sparse_amd/csrc/sda_internal.h",
-                   "decode_attention_sparse_amd/csrc/sda_api.hip")
+# HBM bytes per launch measured with two rocprofv3 counter runs (FETCH_SIZE,
+# then WRITE_SIZE, caches evicted before each call), each scaled by what the
+# counter reads for a plain 256 MiB device copy (FETCH_SIZE x 2.0,
+# WRITE_SIZE x 1.0): the headline chunk kernel (n_q = 4), the prompt kernel
+# and the KV append kernel.  The summaries with the commands are under
+# profiles/.  A figure holds only for the kernel sources it was taken on
+# (their SHA-256); a changed source reports null.
+MEASURED_TRAFFIC = {
+    "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
+                          "decode_attention_sparse_amd/csrc/sda_internal.h",
+                          "decode_attention_sparse_amd/csrc/sda_api.hip"),
+              "sources_sha256": "22fe6a228705c120c9e7d96d7f6845c1209eb8899b1d4c4bb6aefbb3723f3a22", "fetch_bytes": 1972250, "write_bytes": 1634688},
+    "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
+                           "decode_attention_sparse_amd/csrc/sda_internal.h",
+                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
+               "sources_sha256": "22fe6a228705c120c9e7d96d7f6845c1209eb8899b1d4c4bb6aefbb3723f3a22", "fetch_bytes": 263967152, "write_bytes": 25264128},
+    "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
+                           "decode_attention_sparse_amd/csrc/sda_internal.h",
+                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
+               "sources_sha256": "ffeb82a708493d29f307579af79f29975decaaeb70a632bd27abc5217518d35f", "fetch_bytes": 268718940, "write_bytes": 68157472},
+}
 
 
-def chunk_traffic():
-    """Measured HBM bytes per headline chunk launch, or None when the kernel
-    source differs from the one the counters were taken on."""
+def sources_sha256(files) -> str:
     import hashlib
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
-    for f in TRAFFIC_SOURCES:
+    for f in files:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != CHUNK_TRAFFIC["sources_sha256"]:
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """Measured HBM bytes per launch of `kernel` ("chunk", "prompt",
+    "append"), or None when its sources differ from those the counters were
+    taken on."""
+    m = MEASURED_TRAFFIC[kernel]
+    if not m["sources_sha256"] or sources_sha256(m["sources"]) != m["sources_sha256"]:
         return None
-    return CHUNK_TRAFFIC["fetch_bytes"] + CHUNK_TRAFFIC["write_bytes"]
+    return m["fetch_bytes"] + m["write_bytes"]
 
 
 def algorithmic_bytes(x) -> int:
@@ -157,6 +173,19 @@ def time_calls(cases, iters, flush=None):
         for k, (e0, e1) in enumerate(row):
             res[k].append(e0.elapsed_time(e1))
     return res
+
+
+def warm_up(cases, flush, min_ms=50.0):
+    """Untimed cold calls until at least min_ms of them have run (at least
+    five).  After setup, the first 10-20 ms of sustained HBM traffic run up to
+    40 % slower (on the dense workload, cold calls start above 600 us and
+    settle near 440 us after about 20 calls), so timing starts after that.
+    Returns the number of calls run per case."""
+    total, n = 0.0, 0
+    while total < min_ms or n < 5:
+        total += sum(sum(s) for s in time_calls(cases, 5, flush=flush))
+        n += 5
+    return n
 
 
 def time_passes(cases, iters, flush=None):
@@ -349,7 +378,7 @@ def prompt_section(reps, cpu_seconds):
         "query_rows_x_visible_cells": pairs,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_MFMA_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4),
-                     "traffic": None, "kernel": "chunk_mfma_kernel (prompt form)",
+                     "traffic": measured_traffic("prompt"), "kernel": "chunk_mfma_kernel (prompt form)",
                      "algorithmic_flops_per_launch": flops, "launch_ms_mean": round(ms, 4),
                      "note": "flops of the fp32-accurate products (q.k and p.v, 2 x 256 each per "
                              "row and visible cell) against the int8 matrix peak that runs them; "
@@ -410,8 +439,12 @@ def append_section(iters, flush):
     read flush, HIP events around the call on the launch stream."""
     import torch
     x, call = append_case()
-    for _ in range(3):
+    n_warm, t0 = 0, time.perf_counter()
+    while n_warm < 5 or time.perf_counter() - t0 < 0.05:  # past the start-up transient
+        flush()
         call()
+        torch.cuda.synchronize()
+        n_warm += 1
     evs = []
     for _ in range(iters):
         flush()
@@ -436,10 +469,12 @@ def append_section(iters, flush):
         "us_per_call_p90": round(float(np.percentile(us, 90)), 3),
         "rows_per_s": round(x.n_inst * x.n_new / (med * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("append"),
                      "kernel": "kv_append_kernel", "algorithmic_bytes_per_launch": nbytes,
                      "launch_us_median": round(med, 3)},
-        "timing": f"{iters} eager calls, caches evicted before each by reading a 1 GiB buffer",
+        "timing": f"{iters} eager calls after {n_warm} untimed ones, caches evicted before "
+                  "each by reading a 1 GiB buffer",
     }
 
 
@@ -606,7 +641,7 @@ def main(argv=None):
                    "timing": "K steps captured in one HIP graph, HIP events around its replay; back-to-back calls with warm caches, as the pages' 200-call loop"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                     "traffic": chunk_traffic(),
+                     "traffic": measured_traffic("chunk"),
                      "kernel": f"{'chunk_tile_kernel' if c4.fused_chunk == 64 else 'chunk_mfma_kernel'}"
                                f", the n_q = 4 call of the step "
                                f"({c4.fused_chunk}-cell chunks: "
@@ -634,7 +669,7 @@ def main(argv=None):
                 kw["chunk"] = a.chunk2
             x = inputs.make(cfg, **kw)
             c = Case(x, x.chunk)
-            time_calls([c], 3)
+            n_warm = warm_up([c], flush)
             d = summarize(c, time_calls([c], a.batched_iters, flush=flush)[0],
                           time_passes([c], a.batched_iters, flush=flush)[0])
             nch = -(-int(x.sel.shape[1]) // c.fused_chunk)
@@ -647,6 +682,10 @@ def main(argv=None):
                       "two_pass_note": "chunk_us_mean / merge_us_mean: sda_chunk_batch and "
                                        "sda_merge_batch at the call's chunk size, timed as "
                                        "separate calls",
+                      "warmup_calls": n_warm,
+                      "timing": f"{a.batched_iters} eager calls after {n_warm} untimed ones, "
+                                "caches evicted before each by reading a 1 GiB buffer, HIP "
+                                "events around the call on the launch stream; median",
                       "bytes_algorithmic": c.bytes, "partials_bytes_written":
                       0 if c.single_launch else int(x.n_inst * nch * x.n_q * 12 * 258 * 4)})
             batched[x.workload] = d

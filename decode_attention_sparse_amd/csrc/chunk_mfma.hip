@@ -14,12 +14,21 @@
 // lives in one wave; the last wave is the producer: it runs the gather and
 // stages all code rows (the compute waves issue no global loads and hold no
 // staging registers).  Cells are processed in tiles of 64.  The compute
-// waves' state and per-tile step (RowBlock) are shared by three launches:
-//   chunk_mfma_kernel<RB, DS, false>  the pipelined chunk pass below;
-//   chunk_tile_kernel<RB, DS>         one-tile chunks in latency-bound grids
-//                                     (the tile staged at once, no pipeline);
-//   chunk_mfma_kernel<RB, 1, true>    prompt attention: the pipelined pass
-//                                     over an implicit causal cell list.
+// waves' state and per-tile step (RowBlock) are shared by all launches:
+//   chunk_mfma_kernel<RB, DS, false>           the pipelined chunk pass below
+//                                              (chunk partials);
+//   chunk_mfma_kernel<RB, DS, false, 1, true>  the same for calls with one
+//                                              chunk per instance, writing
+//                                              the normalised outputs;
+//   chunk_mfma_kernel<RB, 1, false, 2, true>   calls with two chunks per
+//                                              instance: two pipelines per
+//                                              workgroup, merged in LDS;
+//   chunk_tile_kernel<RB, DS>                  one-tile chunks in latency-
+//                                              bound grids (the tile staged
+//                                              at once, no pipeline);
+//   chunk_mfma_kernel<RB, 1, true>             prompt attention: the
+//                                              pipelined pass over an
+//                                              implicit causal cell list.
 //
 // Exactness of the contractions.  The INT8 codes are used as they are; the
 // fp32 operands are split into int8 digits so that the int8 MFMA (exact
