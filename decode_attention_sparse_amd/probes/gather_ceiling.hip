@@ -1,9 +1,10 @@
 // Cold-cache HBM read ceilings on this GPU for the access shapes of the
 // chunk pass: 256-byte code rows gathered at random, 4 KB pages (16 rows)
-// gathered at random, and a plain sequential read.  Each measurement reads
-// 268 MB (or 1 GiB sequential) after evicting the caches by reading a
-// separate 1 GiB buffer; the median of 5 launches is printed as one JSON
-// line per shape.  Standalone program (no library code); built next to
+// gathered at random, and a plain sequential read.  Each gather measurement
+// reads 268 MB or 2.1 GB (16 or 128 tiles of 64 rows per workgroup), the
+// sequential one 1 GiB, after evicting the caches by reading a separate
+// 1 GiB buffer; after at least 60 ms of untimed launches, the median
+// of 21 launches is printed as one JSON line per shape.  Standalone program (no library code); built next to
 // libsda.so and run by `bench.py --gather-ceiling`.
 #include <hip/hip_runtime.h>
 
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void seq_read(const v4i *src, int64_t n, int *
 
 int main() {
     const int64_t inst = 256, cells_per_inst = 32768, cells = inst * cells_per_inst;  // 2 GiB per pool
-    const int wgs = 512, tiles = 16, per = tiles * 64;
+    const int wgs = 512, max_tiles = 128, max_per = max_tiles * 64;
     int8_t *kp, *vp;
     int *rows, *sink;
     v4i *flush;
@@ -61,7 +62,7 @@ int main() {
     CHECK(hipMalloc(&kp, cells * 256));
     CHECK(hipMalloc(&vp, cells * 256));
     CHECK(hipMalloc(&flush, flush_n * 16));
-    CHECK(hipMalloc(&rows, (size_t)wgs * per * sizeof(int)));
+    CHECK(hipMalloc(&rows, (size_t)wgs * max_per * sizeof(int)));
     CHECK(hipMalloc(&sink, 16));
     CHECK(hipMemset(kp, 1, cells * 256));
     CHECK(hipMemset(vp, 2, cells * 256));
@@ -72,9 +73,13 @@ int main() {
     auto evict = [&] { hipLaunchKernelGGL(seq_read, 2048, 256, 0, 0, flush, flush_n, sink); };
     evict();  // clean lines only from here on
     CHECK(hipDeviceSynchronize());
+    // Untimed rounds first, until at least 60 ms of them have run: the first
+    // 10-20 ms of sustained HBM traffic run slower than the steady state.
+    // Then the median of 21 timed launches.
     auto median_us = [&](auto launch) {
         std::vector<float> v;
-        for (int rep = 0; rep < 6; ++rep) {
+        float warm_ms = 0.f;
+        for (int rep = 0; rep < 100000 && (warm_ms < 60.f || (int)v.size() < 21); ++rep) {
             evict();
             hipEventRecord(e0);
             launch();
@@ -82,39 +87,47 @@ int main() {
             hipEventSynchronize(e1);
             float ms = 0.f;
             hipEventElapsedTime(&ms, e0, e1);
-            if (rep) v.push_back(ms * 1e3f);
+            if (warm_ms < 60.f)
+                warm_ms += ms + 0.15f;  // with the eviction read before it
+            else
+                v.push_back(ms * 1e3f);
         }
         std::sort(v.begin(), v.end());
         return v[v.size() / 2];
     };
-    const double gather_bytes = (double)wgs * per * 512;
+    // Two launch lengths: 16 tiles per workgroup (268 MB, about 50 us, where
+    // the grid's start and drain weigh) and 128 (2.1 GB, about 400 us).
     const char *shape[3] = {"random 256-byte rows", "random 4 KB pages of 16 rows", "sequential rows"};
     std::mt19937_64 rng(7);
-    std::vector<int> host(wgs * per);
-    for (int s = 0; s < 3; ++s) {
-        for (int w = 0; w < wgs; ++w) {
-            const int64_t base = (int64_t)(w / 2) * cells_per_inst;  // two workgroups per instance
-            std::vector<int> c(cells_per_inst);
-            for (int j = 0; j < cells_per_inst; ++j) c[j] = j;
-            if (s == 0) {
-                std::shuffle(c.begin(), c.end(), rng);
-            } else if (s == 1) {
-                std::vector<int> pg(cells_per_inst / 16);
-                for (size_t j = 0; j < pg.size(); ++j) pg[j] = (int)j;
-                std::shuffle(pg.begin(), pg.end(), rng);
-                for (int j = 0; j < per; ++j) c[j] = pg[j / 16] * 16 + (j & 15);
-            } else {
-                for (int j = 0; j < per; ++j) c[j] = (w & 1) * per + j;
+    std::vector<int> host((size_t)wgs * max_per);
+    for (int tiles : {16, max_tiles}) {
+        const int per = tiles * 64;
+        const double gather_bytes = (double)wgs * per * 512;
+        for (int s = 0; s < 3; ++s) {
+            for (int w = 0; w < wgs; ++w) {
+                const int64_t base = (int64_t)(w / 2) * cells_per_inst;  // two workgroups per instance
+                std::vector<int> c(cells_per_inst);
+                for (int j = 0; j < cells_per_inst; ++j) c[j] = j;
+                if (s == 0) {
+                    std::shuffle(c.begin(), c.end(), rng);
+                } else if (s == 1) {
+                    std::vector<int> pg(cells_per_inst / 16);
+                    for (size_t j = 0; j < pg.size(); ++j) pg[j] = (int)j;
+                    std::shuffle(pg.begin(), pg.end(), rng);
+                    for (int j = 0; j < per; ++j) c[j] = pg[j / 16] * 16 + (j & 15);
+                } else {
+                    for (int j = 0; j < per; ++j) c[j] = (w & 1) * per + j;
+                }
+                for (int j = 0; j < per; ++j) host[(size_t)w * per + j] = (int)(base + c[j]);
             }
-            for (int j = 0; j < per; ++j) host[(size_t)w * per + j] = (int)(base + c[j]);
+            for (size_t j = 0; j < (size_t)wgs * per; ++j)
+                if (host[j] < 0 || host[j] >= cells) { fprintf(stderr, "row out of range\n"); return 1; }
+            CHECK(hipMemcpy(rows, host.data(), (size_t)wgs * per * sizeof(int), hipMemcpyHostToDevice));
+            const float us = median_us([&] { hipLaunchKernelGGL(row_gather, wgs, 256, 0, 0, kp, vp, rows, tiles, sink); });
+            printf("{\"shape\": \"%s\", \"tiles_per_workgroup\": %d, \"bytes\": %.0f, \"us\": %.2f, \"GBps\": %.1f}\n",
+                   shape[s], tiles, gather_bytes, us, gather_bytes / (us * 1e-6) / 1e9);
+            fflush(stdout);
         }
-        for (int r : host)
-            if (r < 0 || r >= cells) { fprintf(stderr, "row out of range\n"); return 1; }
-        CHECK(hipMemcpy(rows, host.data(), host.size() * sizeof(int), hipMemcpyHostToDevice));
-        const float us = median_us([&] { hipLaunchKernelGGL(row_gather, wgs, 256, 0, 0, kp, vp, rows, tiles, sink); });
-        printf("{\"shape\": \"%s\", \"bytes\": %.0f, \"us\": %.2f, \"GBps\": %.1f}\n", shape[s], gather_bytes,
-               us, gather_bytes / (us * 1e-6) / 1e9);
-        fflush(stdout);
     }
     const int64_t seq_n = (1ll << 30) / 16;
     const float us = median_us([&] { hipLaunchKernelGGL(seq_read, 4096, 256, 0, 0, (const v4i *)kp, seq_n, sink); });
