@@ -616,8 +616,11 @@ def main(argv=None):
     c4, k4_us = cases[3], per_q["q4"]["chunk_us"]
     achieved = c4.chunk_bytes / (k4_us * 1e-6) / 1e9
     flush = make_flush()
-    cold = time_calls(cases, 20, flush=flush)
+    cold = time_calls(cases, 200, flush=flush)  # 200 calls per query count, as the pages' loop
     cold_us = {f"q{nq}": round(float(np.median(s_)) * 1e3, 3) for nq, s_ in zip((1, 2, 3, 4), cold)}
+    cold_spread = {f"q{nq}": {"p10": round(float(np.percentile(s_, 10)) * 1e3, 3),
+                              "p90": round(float(np.percentile(s_, 90)) * 1e3, 3)}
+                   for nq, s_ in zip((1, 2, 3, 4), cold)}
     del cases
     torch.cuda.empty_cache()
 
@@ -654,7 +657,9 @@ def main(argv=None):
                      "bytes_per_step": bytes_sum, "call_us_per_step": round(call_us_sum, 3)},
         "per_query_count": per_q,
         "cold_us_per_call_median": cold_us,
-        "cold_note": "eager calls, caches evicted before each by reading a 1 GiB buffer, HIP events around the kernels",
+        "cold_us_per_call_p10_p90": cold_spread,
+        "cold_note": "200 eager calls per query count, caches evicted before each by reading a "
+                     "1 GiB buffer, HIP events around each call",
         "hbm_read_ceiling_measured": ceiling,
         "vs_baseline_ref": "pages' v3 kernel on RTX 2080 Ti, sum over q=1..4 of chunk+merge us (context, other hardware)",
         "wall_s_timed_region": round(wall, 3),

@@ -393,6 +393,33 @@ struct RowBlock {
     }
 };
 
+// LDS flags between the roles of one pipeline in a two-pipeline workgroup
+// (in place of the workgroup barrier, which would make each step of both
+// pipelines wait for the slower of the two).  A flag holds the last step its
+// writer completed; a release store after that step's LDS accesses, an
+// acquire load before the reader's.  Waits are bounded: past kSpinLimit polls
+// the wait gives up and reports it, so a wait can never hang the GPU (the
+// kernel then writes NaN for the rows; no correct run comes near the bound,
+// which is tens of milliseconds).
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ void flag_post(int *flag, int step) {
+    __hip_atomic_store(flag, step, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ bool flag_wait(const int *flag, int step) {
+#pragma clang loop unroll(disable)
+    for (int spin = 0; spin < kSpinLimit; ++spin) {
+        // uniform (every lane reads the same flag): a scalar loop exit, so
+        // the wait adds no divergent control flow around the step
+        const int v = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (v >= step) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
 // DS = number of compute waves per 16-row group, each accumulating
 // O^T for 256 / DS of the head dimensions (every one of them scores the
 // whole tile).  DS = 1: two workgroups per CU (LDS-limited; with RB = 1 that
@@ -434,11 +461,17 @@ void chunk_mfma_kernel(Params p, int cpw) {
     __shared__ __attribute__((aligned(16))) float ks_p[SP][4][kTile];
     __shared__ __attribute__((aligned(16))) float vs_p[SP][4][kTile];
     __shared__ __attribute__((aligned(16))) float bias_p[SP][4][kTile];
+    // two pipelines: per pipeline, the producer's last completed step and each
+    // compute wave's; a flag that any wait gave up
+    __shared__ int ready_f[SP], done_f[SP][DS * RB], stuck_f;
 
     // wave index: uniform, so that the role and pipeline branches are scalar
     const int wv = SP == 1 ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pipe = SP == 1 ? 0 : wv / kPipe;
-    const int wave = wv - pipe * kPipe;  // within the pipeline
+    // role within the pipeline (kProducer: the producer).  Pipeline 1 puts its
+    // producer first, so that with waves dealt to the SIMDs in turn the two
+    // producers sit on different SIMDs.
+    const int wave = pipe == 0 ? wv : (wv - kPipe + kPipe - 1) % kPipe;
     const int lane = threadIdx.x & 63;
     int8_t (&kbuf)[2][kBuf] = kbuf_p[pipe];
     int8_t (&vbuf)[2][kBuf] = vbuf_p[pipe];
@@ -497,6 +530,16 @@ void chunk_mfma_kernel(Params p, int cpw) {
         (&vs_p[0][0][0])[e] = 0.f;
         (&bias_p[0][0][0])[e] = -INFINITY;
     }
+    if constexpr (SP > 1) {
+        if (threadIdx.x < SP * (DS * RB + 1)) {
+            const int h = threadIdx.x / (DS * RB + 1), w = threadIdx.x % (DS * RB + 1);
+            if (w == DS * RB)
+                ready_f[h] = -100;  // below every step a wait asks for
+            else
+                done_f[h][w] = -100;
+        }
+        if (threadIdx.x == 0) stuck_f = 0;
+    }
     __syncthreads();
 
     // Both roles run n_iter + 4 iterations with one barrier each.  Iteration
@@ -551,6 +594,17 @@ void chunk_mfma_kernel(Params p, int cpw) {
                         vst[4 * k + cc] = *reinterpret_cast<const v4i *>(src + 64 * cc);
                 }
             }
+            // two pipelines: the compute waves must be done with step t - 1,
+            // whose buffers this step overwrites (the loads above are in
+            // flight meanwhile)
+            if constexpr (SP > 1) {
+                if (t >= 0) {
+                    bool ok = true;
+#pragma unroll
+                    for (int w = 0; w < DS * RB; ++w) ok &= flag_wait(&done_f[pipe][w], t - 1);
+                    if (!ok) stuck_f = 1;
+                }
+            }
             // complete: code rows to LDS (row 16k + l16, bytes 64c + 16g)
             if (ld_k) {
                 int8_t *kb = kbuf[(t + 2) & 1] + l16 * kStride + 16 * g;
@@ -587,9 +641,18 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 ph2 = ph;
             }
             sel3 = (ld_s && j4 < j_end) ? sel4 : -1;
+            if constexpr (SP > 1) {
+                flag_post(&ready_f[pipe], t);  // this step's LDS writes are done (every lane
+                                               // stores the same value)
+                __builtin_amdgcn_sched_barrier(0);  // keep steps apart, as the barrier did
+            } else {
+                __syncthreads();
+            }
+        }
+        if constexpr (SP > 1) {  // the end of both pipelines, then the compute waves' hand-over
+            __syncthreads();
             __syncthreads();
         }
-        if constexpr (SP > 1) __syncthreads();  // the compute waves' hand-over
         return;
     }
 
@@ -607,6 +670,10 @@ void chunk_mfma_kernel(Params p, int cpw) {
     const int64_t lim_row = kPrompt ? pos0 + (row0 + row) / p.n_qheads : 0;
     for (int t = -4; t < n_iter; ++t) {
         if (t >= -1) {
+            // two pipelines: this step reads what the producer wrote in its
+            // step t - 1 (and earlier)
+            if constexpr (SP > 1)
+                if (!flag_wait(&ready_f[pipe], t - 1)) stuck_f = 1;
             // Both halves of a step run every iteration (no validity branches,
             // so the scheduler can interleave them); a tile outside
             // [0, n_tiles) has all scores at -inf and changes nothing.
@@ -627,8 +694,13 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 rb.emit(p, ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row, row, g, dh);
                 rb.reset();
             }
+            if constexpr (SP > 1)
+                flag_post(&done_f[pipe][wave], t);  // this step's LDS reads are done
         }
-        __syncthreads();
+        if constexpr (SP == 1)
+            __syncthreads();
+        else
+            __builtin_amdgcn_sched_barrier(0);  // keep steps apart, as the barrier did
     }
     if constexpr (kPrompt)
         rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
@@ -649,6 +721,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
         float *xm = &ks_p[SP - 1][0][0];
         float *xl = &vs_p[SP - 1][0][0];
         if constexpr (SP > 1) {
+            __syncthreads();  // both pipelines' steps are over: their buffers are idle
             if (pipe == 1) {
 #pragma unroll
                 for (int db = 0; db < kDB; ++db) *xslot(db) = rb.o[db] * rb.frame;
@@ -659,6 +732,16 @@ void chunk_mfma_kernel(Params p, int cpw) {
             }
             __syncthreads();
             if (pipe == 1) return;
+            if (stuck_f) {  // a wait gave up (never in a correct run): poison the rows
+                if (row_ok) {
+                    float *dst = p.out + grow * kDim + 16 * kDB * dh + 4 * g;
+#pragma unroll
+                    for (int db = 0; db < kDB; ++db)
+                        *reinterpret_cast<v4f *>(dst + 16 * db) = (v4f){NAN, NAN, NAN, NAN};
+                    if (g == 0) p.lse[grow] = NAN;
+                }
+                return;
+            }
         }
         if (!row_ok) return;
         // the merge of the instance's nch partials, chunk by chunk
