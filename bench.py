@@ -55,15 +55,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "22fe6a228705c120c9e7d96d7f6845c1209eb8899b1d4c4bb6aefbb3723f3a22", "fetch_bytes": 1972235, "write_bytes": 1634688},
+              "sources_sha256": "e4c11dd107c79df74beb3739ed1382aeaec2f4cac7a686ae9deae6ba2d9bec1b", "fetch_bytes": 1972202, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "22fe6a228705c120c9e7d96d7f6845c1209eb8899b1d4c4bb6aefbb3723f3a22", "fetch_bytes": 263979085, "write_bytes": 25264128},
+               "sources_sha256": "e4c11dd107c79df74beb3739ed1382aeaec2f4cac7a686ae9deae6ba2d9bec1b", "fetch_bytes": 264051724, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "ffeb82a708493d29f307579af79f29975decaaeb70a632bd27abc5217518d35f", "fetch_bytes": 268720392, "write_bytes": 68157483},
+               "sources_sha256": "ffeb82a708493d29f307579af79f29975decaaeb70a632bd27abc5217518d35f", "fetch_bytes": 268718215, "write_bytes": 68157451},
 }
 
 
