@@ -196,7 +196,9 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
     """Many instances: page_table [n_inst][pt_stride], sel [n_inst][sel_stride],
     n_sel device int32 [n_inst], q [n_inst][n_q][n_qheads][256].  The call
     runs chunks of fused_chunk_cells(n_inst, max_sel, chunk_cells) cells; the
-    workspace then holds those partials (partials(..., that chunk size))."""
+    workspace then holds those partials (partials(..., that chunk size)),
+    unless fused_single_launch(...) says the call is one launch that leaves
+    the workspace untouched."""
     n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     if ws is None:
         ws = workspace(n_inst, n_q, n_qheads, max_sel, chunk_cells, q.device)
