@@ -145,3 +145,35 @@ def test_graph_replay_two_pipelines():
         y = dataclasses.replace(x, n_sel=counts, q=dev["q"].cpu().numpy())
         check(y, out.cpu().numpy(), lse.cpu().numpy(), inst_ids=[rep, rep + 3, 199],
               what=f"replay {rep}")
+
+
+@pytest.mark.parametrize("kw,nch", [
+    (dict(n_inst=180, n_q=3, pool_cells=1024, n_sel=700, chunk=256), 2),  # two pipelines, 36 rows
+    (dict(n_inst=200, n_q=2, pool_cells=1024, n_sel=250, chunk=256), 1),  # one chunk, small grid
+])
+def test_output_from_chunk_pass_masked(kw, nch):
+    """Masked pages (-1), page ids past the pool, selected ids past the
+    logical range and an instance with every page masked, in single-launch
+    calls: against the oracle, the two passes bit for bit, gather indices
+    exact."""
+    from decode_attention_sparse_amd import api
+    say(f"case: single launch with masking, {kw}")
+    x = gen.make(None, seed=540 + nch, sel="uniform", **kw)
+    n_inst, n_q, nh, _ = x.q.shape
+    max_sel = int(x.sel.shape[1])
+    assert api.fused_single_launch(n_inst, n_q, nh, max_sel, x.chunk)
+    assert -(-max_sel // api.fused_chunk_cells(n_inst, max_sel, x.chunk)) == nch
+    pt, sel = x.page_table.copy(), x.sel.copy()
+    pt[0, ::7] = -1
+    pt[1, 3] = x.n_phys_pages + 5
+    pt[2, :] = -1                      # every cell of instance 2 masked
+    sel[3, ::11] = x.n_logical_pages * 16 + 3  # past the logical range
+    sel[4, 1] = -9
+    x = dataclasses.replace(x, page_table=pt, sel=sel)
+    from tests.gpu_util import run_batch
+    out, lse, g, _ = run_batch(x)
+    o2, l2, g2, _ = two_pass(x, api.fused_chunk_cells(n_inst, max_sel, x.chunk))
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2) and np.array_equal(g, g2)
+    check(x, out, lse, g, inst_ids=[0, 1, 2, 3, 4, n_inst - 1], what="masked single launch")
+    assert np.all(out[2] == 0) and np.all(np.isneginf(lse[2]))
+    assert np.all(g[2] == -1) and g[3, 0] == -1 and g[4, 1] == -1
