@@ -430,12 +430,14 @@ __device__ __forceinline__ bool flag_wait(const int *flag, int step) {
 // kPrompt = false: decode.  Workgroup (blockIdx.x, blockIdx.y) = instance i,
 // chunks [cpw * y, cpw * y + cpw) of its list; emits chunk partials.
 // kFinal (decode calls whose every instance has at most SP chunks): the
-// workgroup runs all of instance i's chunks, SP = 2 pipelines side by side
-// (pipeline h: chunk h, its own producer wave, compute waves and LDS), and
-// writes the head outputs itself: the partials are merged in LDS with the
-// merge pass's arithmetic (merge_weight, merge_acc), so the result is the
-// two passes' bit for bit, without the partials' round trip through memory
-// or a second launch.
+// workgroup runs all of instance i's chunks and writes the head outputs
+// itself.  SP = 1: its one chunk.  SP = 2: two pipelines side by side
+// (pipeline h: chunk h, its own producer wave, compute waves and LDS),
+// synchronised through LDS flags rather than the workgroup barrier; the two
+// partials are merged in LDS.  Either way the merge pass's arithmetic
+// (merge_weight, merge_acc) turns the partials into outputs, so the result
+// is the two passes' bit for bit, without the partials' round trip through
+// memory or a second launch.
 // kPrompt = true: prompt attention.  Workgroup (i, y) = the 16 RB query rows
 // starting at row 16 RB y of instance i (rows are position-major, so a
 // workgroup holds a few consecutive positions); the cell list is implicit
@@ -452,7 +454,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     static_assert(SP == 1 || RB * 8 * 64 * 16 <= 2 * kBuf,
                   "the hand-over fits a pipeline's K (and V) buffers");
     constexpr int kPipe = DS * RB + 1;  // waves per pipeline
-    constexpr int kProducer = DS * RB;  // a pipeline's last wave
+    constexpr int kProducer = DS * RB;  // the producer's role index in a pipeline
     constexpr int kDB = 16 / DS;        // 16-dim blocks of O^T per compute wave
     __shared__ __attribute__((aligned(1024))) int8_t kbuf_p[SP][2][kBuf];
     __shared__ __attribute__((aligned(1024))) int8_t vbuf_p[SP][2][kBuf];
@@ -471,7 +473,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     // role within the pipeline (kProducer: the producer).  Pipeline 1 puts its
     // producer first, so that with waves dealt to the SIMDs in turn the two
     // producers sit on different SIMDs.
-    const int wave = pipe == 0 ? wv : (wv - kPipe + kPipe - 1) % kPipe;
+    const int wave = pipe == 0 ? wv : (wv - 1) % kPipe;
     const int lane = threadIdx.x & 63;
     int8_t (&kbuf)[2][kBuf] = kbuf_p[pipe];
     int8_t (&vbuf)[2][kBuf] = vbuf_p[pipe];
@@ -489,8 +491,8 @@ void chunk_mfma_kernel(Params p, int cpw) {
     if constexpr (kFinal) {
         // pipeline h runs chunk h (cells [h C, h C + C) clipped to the count);
         // an instance with fewer chunks leaves a pipeline with no tiles, which
-        // still takes every step (no early exit: the workgroup shares its
-        // barriers) and contributes nothing
+        // still takes every step (no early exit: every wave meets the
+        // workgroup's barriers) and contributes nothing
         const int n = count_of(p, i);
         c0 = pipe;
         j_begin = pipe * p.chunk;

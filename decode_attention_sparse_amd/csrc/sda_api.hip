@@ -1,6 +1,7 @@
 // extern "C" entry points of libsda.so (declared in include/sda.h):
-// host-side validation, workspace layout, and the chunk + merge launches on
-// the caller's stream.  No allocation, no synchronisation, no global state.
+// host-side validation, workspace layout, and the kernel launches on the
+// caller's stream (chunk pass + merge pass, or the chunk kernel's
+// single-launch form).  No allocation, no synchronisation, no global state.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -208,9 +209,10 @@ int sda_fused_chunk_cells(int32_t n_inst, int32_t max_sel, int32_t chunk_cells,
 int sda_fused_single_launch(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t max_sel,
                             int32_t chunk_cells, int32_t *single_launch) {
     if (!single_launch || n_inst < 0 || max_sel < 0 || chunk_cells < 1 || n_q < 1 ||
-        n_qheads < 1 || (int64_t)n_q * n_qheads > SDA_MAX_ROWS)
+        n_qheads < 1)
         return SDA_ERR_INVALID_ARG;
-    if (chunk_cells % SDA_CHUNK_ALIGN) return SDA_ERR_UNSUPPORTED;
+    if (chunk_cells % SDA_CHUNK_ALIGN || (int64_t)n_q * n_qheads > SDA_MAX_ROWS)
+        return SDA_ERR_UNSUPPORTED;
     sda::Params p;
     memset(&p, 0, sizeof p);
     p.n_inst = n_inst;

@@ -144,9 +144,9 @@ int sda_fused_chunk_cells(int32_t n_inst, int32_t max_sel, int32_t chunk_cells,
  * <= 48 (one workgroup runs both chunks of an instance, one gather pipeline
  * each); otherwise the call launches the chunk pass and the merge pass.
  *   single_launch (host out): 1 or 0
- * Returns SDA_OK, SDA_ERR_INVALID_ARG (negative sizes, rows outside
- * [1, SDA_MAX_ROWS], null output) or SDA_ERR_UNSUPPORTED (chunk_cells not a
- * multiple of SDA_CHUNK_ALIGN). */
+ * Returns SDA_OK, SDA_ERR_INVALID_ARG (negative sizes, n_q or n_qheads below
+ * 1, null output) or SDA_ERR_UNSUPPORTED (chunk_cells not a multiple of
+ * SDA_CHUNK_ALIGN, or more than SDA_MAX_ROWS rows). */
 int sda_fused_single_launch(int32_t n_inst, int32_t n_q, int32_t n_qheads, int32_t max_sel,
                             int32_t chunk_cells, int32_t *single_launch);
 

@@ -141,7 +141,7 @@ def test_fused_single_launch_sweep_and_status():
     lib = api.library()
     assert lib.sda_fused_single_launch(1, 1, 12, 10, 100, C.byref(out)) == api.SDA_ERR_UNSUPPORTED
     assert lib.sda_fused_single_launch(1, 0, 12, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
-    assert lib.sda_fused_single_launch(1, 5, 13, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
+    assert lib.sda_fused_single_launch(1, 5, 13, 10, 64, C.byref(out)) == api.SDA_ERR_UNSUPPORTED
     assert lib.sda_fused_single_launch(-1, 1, 12, 10, 64, C.byref(out)) == api.SDA_ERR_INVALID_ARG
     assert lib.sda_fused_single_launch(1, 1, 12, 10, 64, None) == api.SDA_ERR_INVALID_ARG
 
