@@ -30,9 +30,11 @@
  *
  * Two entry points mirror the pages' step (one sequence) and batch (many
  * instances) entry points; both run the chunk pass, then the merge, on the
- * caller's stream.  The chunk size is a parameter of the method that
- * changes the result only by rounding; for small grids these fused calls run
- * finer chunks than the caller's (sda_fused_chunk_cells).
+ * caller's stream (or, when every instance has at most two chunks, one
+ * chunk-kernel launch that merges in place: sda_fused_single_launch).  The
+ * chunk size is a parameter of the method that changes the result only by
+ * rounding; these fused calls choose it from the grid
+ * (sda_fused_chunk_cells).
  *
  * Memory and threading contract (all entry points):
  *   - Every array argument is a DEVICE pointer unless marked "host".  The
@@ -45,7 +47,9 @@
  *   - Launch failures reported by the runtime return SDA_ERR_LAUNCH.
  *   - Device-side contents are trusted for shape (n_sel[i] is clamped to
  *     [0, max_sel]); ids out of range are masked, never dereferenced.
- *   - Calls on different streams that share a workspace race.
+ *   - Outputs (out, lse, gather_out, the workspace, and the pools of
+ *     sda_kv_append_batch) must not overlap any other argument's memory.
+ *   - Calls on different streams that share a workspace or an output race.
  */
 #ifndef SDA_H
 #define SDA_H
