@@ -145,3 +145,29 @@ def test_prompt_deterministic_and_graph_replay():
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {k}"
         check(y, out.cpu().numpy(), lse.cpu().numpy(), f"replay {k} pos0={p0}",
               t_ids=[0, 17, 39])
+
+
+@pytest.mark.parametrize("k", range(20))
+def test_prompt_random_geometry(k):
+    """Seeded sweep: instance, query and head counts, pool sizes, start
+    positions (some negative, some running past the page table) and masked
+    pages at random; sampled positions of every instance against the
+    oracle."""
+    rng = np.random.default_rng(9300 + k)
+    n_inst = int(rng.choice([1, 2, 3, 5]))
+    nh = int(rng.integers(1, 17))
+    n_q = int(rng.integers(1, 301))
+    pool_cells = int(rng.choice([256, 512, 1024, 2048]))
+    pos0 = rng.integers(-20, pool_cells + 20, size=n_inst).astype(np.int32)
+    say(f"case {k}: prompt n_inst={n_inst} n_q={n_q} n_qheads={nh} pool={pool_cells} "
+        f"pos0={pos0.tolist()}")
+    x = gen.make_prompt(None, seed=9400 + k, pos0=pos0, n_inst=n_inst, n_q=n_q, n_qheads=nh,
+                        pool_cells=pool_cells)
+    if rng.random() < 0.5:
+        pt = x.page_table.copy()
+        pt[rng.integers(0, n_inst, size=2), rng.integers(0, pt.shape[1], size=2)] = -1
+        x = dataclasses.replace(x, page_table=pt)
+    out, lse = run_prompt(x)
+    t_ids = sorted({0, n_q - 1, n_q // 2, int(rng.integers(0, n_q)), int(rng.integers(0, n_q))})
+    check(x, out, lse, f"case {k}", t_ids=t_ids)
+    assert np.isfinite(out).all()
