@@ -149,3 +149,27 @@ def test_append_then_prompt_attention():
     e1 = assert_close(out[0], ro, OUT_ATOL, OUT_RTOL, "append+prompt out")
     e2 = assert_close(lse[0], rl, LSE_ATOL, LSE_RTOL, "append+prompt lse")
     say(f"  append + prompt: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
+
+
+@pytest.mark.parametrize("k", range(15))
+def test_append_random_geometry(k):
+    """Seeded sweep: instance and row counts, pool sizes, start positions
+    (some negative, some past the table), masked pages and both scale
+    layouts; the whole pools against the oracle, bit for bit."""
+    rng = np.random.default_rng(9500 + k)
+    n_inst = int(rng.choice([1, 2, 3, 7]))
+    pool_cells = int(rng.choice([256, 512, 1024]))
+    n_new = int(rng.integers(1, 400))
+    pos0 = rng.integers(-30, pool_cells, size=n_inst).astype(np.int32)
+    stride = int(rng.choice([1, 2]))
+    say(f"case {k}: append n_inst={n_inst} n_new={n_new} pool={pool_cells} pos0={pos0.tolist()} "
+        f"stride={stride}")
+    x = special_rows(gen.make_append(None, seed=9600 + k, pos0=pos0, n_inst=n_inst, n_new=n_new,
+                                     pool_cells=pool_cells))
+    if rng.random() < 0.5:
+        pt = x.page_table.copy()
+        pt[rng.integers(0, n_inst), rng.integers(0, pt.shape[1])] = -1
+        pt[rng.integers(0, n_inst), rng.integers(0, pt.shape[1])] = 10**7
+        x = dataclasses.replace(x, page_table=pt)
+    pools = random_pools(9700 + k, x.n_inst, x.pool_cells, stride)
+    check_equal(run_append(pools, x, stride), oracle_append(pools, x, stride), f"case {k}")
