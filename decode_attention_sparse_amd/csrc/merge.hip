@@ -20,7 +20,6 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBatch = 8;  // accumulator rows in flight per wave
 
 __device__ __forceinline__ float wave_max_shfl(float x) {
 #pragma unroll
@@ -31,9 +30,12 @@ __device__ __forceinline__ float wave_max_shfl(float x) {
 // KW = waves that share one row's chunks.  KW = 4: workgroup = one (instance,
 // row), wave w takes chunks c = w (mod 4) (long merges).  KW = 1: workgroup =
 // four rows of one instance, one wave per row (short merges, where a row has
-// only a few chunks and splitting them would leave waves idle).
-template <int KW>
+// only a few chunks and splitting them would leave waves idle).  KB =
+// accumulator rows each wave requests at once (a row of up to KW * KB chunks
+// is one round trip); the chunk order of the sums does not depend on it.
+template <int KW, int KB>
 __global__ __launch_bounds__(256) void merge_kernel(Params p) {
+    constexpr int kBatch = KB;
     __shared__ v4f part_o[KW > 1 ? KW - 1 : 1][64];
     __shared__ float part_l[KW > 1 ? KW - 1 : 1];
     const int wave = threadIdx.x >> 6;
@@ -179,12 +181,17 @@ hipError_t launch_merge(const Params &p, hipStream_t s) {
         merge_few_kernel<4><<<dim3(p.n_inst, (p.n_rows + 15) / 16), dim3(256), 0, s>>>(p);
         return hipGetLastError();
     }
-    // rows with more chunks than one batch split them over four waves
-    if (p.n_chunks > kBatch) {
-        merge_kernel<4><<<dim3(p.n_inst, p.n_rows), dim3(256), 0, s>>>(p);
-    } else {
-        merge_kernel<1><<<dim3(p.n_inst, (p.n_rows + 3) / 4), dim3(256), 0, s>>>(p);
-    }
+    // rows with more than eight chunks split them over four waves, each
+    // requesting its share at once (up to 48 chunks in one round trip)
+    const dim3 long_grid(p.n_inst, p.n_rows);
+    if (p.n_chunks > 32)
+        merge_kernel<4, 12><<<long_grid, dim3(256), 0, s>>>(p);
+    else if (p.n_chunks > 16)
+        merge_kernel<4, 8><<<long_grid, dim3(256), 0, s>>>(p);
+    else if (p.n_chunks > 8)
+        merge_kernel<4, 4><<<long_grid, dim3(256), 0, s>>>(p);
+    else
+        merge_kernel<1, 8><<<dim3(p.n_inst, (p.n_rows + 3) / 4), dim3(256), 0, s>>>(p);
     return hipGetLastError();
 }
 
