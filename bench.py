@@ -42,6 +42,9 @@ HBM_PEAK_GBS = 8000.0
 # chunk + merge on RTX 2080 Ti (sm_75), attn_chunk_q8_v3_kernel, 2,051 cells (Strata PR #2220)
 PAGES_V3_US = {1: 34.5, 2: 41.0, 3: 73.0, 4: 84.9}
 PAGES_DEFAULT_US = {1: 51.6, 2: 78.5, 3: 110.0, 4: 145.6}
+# the same table's 600-cell rows (same page and setup)
+PAGES_600_V3_US = {1: 28.6, 2: 32.8, 3: 33.5, 4: 33.3}
+PAGES_600_DEFAULT_US = {1: 45.9, 2: 74.6, 3: 105.5, 4: 136.9}
 
 
 # HBM bytes per launch measured with two rocprofv3 counter runs (FETCH_SIZE,
@@ -609,6 +612,19 @@ def main(argv=None):
         }
         call_us_sum += call_ms * 1e3
         bytes_sum += c.bytes
+    # the pages' 600-cell rows: config 0's pool and list (600 cells) with
+    # 1-4 query positions, each call alone in a graph of K launches
+    x600 = inputs.make(0, n_q=4)
+    per_q600 = {}
+    for nq in (1, 2, 3, 4):
+        c6 = Case(x600.with_n_q(nq), x600.chunk)
+        g6 = graph_of(c6.call, a.steps)
+        us6 = time_graph(g6, a.steps) * 1e3
+        del g6, c6
+        per_q600[f"q{nq}"] = {"us_per_call": round(us6, 3),
+                              "cells_per_s": round(600 / (us6 * 1e-6), 1),
+                              "pages_2080ti_v3_us": PAGES_600_V3_US[nq],
+                              "pages_2080ti_default_us": PAGES_600_DEFAULT_US[nq]}
     cells_step = sum(c.cells for c in cases)
     value = cells_step / (step_ms * 1e-3)
     pages_step_us = sum(PAGES_V3_US.values())
@@ -656,6 +672,7 @@ def main(argv=None):
                              "kernel changed since they were taken",
                      "bytes_per_step": bytes_sum, "call_us_per_step": round(call_us_sum, 3)},
         "per_query_count": per_q,
+        "pages_600_cells_per_query_count": per_q600,
         "cold_us_per_call_median": cold_us,
         "cold_us_per_call_p10_p90": cold_spread,
         "cold_note": "200 eager calls per query count, caches evicted before each by reading a "
