@@ -58,15 +58,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "1e6861d34802cf0b392b2f5d9e14be53a67111c124a515d8552e364f58192d81", "fetch_bytes": 1972271, "write_bytes": 1634688},
+              "sources_sha256": "1e6861d34802cf0b392b2f5d9e14be53a67111c124a515d8552e364f58192d81", "fetch_bytes": 1972236, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "1e6861d34802cf0b392b2f5d9e14be53a67111c124a515d8552e364f58192d81", "fetch_bytes": 263908342, "write_bytes": 25264128},
+               "sources_sha256": "1e6861d34802cf0b392b2f5d9e14be53a67111c124a515d8552e364f58192d81", "fetch_bytes": 263746301, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268718044, "write_bytes": 68157483},
+               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268719495, "write_bytes": 68157525},
 }
 
 
