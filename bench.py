@@ -58,15 +58,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "1e6861d34802cf0b392b2f5d9e14be53a67111c124a515d8552e364f58192d81", "fetch_bytes": 1972236, "write_bytes": 1634688},
+              "sources_sha256": "cdf6c660206dd958d8ba9c1dcc9f74efc5aca5a4e2987c033273d431f9e25eda", "fetch_bytes": 4339492, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "1e6861d34802cf0b392b2f5d9e14be53a67111c124a515d8552e364f58192d81", "fetch_bytes": 263746301, "write_bytes": 25264128},
+               "sources_sha256": "cdf6c660206dd958d8ba9c1dcc9f74efc5aca5a4e2987c033273d431f9e25eda", "fetch_bytes": 263853891, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268719495, "write_bytes": 68157525},
+               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268720093, "write_bytes": 68157483},
 }
 
 
@@ -664,7 +664,8 @@ def main(argv=None):
                      "kernel": f"{'chunk_tile_kernel' if c4.fused_chunk == 64 else 'chunk_mfma_kernel'}"
                                f", the n_q = 4 call of the step "
                                f"({c4.fused_chunk}-cell chunks: "
-                               f"{-(-c4.max_sel // c4.fused_chunk)} workgroups)",
+                               f"{-(-c4.max_sel // c4.fused_chunk)} chunks, one workgroup per "
+                               f"chunk and 16-row group)",
                      "algorithmic_bytes_per_launch": c4.chunk_bytes,
                      "launch_us_mean": k4_us,
                      "note": "latency-bound: one instance, 2,051 cells; "

@@ -793,8 +793,8 @@ constexpr int kPtLdsPages = 2048;  // page tables up to this size are staged who
 // LDS read: two dependent round trips to memory instead of three.  LDS
 // layout as in the pipelined kernel (row r = tile cell r, padded rows;
 // scales and bias by cell).
-__device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j_end, int lane,
-                                           int8_t *kb, int8_t *vb, float *ks, float *vs,
+__device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out, int i, int j0,
+                                           int j_end, int lane, int8_t *kb, int8_t *vb, float *ks, float *vs,
                                            float *bias, int *pt_s) {
     const int g = lane >> 4, l16 = lane & 15;
     const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
@@ -847,7 +847,7 @@ __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j
     }
     int ph = -1;
     if (id_ok && pte >= 0 && (int64_t)pte < p.n_phys_pages) ph = (pte << 4) | (c & 15);
-    if (p.gather_out && j < j_end) p.gather_out[(int64_t)i * p.sel_stride + j] = ph;
+    if (gather_out && j < j_end) gather_out[(int64_t)i * p.sel_stride + j] = ph;
     const int64_t sc = (int64_t)(ph < 0 ? 0 : ph) * p.scale_stride;
     const unsigned kh = p.k_scales[sc];
     const unsigned vh = p.v_scales[sc];
@@ -881,12 +881,14 @@ __device__ __forceinline__ void stage_tile(const Params &p, int i, int j0, int j
         }
 }
 
-// Chunks of one tile (64 cells) in a latency-bound grid: workgroup = one
-// (instance, chunk), DS * RB compute waves and one producer wave that stages
-// the tile in three round trips (the pipelined kernel takes five steps for
-// one tile).  The compute waves then run the same two steps the pipelined
-// kernel runs for a one-tile chunk (the scores, then the softmax and V
-// accumulation), so the partial is bit for bit the same.
+// Chunks of one tile (64 cells) in a latency-bound grid: workgroup =
+// (instance, chunk, blockIdx.z), holding the 16 RB query rows from row
+// 16 RB blockIdx.z on, with DS * RB compute waves and one producer wave
+// that stages the tile in three round trips (the pipelined kernel takes five
+// steps for one tile).  The compute waves then run the same two steps the
+// pipelined kernel runs for a one-tile chunk (the scores, then the softmax
+// and V accumulation), so the partial is bit for bit the same whichever
+// workgroup holds a row.
 template <int RB, int DS>
 __global__ __launch_bounds__(64 * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu(2, 2)))  // at most 256 registers: no AGPR copies
@@ -910,13 +912,14 @@ void chunk_tile_kernel(Params p) {
     const int j_end = min(j_begin + kTile, n);
 
     if (wave == kProducer) {
-        stage_tile(p, i, j_begin, j_end, lane, kbuf, vbuf, ks_s, vs_s, bias_s,
-                   p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
+        // every row group's workgroup stages the tile; one writes gather_out
+        stage_tile(p, blockIdx.z == 0 ? p.gather_out : nullptr, i, j_begin, j_end, lane, kbuf,
+                   vbuf, ks_s, vs_s, bias_s, p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
         __syncthreads();
         return;
     }
     const int g = lane >> 4, l16 = lane & 15;
-    const int row = (wave / DS) * 16 + l16;
+    const int row = ((int)blockIdx.z * RB + wave / DS) * 16 + l16;
     const int dh = wave % DS;
     const int R = p.n_rows;
     RowBlock<kDB> rb;
@@ -942,9 +945,18 @@ void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
 hipError_t launch_chunk(const Params &p, hipStream_t s) {
     const int64_t items = (int64_t)p.n_inst * p.n_chunks;
     // one-tile chunks in a grid of at most one workgroup per CU: stage the
-    // tile at once (a single 16-row group splits its V accumulation over two
-    // waves; with more groups that measured slower)
+    // tile at once.  While the grid still fits one workgroup per CU with a
+    // workgroup per 16-row group, each row group gets its own (its V
+    // accumulation split over two waves): the tile's compute then takes the
+    // time of one group's, and the extra stagings of the tile are L2 hits.
+    // Otherwise all groups share one workgroup (a single group still splits
+    // its V accumulation; with more groups that measured slower).
     if (p.chunk == kTile && items <= kLatencyWorkgroups) {
+        const int groups = (p.n_rows + 15) / 16;
+        if (groups > 1 && items * groups <= kLatencyWorkgroups) {
+            chunk_tile_kernel<1, 2><<<dim3(p.n_inst, p.n_chunks, groups), 64 * 3, 0, s>>>(p);
+            return hipGetLastError();
+        }
         const dim3 grid(p.n_inst, p.n_chunks);
         switch ((p.n_rows + 15) / 16) {
             case 1: chunk_tile_kernel<1, 2><<<grid, 64 * 3, 0, s>>>(p); break;

@@ -161,21 +161,27 @@ def test_edge_counts_large_grid(n_q):
 def test_batch_size_independence(n_q):
     """The chunk pass and merge at a given chunk size do not depend on the
     batch: the same instances run in a small grid and in larger ones (which
-    the library launches differently: one-tile workgroups and the V
-    accumulation split over two waves per row group in small grids, several
-    chunks per workgroup in large ones); every instance gets the same
-    arithmetic in the same order, so outputs and gather indices agree bit
-    for bit.  The fused call chooses its chunk size from the grid
+    the library launches differently: one-tile workgroups, one per 16-row
+    group in the smallest grids and one per (instance, chunk) above that,
+    the V accumulation split over two waves per row group in small grids,
+    several chunks per workgroup in large ones); every instance gets the
+    same arithmetic in the same order, so outputs and gather indices agree
+    bit for bit.  The fused call chooses its chunk size from the grid
     (sda_fused_chunk_cells), so it is checked against the oracle."""
     say(f"case: batch-size independence, n_q={n_q}")
     spec = dict(n_q=n_q, pool_cells=2048, n_sel=600, sel="uniform", chunk=64)
+    tiny = gen.make(None, seed=123, n_inst=5, **spec)     # 5 x 10 chunks: a workgroup per row group
     small = gen.make(None, seed=123, n_inst=20, **spec)   # 20 x 10 chunks
     large = gen.make(None, seed=123, n_inst=30, **spec)   # 30 x 10 chunks
     huge = gen.make(None, seed=123, n_inst=120, **spec)   # 120 x 10: two chunks per workgroup
     assert np.array_equal(small.sel, large.sel[:20]) and np.array_equal(small.q, large.q[:20])
+    assert np.array_equal(tiny.sel, small.sel[:5]) and np.array_equal(tiny.q, small.q[:5])
+    o0, l0, g0, _ = two_pass(tiny, 64)
     o1, l1, g1, _ = two_pass(small, 64)
     o2, l2, g2, _ = two_pass(large, 64)
     o3, l3, g3, _ = two_pass(huge, 64)
+    assert np.array_equal(o0, o1[:5]) and np.array_equal(l0, l1[:5])
+    assert np.array_equal(g0, g1[:5])
     for o, l, g_ in ((o2, l2, g2), (o3, l3, g3)):
         assert np.array_equal(o1, o[:20]) and np.array_equal(l1, l[:20])
         assert np.array_equal(g1, g_[:20])
