@@ -229,12 +229,37 @@ struct RowBlock {
     // the next tile (K rows kb, K scales ks, bias 0 or -inf per cell) into su,
     // or -inf everywhere when next_ok is false.  kCausal: cells of the next
     // tile past index lim (this lane's row's last visible cell, counted from
-    // the tile's first cell) are masked too.
+    // the tile's first cell) are masked too.  The two halves are independent
+    // (score() and stats() + accumulate()); a one-tile chunk runs them one
+    // after the other (tile()), with the same arithmetic.
     template <bool kCausal = false>
     __device__ __forceinline__ void step(const int8_t *kb, const float *ks_t, const float *bias_t,
                                          bool next_ok, const int8_t *vb, const float *vs_t,
                                          int dh, int lim = 0) {
-        // ---------------- softmax statistics of the current tile (scores in su)
+        const Stats st = stats();
+        v4f sn[4];
+        score<kCausal>(sn, kb, ks_t, bias_t, next_ok, lim);
+        accumulate(st, vb, vs_t, dh);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
+    }
+
+    // A whole one-tile chunk: its scores, then their softmax and V
+    // accumulation.  The same state as step() on the tile followed by step()
+    // with next_ok false, without the halves that change nothing (the softmax
+    // of the initial -inf scores, the scores of a tile past the end).
+    __device__ __forceinline__ void tile(const int8_t *kb, const float *ks_t, const float *bias_t,
+                                         const int8_t *vb, const float *vs_t, int dh) {
+        score(su, kb, ks_t, bias_t, true);
+        accumulate(stats(), vb, vs_t, dh);
+    }
+
+    // Softmax statistics of the tile whose scores are in su: the running max
+    // moves to include it; the frame and the reference max it implies.
+    struct Stats {
+        float m_use, corr, frame_new;
+    };
+    __device__ __forceinline__ Stats stats() {
         float tmax = -INFINITY;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
@@ -243,13 +268,19 @@ struct RowBlock {
         tmax = max4(tmax);
         tmax = (tmax == -INFINITY) ? -INFINITY : tmax * coef;  // base-2 tile max
         const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-        const float frame_new = (m_run == -INFINITY) ? 1.f : frame * corr;
+        Stats st;
+        st.m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        st.corr = __builtin_amdgcn_exp2f(m_run - st.m_use);
+        st.frame_new = (m_run == -INFINITY) ? 1.f : frame * st.corr;
         m_run = m_new;
+        return st;
+    }
 
-        // ---------------- scores of the next tile: u = (AB + C/2^8) * k_scale + bias
-        v4f sn[4];
+    // Scores of a tile: u = (AB + C/2^8) * k_scale + bias, into sn (-inf
+    // everywhere when next_ok is false; kCausal and lim as in step()).
+    template <bool kCausal = false>
+    __device__ __forceinline__ void score(v4f (&sn)[4], const int8_t *kb, const float *ks_t,
+                                          const float *bias_t, bool next_ok, int lim = 0) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
@@ -285,6 +316,13 @@ struct RowBlock {
             }
         }
 
+    }
+
+    // Softmax and V accumulation of the tile whose scores are in su (its
+    // statistics st from stats()): probabilities, their digits, O^T += V^T P^T.
+    __device__ __forceinline__ void accumulate(const Stats &st, const int8_t *vb,
+                                               const float *vs_t, int dh) {
+        const float m_use = st.m_use, corr = st.corr, frame_new = st.frame_new;
         // ---------------- probabilities and their digits for the current tile
         // weights w = p * v_scale; W = 256 / tau = 32512 / (row max of w), and
         // X = rint(w * W) lands in the low bits of fma(w, W, 2^23)
@@ -321,8 +359,6 @@ struct RowBlock {
             xb[cb] = (int)(lo01 | lo23);
         }
         l_part = fmaf(l_part, corr, psum);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
 
         // rare: fold the frame into the accumulator before it gets too small
         frame = frame_new;
@@ -885,10 +921,10 @@ __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out,
 // (instance, chunk, blockIdx.z), holding the 16 RB query rows from row
 // 16 RB blockIdx.z on, with DS * RB compute waves and one producer wave
 // that stages the tile in three round trips (the pipelined kernel takes five
-// steps for one tile).  The compute waves then run the same two steps the
-// pipelined kernel runs for a one-tile chunk (the scores, then the softmax
-// and V accumulation), so the partial is bit for bit the same whichever
-// workgroup holds a row.
+// steps for one tile).  The compute waves then score the tile and run its
+// softmax and V accumulation (RowBlock::tile: the arithmetic the pipelined
+// kernel applies to a one-tile chunk), so the partial is bit for bit the
+// same whichever kernel or workgroup holds a row.
 template <int RB, int DS>
 __global__ __launch_bounds__(64 * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu(2, 2)))  // at most 256 registers: no AGPR copies
@@ -925,8 +961,7 @@ void chunk_tile_kernel(Params p) {
     RowBlock<kDB> rb;
     rb.init(p.q + ((int64_t)i * R + (row < R ? row : 0)) * kDim, row < R, p.scale_log2, g, l16);
     __syncthreads();
-    rb.step(kbuf, ks_s, bias_s, true, vbuf, vs_s, dh);   // scores of the tile
-    rb.step(kbuf, ks_s, bias_s, false, vbuf, vs_s, dh);  // its softmax and V
+    rb.tile(kbuf, ks_s, bias_s, vbuf, vs_s, dh);
     rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
 }
 
