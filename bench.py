@@ -58,15 +58,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "25cd1f7ac3ae791bef1ba54c64d33a46226f15f90aed1d3e62cb35a19db2d2f5", "fetch_bytes": 4299526, "write_bytes": 1634688},
+              "sources_sha256": "1a365f3b22a85788f31827478b06bfb36f8eb3b2d82940059889891bac6dd303", "fetch_bytes": 4299511, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "25cd1f7ac3ae791bef1ba54c64d33a46226f15f90aed1d3e62cb35a19db2d2f5", "fetch_bytes": 264057771, "write_bytes": 25264128},
+               "sources_sha256": "1a365f3b22a85788f31827478b06bfb36f8eb3b2d82940059889891bac6dd303", "fetch_bytes": 264129920, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268718556, "write_bytes": 68157483},
+               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268718086, "write_bytes": 68157504},
 }
 
 

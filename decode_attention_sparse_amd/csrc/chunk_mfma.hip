@@ -282,28 +282,7 @@ struct RowBlock {
     __device__ __forceinline__ void score(v4f (&sn)[4], const int8_t *kb, const float *ks_t,
                                           const float *bias_t, bool next_ok, int lim = 0) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
-            v4i ka[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
-            v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                aa = mfma_i8(ka[s], qa[s], aa);
-                bb = mfma_i8(ka[s], qb[s], bb);
-                cc = mfma_i8(ka[s], qc[s], cc);
-            }
-            const v4i ab = (aa << 8) + bb;  // 2^8 A + B, |.| < 2^30
-            const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
-            const v4f ks = *reinterpret_cast<const v4f *>(ks_t + mo);
-            const v4f bs = *reinterpret_cast<const v4f *>(bias_t + mo);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
-                sn[cb][u] = next_ok ? fmaf(tq, ks[u], bs[u]) : -INFINITY;
-            }
-        }
+        for (int cb = 0; cb < 4; ++cb) sn[cb] = score_block(cb, kb, ks_t, bias_t, next_ok);
         if constexpr (kCausal) {
             if (__any(lim < kTile - 1)) {  // only tiles that reach past some row's position
 #pragma unroll
@@ -316,6 +295,55 @@ struct RowBlock {
             }
         }
 
+    }
+
+    // The scores of this lane's 4 cells of cell block cb (cells 16 cb to
+    // 16 cb + 15 of the tile), -inf when next_ok is false.
+    __device__ __forceinline__ v4f score_block(int cb, const int8_t *kb, const float *ks_t,
+                                               const float *bias_t, bool next_ok) {
+        const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
+        v4i ka[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
+        v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            aa = mfma_i8(ka[s], qa[s], aa);
+            bb = mfma_i8(ka[s], qb[s], bb);
+            cc = mfma_i8(ka[s], qc[s], cc);
+        }
+        const v4i ab = (aa << 8) + bb;  // 2^8 A + B, |.| < 2^30
+        const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
+        const v4f ks = *reinterpret_cast<const v4f *>(ks_t + mo);
+        const v4f bs = *reinterpret_cast<const v4f *>(bias_t + mo);
+        v4f sn;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
+            sn[u] = next_ok ? fmaf(tq, ks[u], bs[u]) : -INFINITY;
+        }
+        return sn;
+    }
+
+    // tile() with the scoring shared by the DS waves that hold the same 16
+    // rows: wave dh scores cell blocks (4 / DS) dh to (4 / DS) (dh + 1) - 1
+    // and the blocks meet in LDS (xs: 4 blocks x 64 lanes for this row
+    // group), so every wave goes on with the scores tile() computes, bit for
+    // bit.  Contains a workgroup barrier that every wave must reach.
+    template <int DS>
+    __device__ __forceinline__ void tile_shared(const int8_t *kb, const float *ks_t,
+                                                const float *bias_t, const int8_t *vb,
+                                                const float *vs_t, int dh, v4f *xs, int lane) {
+        constexpr int kPer = 4 / DS;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int cb = kPer * dh + k;
+            xs[64 * cb + lane] = score_block(cb, kb, ks_t, bias_t, true);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) su[cb] = xs[64 * cb + lane];
+        accumulate(stats(), vb, vs_t, dh);
     }
 
     // Softmax and V accumulation of the tile whose scores are in su (its
@@ -923,14 +951,18 @@ __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out,
 // that stages the tile in three round trips (the pipelined kernel takes five
 // steps for one tile).  The compute waves then score the tile and run its
 // softmax and V accumulation (RowBlock::tile: the arithmetic the pipelined
-// kernel applies to a one-tile chunk), so the partial is bit for bit the
-// same whichever kernel or workgroup holds a row.
+// kernel applies to a one-tile chunk; with DS = 2 the two waves of a row
+// group each score half the cell blocks and exchange them in LDS,
+// RowBlock::tile_shared), so the partial is bit for bit the same whichever
+// kernel or workgroup holds a row.
 template <int RB, int DS>
 __global__ __launch_bounds__(64 * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu(2, 2)))  // at most 256 registers: no AGPR copies
 void chunk_tile_kernel(Params p) {
     constexpr int kProducer = DS * RB;
     constexpr int kDB = 16 / DS;
+    constexpr bool kShared = DS > 1;  // the DS waves of a row group share its scoring
+    __shared__ __attribute__((aligned(16))) v4f xs[kShared ? RB * 4 * 64 : 1];
     __shared__ __attribute__((aligned(1024))) int8_t kbuf[kBuf];
     __shared__ __attribute__((aligned(1024))) int8_t vbuf[kBuf];
     __shared__ __attribute__((aligned(16))) float ks_s[kTile];
@@ -952,6 +984,7 @@ void chunk_tile_kernel(Params p) {
         stage_tile(p, blockIdx.z == 0 ? p.gather_out : nullptr, i, j_begin, j_end, lane, kbuf,
                    vbuf, ks_s, vs_s, bias_s, p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
         __syncthreads();
+        if constexpr (kShared) __syncthreads();  // the compute waves' score exchange
         return;
     }
     const int g = lane >> 4, l16 = lane & 15;
@@ -961,7 +994,12 @@ void chunk_tile_kernel(Params p) {
     RowBlock<kDB> rb;
     rb.init(p.q + ((int64_t)i * R + (row < R ? row : 0)) * kDim, row < R, p.scale_log2, g, l16);
     __syncthreads();
-    rb.tile(kbuf, ks_s, bias_s, vbuf, vs_s, dh);
+    if constexpr (kShared)
+        rb.template tile_shared<DS>(kbuf, ks_s, bias_s, vbuf, vs_s,
+                                    __builtin_amdgcn_readfirstlane(dh),
+                                    xs + 256 * (wave / DS), lane);
+    else
+        rb.tile(kbuf, ks_s, bias_s, vbuf, vs_s, dh);
     rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
 }
 
