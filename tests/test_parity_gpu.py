@@ -190,6 +190,30 @@ def test_batch_size_independence(n_q):
     check(huge, o4, l4, g4, inst_ids=[0, 19, 77, 119], what="fused call, batch of 120")
 
 
+@pytest.mark.parametrize("n_q,n_qheads", [(1, 12), (1, 17), (2, 12), (1, 33), (4, 12), (4, 16)])
+def test_single_tile_forms_bitwise(n_q, n_qheads):
+    """One-tile chunks run in three forms, chosen by the grid: a workgroup
+    per (instance, chunk, 16-row group) in the smallest grids, all row
+    groups in one workgroup up to one workgroup per CU, and the pipelined
+    kernel beyond; with a single 16-row group its two waves share the
+    scoring through LDS.  The same instances through each form give the
+    same outputs, log-sum-exps and gather indices bit for bit (row counts
+    12 to 64, one to four row groups), and the smallest grid matches the
+    oracle."""
+    say(f"case: single-tile forms, n_q={n_q}, n_qheads={n_qheads}")
+    spec = dict(n_q=n_q, n_qheads=n_qheads, pool_cells=1024, n_sel=600, sel="uniform", chunk=64)
+    res = []
+    for n_inst in (2, 25, 60):  # 20, 250 and 600 (instance, chunk) pairs
+        x = gen.make(None, seed=311, n_inst=n_inst, **spec)
+        res.append((x, two_pass(x, 64)))
+    x0, (o0, l0, g0, _) = res[0]
+    for x, (o, l, g_, _) in res[1:]:
+        assert np.array_equal(x0.sel, x.sel[:2]) and np.array_equal(x0.q, x.q[:2])
+        assert np.array_equal(o0, o[:2]) and np.array_equal(l0, l[:2])
+        assert np.array_equal(g0, g_[:2])
+    check(x0, o0, l0, g0, what=f"single-tile forms R={n_q * n_qheads}")
+
+
 def test_many_instances_coarse_chunks():
     """More than 256 instances and 512 (instance, chunk) pairs: the fused
     call takes chunks k times the caller's (300 x 600 cells at chunk 64:
