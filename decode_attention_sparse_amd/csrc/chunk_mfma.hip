@@ -25,7 +25,9 @@
 //                                              workgroup, merged in LDS;
 //   chunk_tile_kernel<RB, DS>                  one-tile chunks in latency-
 //                                              bound grids (the tile staged
-//                                              at once, no pipeline);
+//                                              at once, no pipeline; a
+//                                              workgroup per 16-row group
+//                                              in the smallest grids);
 //   chunk_mfma_kernel<RB, 1, true>             prompt attention: the
 //                                              pipelined pass over an
 //                                              implicit causal cell list.
@@ -158,35 +160,45 @@ struct RowBlock {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (!valid) qv[s][w] = (v4f){0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < 4; ++w)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fabsf(qv[s][w][u]));
-            }
-        mx = wave_max(mx);
-        const float inv = mx > 0.f ? (scale_log2 < 0.f ? -65536.f : 65536.f) * 127.f / mx : 0.f;
+        // a row past the end counts as zeros: out of the maximum, and its
+        // digits come out 0 (its values are multiplied by 0)
+        mx = wave_max(valid ? mx : 0.f);
+        const float inv_row =
+            mx > 0.f ? (scale_log2 < 0.f ? -65536.f : 65536.f) * 127.f / mx : 0.f;
+        const float inv = valid ? inv_row : 0.f;
         // clamped away from 0 so that masked cells (-inf) never meet a zero factor
         coef = fmaxf((mx / 127.f) * fabsf(scale_log2) * (1.f / 256.f), 1e-30f);
+        // X = round(q * 127 * 2^16 / max) = 2^16 a + 2^8 b + c with balanced
+        // digits b, c in [-128, 127] (a in [-127, 127]).  Then X + 2^7 =
+        // 2^8 (2^8 a + b) + (c + 2^7) and X + 2^7 + 2^15 = 2^16 a + 2^8 (b +
+        // 2^7) + (c + 2^7) with the added digits in [0, 255], so the two's
+        // complement bytes are c = byte 0 of X, b = byte 1 of X + 2^7 and
+        // a = byte 2 of X + 2^7 + 2^15; each operand gathers one such byte
+        // of four values (byte permutes).
+        auto gather = [](const unsigned (&v)[4], unsigned byte) {
+            const unsigned sel = 0x0c0c0400u + byte * 0x0101u;  // bytes 0, 1: v[0], v[1]
+            const unsigned lo = __builtin_amdgcn_perm(v[1], v[0], sel);
+            const unsigned hi = __builtin_amdgcn_perm(v[3], v[2], sel);
+            return (int)__builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        };
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                unsigned pa = 0, pb = 0, pc = 0;
+                unsigned x0[4], x1[4], x2[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    // X = round(q * 127 * 2^16 / max) = 2^16 a + 2^8 b + c, balanced digits
                     const int X = (int)rintf(qv[s][w][u] * inv);
-                    const int dc = __builtin_amdgcn_sbfe(X, 0, 8);
-                    const int X1 = (X - dc) >> 8;
-                    const int db = __builtin_amdgcn_sbfe(X1, 0, 8);
-                    const int da = (X1 - db) >> 8;
-                    pa |= ((unsigned)da & 0xffu) << (8 * u);
-                    pb |= ((unsigned)db & 0xffu) << (8 * u);
-                    pc |= ((unsigned)dc & 0xffu) << (8 * u);
+                    x0[u] = (unsigned)X;
+                    x1[u] = (unsigned)(X + 128);
+                    x2[u] = (unsigned)(X + 32896);
                 }
-                qa[s][w] = (int)pa;
-                qb[s][w] = (int)pb;
-                qc[s][w] = (int)pc;
+                qc[s][w] = gather(x0, 0);
+                qb[s][w] = gather(x1, 1);
+                qa[s][w] = gather(x2, 2);
             }
         }
         // per-lane constant LDS offsets (everything else is an immediate):
