@@ -58,15 +58,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "09f757ef4da2ea20a3bfad3142a79a425a69133ff6a2f946ceab5676696774fa", "fetch_bytes": 4279070, "write_bytes": 1634688},
+              "sources_sha256": "8705f870d0904da04554e32ff709032bd403bd91c3fa6981994f14b032e3d010", "fetch_bytes": 4279070, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "09f757ef4da2ea20a3bfad3142a79a425a69133ff6a2f946ceab5676696774fa", "fetch_bytes": 264324063, "write_bytes": 25264128},
+               "sources_sha256": "8705f870d0904da04554e32ff709032bd403bd91c3fa6981994f14b032e3d010", "fetch_bytes": 264170527, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "43bb9df7e9f9ee46465b8cffa2c81e94c016552439a735ff7e2be4bac94996fb", "fetch_bytes": 268719025, "write_bytes": 68157504},
+               "sources_sha256": "9dad7d37f1db1233e70e4626887f6203ce8a3bb17de5189587b1926ba830641c", "fetch_bytes": 268718598, "write_bytes": 68157515},
 }
 
 

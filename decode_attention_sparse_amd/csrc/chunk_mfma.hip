@@ -91,35 +91,13 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 (one query row), with the
-// gfx950 lane swaps (VALU, no LDS round trip).
-__device__ __forceinline__ float max4(float x) {
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
+// Sum over the four lanes l, l^16, l^32, l^48 (one query row), with the
+// gfx950 lane swaps (VALU, no LDS round trip); max4 is its maximum.
 __device__ __forceinline__ float sum4(float x) {
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Maximum over all 64 lanes: quad permutes, half-row and row mirrors (DPP),
-// then the 16- and 32-lane swaps.
-__device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, dpp<0xb1>(x));   // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp<0x4e>(x));   // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
-    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
-    return max4(x);
 }
 
 // LDS row of the QK operand index 16*cb + l: a permutation within the tile

@@ -24,29 +24,11 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Maximum over the 64 lanes (quad permutes, half-row and row mirrors, then
-// the 16- and 32-lane swaps).
-__device__ __forceinline__ float wave_max64(float x) {
-    x = fmaxf(x, dpp_f<0xb1>(x));
-    x = fmaxf(x, dpp_f<0x4e>(x));
-    x = fmaxf(x, dpp_f<0x141>(x));
-    x = fmaxf(x, dpp_f<0x140>(x));
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 // Quantises this lane's four values of one row; returns the packed codes and
 // sets the scale's binary16 bits.
 __device__ __forceinline__ uint32_t quantise4(v4f x, uint16_t *scale_bits) {
     float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-    amax = wave_max64(amax);
+    amax = wave_max(amax);  // over the row's 64 lanes
     const float s32 = fminf(amax / 127.0f, 65504.0f);
     const _Float16 s16 = (_Float16)s32;  // round to nearest even
     const float s = (float)s16;

@@ -21,12 +21,6 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 
-__device__ __forceinline__ float wave_max_shfl(float x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
-    return x;
-}
-
 // KW = waves that share one row's chunks.  KW = 4: workgroup = one (instance,
 // row), wave w takes chunks c = w (mod 4) (long merges).  KW = 1: workgroup =
 // four rows of one instance, one wave per row (short merges, where a row has
@@ -72,7 +66,7 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p) {
     if (share < nch) {
         load_batch(share);  // in flight while the maximum is formed
         for (int c = lane; c < nch; c += 64) M = fmaxf(M, p.m[row0 + (int64_t)c * R]);
-        M = wave_max_shfl(M);
+        M = wave_max(M);
         for (int c0 = share;;) {
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {

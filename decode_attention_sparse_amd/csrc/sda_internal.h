@@ -64,6 +64,30 @@ __device__ __forceinline__ float merge_weight(float mc, float M) {
     return mc == -INFINITY ? 0.f : expf(mc - M);
 }
 
+// Maximum over the four lanes l, l^16, l^32, l^48 (one query row of an
+// MFMA output), with the gfx950 lane swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float max4(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Maximum over all 64 lanes: quad permutes, half-row and row mirrors (DPP),
+// then the 16- and 32-lane swaps (no LDS round trip).
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<0xb1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4e>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return max4(x);
+}
+
 typedef float merge_v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ merge_v4f merge_acc(merge_v4f o, float w, merge_v4f a) {
