@@ -58,15 +58,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "8705f870d0904da04554e32ff709032bd403bd91c3fa6981994f14b032e3d010", "fetch_bytes": 4279070, "write_bytes": 1634688},
+              "sources_sha256": "1307d54235bc221be6be74ab86cc541c35b822ee49b2c3b00258fce2015d61ce", "fetch_bytes": 4279100, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "8705f870d0904da04554e32ff709032bd403bd91c3fa6981994f14b032e3d010", "fetch_bytes": 264170527, "write_bytes": 25264128},
+               "sources_sha256": "1307d54235bc221be6be74ab86cc541c35b822ee49b2c3b00258fce2015d61ce", "fetch_bytes": 264120861, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "9dad7d37f1db1233e70e4626887f6203ce8a3bb17de5189587b1926ba830641c", "fetch_bytes": 268718598, "write_bytes": 68157515},
+               "sources_sha256": "0dde29e316c02f7693a39855cfc63bde501a858e30f4f8969b7d24a002d2b566", "fetch_bytes": 268718385, "write_bytes": 68157472},
 }
 
 
