@@ -53,30 +53,38 @@ PAGES_600_DEFAULT_US = {1: 45.9, 2: 74.6, 3: 105.5, 4: 136.9}
 # WRITE_SIZE x 1.0): the headline chunk kernel (n_q = 4), the prompt kernel
 # and the KV append kernel.  The summaries with the commands are under
 # profiles/.  A figure holds only for the kernel sources it was taken on
-# (their SHA-256); a changed source reports null.
+# (the SHA-256 of their code, comments left out); a changed source reports
+# null.
 MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "1307d54235bc221be6be74ab86cc541c35b822ee49b2c3b00258fce2015d61ce", "fetch_bytes": 4279100, "write_bytes": 1634688},
+              "sources_sha256": "5075d4b4b8ee0e5d27737b22d568399fc542de9d29bc749b7e5f96458365c338", "fetch_bytes": 4279100, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "1307d54235bc221be6be74ab86cc541c35b822ee49b2c3b00258fce2015d61ce", "fetch_bytes": 264120861, "write_bytes": 25264128},
+               "sources_sha256": "5075d4b4b8ee0e5d27737b22d568399fc542de9d29bc749b7e5f96458365c338", "fetch_bytes": 264120861, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "0dde29e316c02f7693a39855cfc63bde501a858e30f4f8969b7d24a002d2b566", "fetch_bytes": 268718385, "write_bytes": 68157472},
+               "sources_sha256": "d5d07849bfcb217d37d5c658e92df99d7d050d612ce35dc00f09883bebb974a8", "fetch_bytes": 268718385, "write_bytes": 68157472},
 }
 
 
 def sources_sha256(files) -> str:
+    """SHA-256 of the sources' code: comments removed and white space
+    collapsed, so that editing a comment keeps a measurement valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     root = os.path.dirname(os.path.abspath(__file__))
     for f in files:
-        with open(os.path.join(root, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(root, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

@@ -56,8 +56,9 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
 // The log-sum-exp merge of a row's chunk partials (m_c, l_c, acc_c), as every
 // merge in the library runs it, chunk by chunk in chunk order:
 //   M = max_c m_c (from -inf),  w_c = e^(m_c - M) (0 for an empty chunk;
-//   computed as 2^((m_c - M) log2 e) with the hardware exp2, whose error,
-//   with the rounding of the product, is a few units in the last place),
+//   computed as 2^((m_c - M) log2 e) with the hardware exp2: with the
+//   roundings of the difference and the product, relative error below
+//   (1 + |m_c - M|) 2^-23, and weights far below 1 where that grows),
 //   L = fma(l_c, w_c, L),  o = fma(w_c, acc_c, o) element by element (from 0),
 //   out = o * (1 / L),  lse = M + ln L  (L = 0: out = 0, lse = -inf).
 // The explicit fmas fix the rounding, so the merge kernels and the chunk
