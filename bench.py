@@ -59,15 +59,15 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "5075d4b4b8ee0e5d27737b22d568399fc542de9d29bc749b7e5f96458365c338", "fetch_bytes": 4279100, "write_bytes": 1634688},
+              "sources_sha256": "5435c9c410341dae1094edbb9b13fa06c0d9fced2e13c69cbfb9c9789276c28e", "fetch_bytes": 4279045, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "5075d4b4b8ee0e5d27737b22d568399fc542de9d29bc749b7e5f96458365c338", "fetch_bytes": 264120861, "write_bytes": 25264128},
+               "sources_sha256": "5435c9c410341dae1094edbb9b13fa06c0d9fced2e13c69cbfb9c9789276c28e", "fetch_bytes": 262947267, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "d5d07849bfcb217d37d5c658e92df99d7d050d612ce35dc00f09883bebb974a8", "fetch_bytes": 268718385, "write_bytes": 68157472},
+               "sources_sha256": "d5d07849bfcb217d37d5c658e92df99d7d050d612ce35dc00f09883bebb974a8", "fetch_bytes": 268718685, "write_bytes": 68157515},
 }
 
 

@@ -59,7 +59,8 @@
 // scales and K rows of tile t+2, V rows of tile t+1.  Code rows (256 B) are
 // loaded into VGPRs with 16-byte loads (16 lanes per row) and written to LDS
 // rows padded to 272 B, double-buffered; the padding and a row permutation
-// make the LDS reads conflict-free with immediate offsets.  K rows feed
+// (lds_row) spread the K and the transposed V reads over the 64 LDS banks,
+// with immediate offsets.  K rows feed
 // S^T = K Q^T through ds_read_b128; V rows are read transposed with
 // ds_read_b64_tr_b8 to feed O^T = V^T P^T.
 //
@@ -101,9 +102,14 @@ __device__ __forceinline__ float sum4(float x) {
 }
 
 // LDS row of the QK operand index 16*cb + l: a permutation within the tile
-// chosen so that the K reads (8 lanes) and the transposed V reads (8 rows per
-// 16 lanes) each touch 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (4 * (cb & 1))); }
+// (odd cell blocks exchange their two halves of 8 rows) laid out for 64 LDS
+// banks of 4 bytes.  With 272-byte rows a row starts 4 banks after the
+// previous one, so rows 16 apart share banks: the 16 lanes of a K read take
+// 16 consecutive rows (distinct), and the 32 lanes of a transposed V read,
+// which take rows from an even and an odd cell block, get rows that differ
+// modulo 16.  (Exchanging groups of 4 instead, the layout for 32 banks, had
+// twice the prompt kernel's counted bank conflicts.)
+__device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (8 * (cb & 1))); }
 
 // The state of one compute wave: query digits, per-lane LDS offsets, and the
 // running softmax statistics and accumulator of its 16 query rows (for the
@@ -186,10 +192,10 @@ struct RowBlock {
         // transposed V read: source role (b, h) = (l16 >> 1, l16 & 1) reads row
         // lds_row(2r + (b >> 2), 4g + (b & 3)), bytes 16db + 8h
         const int tb = l16 >> 1, th = l16 & 1;
-        v_off = (16 * (tb >> 2) + 4 * (g ^ (tb >> 2)) + (tb & 3)) * kStride + 8 * th;
-        // this lane's S cells (cb, 4g + u) live in LDS rows 16cb + 4(g ^ (cb & 1)) + u
-        m_off0 = 4 * g;
-        m_off1 = 4 * (g ^ 1);
+        v_off = lds_row(tb >> 2, 4 * g + (tb & 3)) * kStride + 8 * th;
+        // this lane's S cells (cb, 4g + u) live in LDS rows lds_row(cb, 4g + u)
+        m_off0 = lds_row(0, 4 * g);
+        m_off1 = lds_row(1, 4 * g) - 16;
         reset();
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
