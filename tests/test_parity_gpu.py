@@ -214,6 +214,21 @@ def test_single_tile_forms_bitwise(n_q, n_qheads):
     check(x0, o0, l0, g0, what=f"single-tile forms R={n_q * n_qheads}")
 
 
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_merge_of_many_chunks(n_q):
+    """Rows with far more chunk partials than the merge requests at once
+    (up to 48): sda_chunk_batch + sda_merge_batch at chunk 64 over
+    12,800-cell lists (200 chunks: several batches per wave, and the maximum
+    over chunk maxima past 64 chunks), a ragged second instance (3,001 cells,
+    47 chunks) and a third with 65 chunks, against the oracle."""
+    say(f"case: merge of 200 chunks, n_q={n_q}")
+    x = gen.make(None, seed=77 + n_q, n_inst=3, n_q=n_q, pool_cells=16384, n_sel=12800,
+                 sel="uniform", chunk=64)
+    x = dataclasses.replace(x, n_sel=np.array([12800, 3001, 4097], np.int32))
+    out, lse, g, _ = two_pass(x, 64)
+    check(x, out, lse, g, what=f"200-chunk merge nq{n_q}")
+
+
 def test_many_instances_coarse_chunks():
     """More than 256 instances and 512 (instance, chunk) pairs: the fused
     call takes chunks k times the caller's (300 x 600 cells at chunk 64:
