@@ -678,7 +678,12 @@ def main(argv=None):
                      "launch_us_mean": k4_us,
                      "note": "latency-bound: one instance, 2,051 cells; "
                              "traffic = HBM bytes per launch (cold, counters), null if the "
-                             "kernel changed since they were taken",
+                             "kernel changed since they were taken; it exceeds the algorithmic "
+                             "bytes because each chunk's tile is staged by one workgroup per "
+                             "16-row group (up to three XCD caches fetch it) and each workgroup "
+                             "reads the whole page-table row to save a dependent round trip: "
+                             "re-reads that cost no time in this launch, whose duration is "
+                             "set by its round trips",
                      "bytes_per_step": bytes_sum, "call_us_per_step": round(call_us_sum, 3)},
         "per_query_count": per_q,
         "pages_600_cells_per_query_count": per_q600,
