@@ -113,6 +113,65 @@ def _ptr(t):
     return t.data_ptr() or None
 
 
+_HALF = (torch.int16, torch.uint16, torch.float16)
+
+
+def _check(t, name, dtypes, shape=None, optional=False):
+    """Raise ValueError unless t is a contiguous tensor of one of dtypes with
+    the given shape (None entries: any size).  The library trusts sizes it
+    cannot see, so a tensor smaller than the arguments say would be read or
+    written out of bounds on the device.  (Devices: _on.)"""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, "
+                         f"not {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(s is not None and int(a) != int(s)
+                                         for a, s in zip(t.shape, shape)):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                             f"{tuple('*' if s is None else s for s in shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on(**tensors):
+    """Raise ValueError unless every given tensor (None: absent) is on one GPU."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU, not {t.device}")
+        if dev is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+        dev = t.device
+
+
+def _check_pool(pool):
+    """The pool's shapes and dtypes; returns its tensors by name (for _on)."""
+    _check(pool.k_codes, "pool.k_codes", torch.int8, (None, HEAD_DIM))
+    cells = int(pool.k_codes.shape[0])
+    if cells % PAGE_SIZE:
+        raise ValueError(f"pool cells ({cells}) must be a multiple of {PAGE_SIZE}")
+    _check(pool.v_codes, "pool.v_codes", torch.int8, (cells, HEAD_DIM))
+    if pool.scales is not None:
+        if pool.k_scales is not None or pool.v_scales is not None:
+            raise ValueError("give either interleaved scales or k_scales and v_scales")
+        _check(pool.scales, "pool.scales", _HALF, (cells, 2))
+    else:
+        _check(pool.k_scales, "pool.k_scales", _HALF, (cells,))
+        _check(pool.v_scales, "pool.v_scales", _HALF, (cells,))
+    return {"pool.k_codes": pool.k_codes, "pool.v_codes": pool.v_codes,
+            "pool.k_scales": pool.k_scales, "pool.v_scales": pool.v_scales,
+            "pool.scales": pool.scales}
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -176,8 +235,19 @@ def decode_attn_step(pool: Pool, page_table, sel, q, softmax_scale: float, chunk
                      out, lse, gather_out=None, ws=None, stream=None, n_sel: int | None = None):
     """One sequence: q [n_q][n_qheads][256] fp32; out like q; lse [n_q][n_qheads].
     Chunks of fused_chunk_cells(1, n_sel, chunk_cells) cells, as the batch call."""
+    _check(q, "q", torch.float32, (None, None, HEAD_DIM))
     n_q, n_qheads = int(q.shape[0]), int(q.shape[1])
+    _check(sel, "sel", torch.int32, (None,))
     n = int(sel.numel()) if n_sel is None else int(n_sel)
+    if not 0 <= n <= sel.numel():
+        raise ValueError(f"n_sel {n} outside [0, {sel.numel()}]")
+    _check(page_table, "page_table", torch.int32, (None,))
+    _check(out, "out", torch.float32, tuple(q.shape))
+    _check(lse, "lse", torch.float32, (n_q, n_qheads))
+    _check(gather_out, "gather_out", torch.int32, (sel.numel(),), optional=True)
+    _check(ws, "ws", torch.uint8, (None,), optional=True)
+    _on(q=q, sel=sel, page_table=page_table, out=out, lse=lse, gather_out=gather_out, ws=ws,
+        **_check_pool(pool))
     if ws is None:
         ws = workspace(1, n_q, n_qheads, n, chunk_cells, q.device)
     ps = pool.c_struct()
@@ -199,14 +269,15 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
     workspace then holds those partials (partials(..., that chunk size)),
     unless fused_single_launch(...) says the call is one launch that leaves
     the workspace untouched."""
-    n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    n_inst, n_q, n_qheads = _check_decode(pool, page_table, sel, n_sel, max_sel, q, gather_out,
+                                          ws, out=out, lse=lse)
     if ws is None:
         ws = workspace(n_inst, n_q, n_qheads, max_sel, chunk_cells, q.device)
-    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    nlp = _n_logical(page_table, n_logical_pages)
     ps = pool.c_struct()
     st = library().sda_decode_attn_batch(
-        C.byref(ps), n_inst, _ptr(page_table), int(page_table.stride(0)), nlp, _ptr(sel),
-        int(sel.stride(0)), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.shape[1]), nlp, _ptr(sel),
+        int(sel.shape[1]), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
         float(softmax_scale), int(chunk_cells), _ptr(out), _ptr(lse), _ptr(gather_out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     if st != SDA_OK:
@@ -214,14 +285,45 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
     return ws
 
 
+def _n_logical(page_table, n_logical_pages):
+    """Logical pages per instance: the table's row length, or fewer."""
+    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    if not 0 <= nlp <= int(page_table.shape[1]):
+        raise ValueError(f"n_logical_pages {nlp} outside [0, {int(page_table.shape[1])}]")
+    return nlp
+
+
+def _check_decode(pool, page_table, sel, n_sel, max_sel, q, gather_out, ws, out=None, lse=None):
+    """Shapes, dtypes and devices of a batched decode call's tensors (out and
+    lse when given); returns (n_inst, n_q, n_qheads)."""
+    _check(q, "q", torch.float32, (None, None, None, HEAD_DIM))
+    n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    _check(page_table, "page_table", torch.int32, (n_inst, None))
+    _check(sel, "sel", torch.int32, (n_inst, None))
+    if not 0 <= int(max_sel) <= int(sel.shape[1]):
+        raise ValueError(f"max_sel {max_sel} outside [0, {int(sel.shape[1])}] (sel's row length)")
+    _check(n_sel, "n_sel", torch.int32, (n_inst,))
+    _check(gather_out, "gather_out", torch.int32, tuple(sel.shape), optional=True)
+    _check(ws, "ws", torch.uint8, (None,), optional=True)
+    if out is not None or lse is not None:
+        _check(out, "out", torch.float32, tuple(q.shape))
+        _check(lse, "lse", torch.float32, (n_inst, n_q, n_qheads))
+    _on(q=q, page_table=page_table, sel=sel, n_sel=n_sel, gather_out=gather_out, ws=ws, out=out,
+        lse=lse, **_check_pool(pool))
+    return n_inst, n_q, n_qheads
+
+
 def chunk_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softmax_scale: float,
                 chunk_cells: int, ws, gather_out=None, stream=None):
     """Chunk pass only, at exactly chunk_cells: partials into ws (see partials())."""
+    if ws is None:
+        raise ValueError("ws is required")
+    _check_decode(pool, page_table, sel, n_sel, max_sel, q, gather_out, ws)
     n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     ps = pool.c_struct()
     st = library().sda_chunk_batch(
-        C.byref(ps), n_inst, _ptr(page_table), int(page_table.stride(0)), int(page_table.shape[1]),
-        _ptr(sel), int(sel.stride(0)), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.shape[1]), int(page_table.shape[1]),
+        _ptr(sel), int(sel.shape[1]), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
         float(softmax_scale), int(chunk_cells), _ptr(gather_out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream))
     if st != SDA_OK:
@@ -230,7 +332,12 @@ def chunk_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softmax_sca
 
 def merge_batch(n_sel, max_sel: int, chunk_cells: int, ws, out, lse, stream=None):
     """Merge pass only: partials in ws -> out [n_inst][n_q][n_qheads][256], lse."""
+    _check(out, "out", torch.float32, (None, None, None, HEAD_DIM))
     n_inst, n_q, n_qheads = int(out.shape[0]), int(out.shape[1]), int(out.shape[2])
+    _check(lse, "lse", torch.float32, (n_inst, n_q, n_qheads))
+    _check(n_sel, "n_sel", torch.int32, (n_inst,))
+    _check(ws, "ws", torch.uint8, (None,))
+    _on(out=out, lse=lse, n_sel=n_sel, ws=ws)
     st = library().sda_merge_batch(n_inst, n_q, n_qheads, _ptr(n_sel), int(max_sel),
                                    int(chunk_cells), _ptr(ws), ws.numel() * ws.element_size(),
                                    _ptr(out), _ptr(lse), _stream(stream))
@@ -244,11 +351,17 @@ def prompt_attn_batch(pool: Pool, page_table, pos0, q, softmax_scale: float, out
     [n_inst] (position of query 0), q [n_inst][n_q][n_qheads][256] fp32; query
     t of instance i attends causally to logical cells 0..pos0[i] + t.  out like
     q, lse [n_inst][n_q][n_qheads]."""
+    _check(q, "q", torch.float32, (None, None, None, HEAD_DIM))
     n_inst, n_q, n_qheads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
-    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    _check(page_table, "page_table", torch.int32, (n_inst, None))
+    _check(pos0, "pos0", torch.int32, (n_inst,))
+    _check(out, "out", torch.float32, tuple(q.shape))
+    _check(lse, "lse", torch.float32, (n_inst, n_q, n_qheads))
+    _on(q=q, page_table=page_table, pos0=pos0, out=out, lse=lse, **_check_pool(pool))
+    nlp = _n_logical(page_table, n_logical_pages)
     ps = pool.c_struct()
     st = library().sda_prompt_attn_batch(
-        C.byref(ps), n_inst, _ptr(page_table), int(page_table.stride(0)), nlp, _ptr(pos0), _ptr(q),
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.shape[1]), nlp, _ptr(pos0), _ptr(q),
         n_q, n_qheads, float(softmax_scale), _ptr(out), _ptr(lse), _stream(stream))
     if st != SDA_OK:
         raise SdaError(st, "sda_prompt_attn_batch")
@@ -259,13 +372,16 @@ def kv_append_batch(pool: Pool, page_table, pos0, k_new, v_new, stream=None,
     """Quantise new rows k_new, v_new float32 [n_inst][n_new][256] into the
     pools at logical cells pos0[i] + t (pos0 device int32 [n_inst]) through
     page_table [n_inst][pt_stride]; writes the pool tensors in place."""
+    _check(k_new, "k_new", torch.float32, (None, None, HEAD_DIM))
     n_inst, n_new = int(k_new.shape[0]), int(k_new.shape[1])
-    if tuple(v_new.shape) != tuple(k_new.shape):
-        raise ValueError("k_new and v_new must have the same shape")
-    nlp = int(page_table.shape[1]) if n_logical_pages is None else int(n_logical_pages)
+    _check(v_new, "v_new", torch.float32, tuple(k_new.shape))
+    _check(page_table, "page_table", torch.int32, (n_inst, None))
+    _check(pos0, "pos0", torch.int32, (n_inst,))
+    _on(k_new=k_new, v_new=v_new, page_table=page_table, pos0=pos0, **_check_pool(pool))
+    nlp = _n_logical(page_table, n_logical_pages)
     ps = pool.c_struct()
     st = library().sda_kv_append_batch(C.byref(ps), n_inst, _ptr(page_table),
-                                       int(page_table.stride(0)), nlp, _ptr(pos0), _ptr(k_new),
+                                       int(page_table.shape[1]), nlp, _ptr(pos0), _ptr(k_new),
                                        _ptr(v_new), n_new, _stream(stream))
     if st != SDA_OK:
         raise SdaError(st, "sda_kv_append_batch")

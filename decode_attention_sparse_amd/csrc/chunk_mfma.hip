@@ -44,13 +44,14 @@
 //       conversion to fp32.  Score errors are at fp32 level relative to the
 //       wave's largest score.
 //   PV  x = p * v_scale / tau in [0, 127], tau = (the row's largest
-//       p * v_scale in the tile) / 127; X = rint(256 x) in [0, 32512] is
-//       written as 2^8 hi + lo (hi in [0,127], lo in [-128,127]); the tile's
-//       sum over cells of X * v_code (two MFMAs, combined as 2^8 HI + LO) is
-//       exact in int32 and folded into the fp32 accumulator once per tile.
-//       The probability split keeps 15 bits relative to the tile's largest
-//       weighted probability p * v_scale, whatever the spread of the V
-//       scales.
+//       p * v_scale in the tile) / 127; X = rint(2^16 x) in [0, 127 * 2^16]
+//       is written as 2^16 a + 2^8 b + c (a in [0,127], b, c in [-128,127]);
+//       the tile's sums over cells of a, b and c times v_code (three MFMAs)
+//       are exact in int32, 2^8 A + B is formed in int32 (|.| < 2^29), and
+//       2^8 (2^8 A + B) + C is folded into the fp32 accumulator once per
+//       tile.  Each weight is represented to 2^-24 of the tile's largest
+//       weighted probability p * v_scale (the resolution of an fp32 sum of
+//       such terms), whatever the spread of the V scales.
 //
 // Pipeline.  Iteration t of the tile loop computes the scores of tile t+1
 // while it runs the softmax and the V accumulation of tile t, so matrix-core
@@ -82,7 +83,7 @@ constexpr int kTile = 64;            // cells per tile (the K extent of one PV M
 constexpr int kStride = kDim + 16;   // LDS bytes per code row (padded)
 constexpr int kBuf = kTile * kStride;
 constexpr int kRows = kTile / 4;     // 1 KB staging loads per tile and pool (4 rows each)
-constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^22) to integers in the low bits
+constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^23) to integers in the low bits
 constexpr float kWTiny = 7.888609052210118e-31f;  // 2^-100: tiles whose weights stay below carry none
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
@@ -348,8 +349,12 @@ struct RowBlock {
                                                const float *vs_t, int dh) {
         const float m_use = st.m_use, corr = st.corr, frame_new = st.frame_new;
         // ---------------- probabilities and their digits for the current tile
-        // weights w = p * v_scale; W = 256 / tau = 32512 / (row max of w), and
-        // X = rint(w * W) lands in the low bits of fma(w, W, 2^23)
+        // weights w = p * v_scale; W = 2^16 / tau = 2^16 * 127 / (row max of
+        // w), and X = rint(w * W) < 2^23 lands in the low bits of
+        // fma(w, W, 2^23): X = 2^16 a + 2^8 b + c with balanced digits b, c in
+        // [-128, 127] (a in [0, 127]): c = byte 0 of X, b = byte 1 of X + 2^7,
+        // a = byte 2 of X + 2^7 + 2^15 (bit 23 of the float pattern, the
+        // exponent's lowest bit, is 0 in [2^23, 2^24))
         float psum = 0.f;
         float wt[4][4];
         float wmax = 0.f;
@@ -367,20 +372,26 @@ struct RowBlock {
         }
         wmax = max4(wmax);
         const bool live = wmax > kWTiny;
-        const float W = live ? (256.f * 127.f) * __builtin_amdgcn_rcpf(wmax) : 0.f;
-        v4i xa, xb;
+        const float W = live ? (65536.f * 127.f) * __builtin_amdgcn_rcpf(wmax) : 0.f;
+        v4i xa, xb, xc;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            unsigned xs[4];
+            unsigned xs[4], x1[4], x2[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) xs[u] = __float_as_uint(fmaf(wt[cb][u], W, kRound));
-            // low digit = byte 0 of X; high digit = byte 1 of X + 128
-            const unsigned lo01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
-            const unsigned lo23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
-            const unsigned hi01 = __builtin_amdgcn_perm(xs[1] + 128u, xs[0] + 128u, 0x0c0c0501u);
-            const unsigned hi23 = __builtin_amdgcn_perm(xs[3] + 128u, xs[2] + 128u, 0x05010c0cu);
-            xa[cb] = (int)(hi01 | hi23);
-            xb[cb] = (int)(lo01 | lo23);
+            for (int u = 0; u < 4; ++u) {
+                xs[u] = __float_as_uint(fmaf(wt[cb][u], W, kRound));
+                x1[u] = xs[u] + 128u;
+                x2[u] = xs[u] + 32896u;
+            }
+            const unsigned c01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
+            const unsigned c23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
+            const unsigned b01 = __builtin_amdgcn_perm(x1[1], x1[0], 0x0c0c0501u);
+            const unsigned b23 = __builtin_amdgcn_perm(x1[3], x1[2], 0x05010c0cu);
+            const unsigned a01 = __builtin_amdgcn_perm(x2[1], x2[0], 0x0c0c0602u);
+            const unsigned a23 = __builtin_amdgcn_perm(x2[3], x2[2], 0x06020c0cu);
+            xa[cb] = (int)(a01 | a23);
+            xb[cb] = (int)(b01 | b23);
+            xc[cb] = (int)(c01 | c23);
         }
         l_part = fmaf(l_part, corr, psum);
 
@@ -391,7 +402,8 @@ struct RowBlock {
             for (int db = 0; db < kDB; ++db) o[db] *= frame;
             frame = 1.f;
         }
-        const float tau2 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 256 / frame
+        const float tau3 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 2^16 / frame
+        const float tau3h = 256.f * tau3;
 
         // ---------------- O^T += V^T P^T for this wave's blocks of 16 dims
         const int8_t *vp = vb + v_off + 16 * kDB * dh;
@@ -402,10 +414,14 @@ struct RowBlock {
                 (v2i LDS_AS *)(vp + 32 * kStride + 16 * db));
             const v4i va = {h0[0], h0[1], h1[0], h1[1]};
             const v4i hi = mfma_i8(va, xa, (v4i){0, 0, 0, 0});
-            const v4i lo = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
-            const v4i acc = (hi << 8) + lo;  // sum of X * v_code, exact
+            const v4i mid = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
+            const v4i lo = mfma_i8(va, xc, (v4i){0, 0, 0, 0});
+            // sum of X * v_code = 2^8 T + LO, with T = 2^8 HI + MID exact in
+            // int32 (|T| < 2^29, |LO| < 2^21)
+            const v4i top = (hi << 8) + mid;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) o[db][u] = fmaf((float)acc[u], tau2, o[db][u]);
+            for (int u = 0; u < 4; ++u)
+                o[db][u] = fmaf((float)top[u], tau3h, fmaf((float)lo[u], tau3, o[db][u]));
         }
     }
 

@@ -266,9 +266,11 @@ class AppendInputs:
 
 
 def make_append(name: str | None = None, seed: int | None = None, pos0=None, spread: float = 8.0,
-                **overrides) -> AppendInputs:
+                k_spread: float | None = None, **overrides) -> AppendInputs:
     """Page tables drawn as make() draws them, new rows N(0, 1) scaled per row
-    by 2^U(-spread, spread) (rows of very different magnitudes)."""
+    by 2^U(-spread, spread) (rows of very different magnitudes); k_spread,
+    when given, replaces spread for the K rows (k_spread 0: K rows N(0, 1),
+    so scores stay of order 1 and attention spreads over many cells)."""
     spec = dict(APPEND_CONFIGS[name]) if name is not None else {"n_inst": 1}
     spec.update(overrides)
     n_inst, n_new, cells = int(spec["n_inst"]), int(spec["n_new"]), int(spec["pool_cells"])
@@ -282,9 +284,9 @@ def make_append(name: str | None = None, seed: int | None = None, pos0=None, spr
     def fill(i):
         rng = np.random.Generator(np.random.PCG64(children[i]))
         pt[i] = rng.permutation(pages) + i * pages
-        for a in (k_new, v_new):
+        for a, sp in ((k_new, spread if k_spread is None else k_spread), (v_new, spread)):
             a[i] = rng.standard_normal((n_new, D), dtype=np.float32)
-            a[i] *= np.exp2(rng.uniform(-spread, spread, (n_new, 1))).astype(np.float32)
+            a[i] *= np.exp2(rng.uniform(-sp, sp, (n_new, 1))).astype(np.float32)
 
     with _cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
         list(ex.map(fill, range(n_inst)))

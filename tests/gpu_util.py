@@ -52,9 +52,13 @@ def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda", interleave=Fa
     return (out.cpu().numpy(), lse.cpu().numpy(), None if g is None else g.cpu().numpy(), ws)
 
 
-def check(x, out, lse, g=None, inst_ids=None, what=""):
+def check(x, out, lse, g=None, inst_ids=None, what="", strict_out=True, strict_lse=True):
     """The outputs (and gather indices) of a decode call against the oracle,
-    on all instances or the sampled inst_ids."""
+    on all instances or the sampled inst_ids.  Beyond the elementwise
+    atol + rtol |ref| bound, strict_out / strict_lse assert the absolute
+    bounds alone (max |dout| <= 1e-3, max |dlse| <= 1e-4), which float32
+    meets wherever |lse| stays below about 100 (scores far larger, as in the
+    heavy-tailed batched workload, leave float32 itself short of 1e-4)."""
     import oracle
     ro, rl = oracle.attend(x, inst_ids)
     sl = slice(None) if inst_ids is None else np.asarray(inst_ids)
@@ -64,7 +68,13 @@ def check(x, out, lse, g=None, inst_ids=None, what=""):
         rg = oracle.gather(x)
         valid = np.arange(x.sel.shape[1])[None, :] < x.n_sel[:, None]
         assert np.array_equal(g[valid], rg[valid]), f"{what}: gather indices differ"
-    say(f"  {what}: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
+    say(f"  {what}: max|dout| {e1:.2e} ({e1 / OUT_ATOL:.1%} of {OUT_ATOL:g}), max|dlse| {e2:.2e} "
+        f"({e2 / LSE_ATOL:.1%} of {LSE_ATOL:g})")
+    if strict_out:
+        assert e1 <= OUT_ATOL, f"{what}: max|dout| {e1:.3e} above {OUT_ATOL}"
+    if strict_lse:
+        assert e2 <= LSE_ATOL, f"{what}: max|dlse| {e2:.3e} above {LSE_ATOL}"
+    return e1, e2
 
 
 def two_pass(x, chunk, gather=True):

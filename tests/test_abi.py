@@ -313,3 +313,59 @@ def test_append_rejects_before_launch():
     assert call(v=FAKE + 4) == api.SDA_ERR_INVALID_ARG
     assert call(pt=None) == api.SDA_ERR_INVALID_ARG
     assert call(n_inst=0) == api.SDA_OK and call(n_new=0) == api.SDA_OK  # nothing launched
+
+
+def _cpu_call_args():
+    """Well-formed CPU tensors for a batched decode call (2 instances, 2
+    query positions of 3 heads, 40 selected cells, 8 logical pages)."""
+    import torch
+    from decode_attention_sparse_amd import api
+    cells = 256
+    pool = api.Pool(torch.zeros((cells, 256), dtype=torch.int8), torch.zeros(cells, dtype=torch.int16),
+                    torch.zeros((cells, 256), dtype=torch.int8), torch.zeros(cells, dtype=torch.int16))
+    return dict(pool=pool, page_table=torch.zeros((2, 8), dtype=torch.int32),
+                sel=torch.zeros((2, 40), dtype=torch.int32), n_sel=torch.zeros(2, dtype=torch.int32),
+                max_sel=40, q=torch.zeros((2, 2, 3, 256)), softmax_scale=0.0625, chunk_cells=64,
+                out=torch.zeros((2, 2, 3, 256)), lse=torch.zeros((2, 2, 3)))
+
+
+@pytest.mark.parametrize("change,msg", [
+    (dict(n_sel=("dtype", "int64")), "n_sel must have dtype"),
+    (dict(q=("dtype", "float64")), "q must have dtype"),
+    (dict(q=("shape", (2, 2, 3, 128))), "q has shape"),
+    (dict(out=("shape", (2, 2, 3, 128))), "out has shape"),
+    (dict(lse=("shape", (2, 2))), "lse has shape"),
+    (dict(sel=("dtype", "int64")), "sel must have dtype"),
+    (dict(sel=("shape", (3, 40))), "sel has shape"),
+    (dict(page_table=("shape", (1, 8))), "page_table has shape"),
+    (dict(max_sel=("value", 41)), "max_sel 41 outside"),
+    (dict(n_sel=("shape", (3,))), "n_sel has shape"),
+    (dict(pool_v=("shape", (128, 256))), "pool.v_codes has shape"),
+    (dict(pool_ks=("shape", (100,))), "pool.k_scales has shape"),
+    (dict(pool_ks=("dtype", "int32")), "pool.k_scales must have dtype"),
+    (dict(), "must be on a GPU"),
+])
+def test_binding_rejects_bad_tensors(change, msg):
+    """The binding checks dtypes, shapes and devices before calling into the
+    library, which trusts the sizes it is given (an int64 count read as int32
+    pairs or an undersized tensor would be read out of bounds on the GPU).
+    Run with CPU tensors: every call must raise ValueError (the last case is
+    well formed except for the device)."""
+    import torch
+    from decode_attention_sparse_amd import api
+    a = _cpu_call_args()
+    for key, (what, val) in change.items():
+        if key.startswith("pool_"):
+            pool = a["pool"]
+            attr = {"pool_v": "v_codes", "pool_ks": "k_scales"}[key]
+            t = getattr(pool, attr)
+            setattr(pool, attr, t.to(getattr(torch, val)) if what == "dtype"
+                    else torch.zeros(val, dtype=t.dtype))
+        elif what == "dtype":
+            a[key] = a[key].to(getattr(torch, val))
+        elif what == "shape":
+            a[key] = torch.zeros(val, dtype=a[key].dtype)
+        else:
+            a[key] = val
+    with pytest.raises(ValueError, match=msg):
+        api.decode_attn_batch(**a)

@@ -151,6 +151,93 @@ def test_append_then_prompt_attention():
     say(f"  append + prompt: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
 
 
+def f32_attend(q, k_hat, v_hat, scale, visible=None):
+    """Plain float32 softmax attention (numpy float32 products and sums) over
+    dequantised rows: the error level a float32 computation reaches."""
+    s = (q @ k_hat.T) * np.float32(scale)
+    if visible is not None:
+        s = np.where(visible, s, np.float32(-np.inf))
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True, dtype=np.float32)
+    return (p @ v_hat) / l, (m + np.log(l))[:, 0]
+
+
+def dequant(codes, scales, phys):
+    ok = phys >= 0
+    rows = np.where(ok[:, None], codes[np.where(ok, phys, 0)].astype(np.float32), np.float32(0))
+    return rows * scales[np.where(ok, phys, 0)].view(np.float16).astype(np.float32)[:, None]
+
+
+# GPU error may exceed a float32 computation's by at most this factor
+F32_FACTOR = 4.0
+
+
+def test_append_wide_v_diffuse_attention():
+    """V rows at the append workload's full range (N(0, 1) x 2^U(-8, 8): V
+    scales over 2^16) and K rows N(0, 1), so scores are of order 1 and
+    attention spreads over hundreds of cells: a weight's rounding then adds
+    up over many cells.  GPU append, then GPU decode over a selection holding
+    every appended cell, and GPU prompt attention over the pool; each against
+    the oracle's append + attention, and no further from it than a few times
+    a plain float32 attention on the same pools."""
+    n_new, cells, n_sel = 300, 2048, 1024
+    pos0 = cells - n_new
+    say("case: V rows over 2^+-8 and K rows N(0,1) appended at 1748..2047 of a 2,048-cell pool")
+    x = gen.make(None, seed=31, n_inst=1, n_q=4, pool_cells=cells, n_sel=n_sel, sel="uniform",
+                 chunk=256)
+    app = gen.make_append(None, seed=32, n_inst=1, n_new=n_new, pool_cells=cells, pos0=pos0,
+                          spread=8.0, k_spread=0.0)
+    app = dataclasses.replace(app, page_table=x.page_table)
+    pools = (x.k_codes, x.k_scales, x.v_codes, x.v_scales)
+    gp = run_append(pools, app)
+    check_equal(gp, oracle_append(pools, app), "appended pools")
+    rng = np.random.default_rng(33)
+    others = rng.choice(pos0, n_sel - n_new, replace=False)
+    sel = np.empty((1, n_sel), np.int32)
+    sel[0] = np.sort(np.concatenate([others, np.arange(pos0, cells)]))
+    x = dataclasses.replace(x, sel=sel, k_codes=gp[0], k_scales=gp[1], v_codes=gp[2],
+                            v_scales=gp[3])
+
+    def compare(got_o, got_l, ref_o, ref_l, f32_o, f32_l, what):
+        assert np.isfinite(got_o).all() and np.isfinite(got_l).all(), what
+        assert_close(got_o, ref_o, OUT_ATOL, OUT_RTOL, f"{what} out")
+        assert_close(got_l, ref_l, LSE_ATOL, LSE_RTOL, f"{what} lse")
+        e_o, f_o = np.abs(got_o - ref_o).max(), np.abs(f32_o - ref_o).max()
+        e_l, f_l = np.abs(got_l - ref_l).max(), np.abs(f32_l - ref_l).max()
+        say(f"  {what}: max|out| {np.abs(ref_o).max():.1f}; max|dout| GPU {e_o:.2e} float32 "
+            f"{f_o:.2e}; max|dlse| GPU {e_l:.2e} float32 {f_l:.2e}")
+        assert e_o <= F32_FACTOR * f_o, f"{what}: out error {e_o:.3e} vs float32 {f_o:.3e}"
+        assert e_l <= F32_FACTOR * f_l + 1e-6, f"{what}: lse error {e_l:.3e} vs float32 {f_l:.3e}"
+
+    # decode over the selection
+    from tests.gpu_util import run_batch
+    out, lse, g, _ = run_batch(x)
+    ro, rl = oracle.attend(x)
+    phys = oracle.gather(x)[0]
+    qr = x.q[0].reshape(-1, 256)
+    fo, fl = f32_attend(qr, dequant(gp[0], gp[1], phys), dequant(gp[2], gp[3], phys),
+                        x.softmax_scale)
+    compare(out[0].reshape(-1, 256), lse[0].reshape(-1), ro[0].reshape(-1, 256),
+            rl[0].reshape(-1), fo, fl, "append + decode")
+
+    # prompt attention of the appended chunk's positions over the pool
+    xp = gen.make_prompt(None, seed=34, n_q=n_new, pool_cells=cells)
+    xp = dataclasses.replace(xp, page_table=x.page_table, k_codes=gp[0], k_scales=gp[1],
+                             v_codes=gp[2], v_scales=gp[3])
+    assert int(xp.pos0[0]) == pos0
+    po, pl = run_prompt(xp)
+    pro, prl = oracle.prompt_attend(xp, 0)
+    c = np.arange(cells)
+    phys_all = x.page_table[0][c >> 4] * 16 + (c & 15)
+    t = np.repeat(np.arange(n_new), xp.q.shape[2])
+    vis = c[None, :] <= (pos0 + t)[:, None]
+    fo, fl = f32_attend(xp.q[0].reshape(-1, 256), dequant(gp[0], gp[1], phys_all),
+                        dequant(gp[2], gp[3], phys_all), xp.softmax_scale, vis)
+    compare(po[0].reshape(-1, 256), pl[0].reshape(-1), pro.reshape(-1, 256), prl.reshape(-1),
+            fo, fl, "append + prompt")
+
+
 @pytest.mark.parametrize("k", range(15))
 def test_append_random_geometry(k):
     """Seeded sweep: instance and row counts, pool sizes, start positions

@@ -52,9 +52,10 @@ def test_wide_scale_range(n_q):
     say(f"case: scales over 2^16, config 1, n_q={n_q}")
     x = wide_scales(gen.make(1).with_n_q(n_q), 40 + n_q)
     out, lse, g, _ = run_batch(x)
-    check(x, out, lse, g, what=f"wide scales nq{n_q}")
+    # scores reach the hundreds here: lse to the relative bound only
+    check(x, out, lse, g, what=f"wide scales nq{n_q}", strict_lse=False)
     o2, l2, g2, _ = two_pass(x, 256)
-    check(x, o2, l2, g2, what=f"wide scales nq{n_q}, two passes at chunk 256")
+    check(x, o2, l2, g2, what=f"wide scales nq{n_q}, two passes at chunk 256", strict_lse=False)
 
 
 @pytest.mark.parametrize("cfg", [0, 1])
@@ -328,16 +329,18 @@ def test_ragged_batch_and_unsorted():
     check(x, out, lse, g, what="ragged")
 
 
-@pytest.mark.parametrize("cfg,ids", [(2, [0, 1, 97, 255]), (3, [0, 31, 63]), (4, [0, 31])])
-def test_full_size_configs_sampled(cfg, ids):
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_configs(cfg):
     """The batched workloads at full size, in the launch configuration the
-    bench times (interleaved scale pairs); sampled instances against the
-    oracle, every gather index bit-exact."""
-    say(f"case: config {cfg} full size, oracle on instances {ids}")
+    bench times (interleaved scale pairs); every instance against the oracle,
+    every gather index bit-exact.  The heavy-tailed K scales of the batched
+    decode workload put |lse| between about 800 and 2,300, where float32
+    itself misses an absolute 1e-4: its lse keeps the relative bound."""
+    say(f"case: config {cfg} full size, oracle on every instance")
     x = gen.make(cfg)
     out, lse, g, _ = run_batch(x, interleave=True)
-    check(x, out, lse, g, inst_ids=ids, what=f"cfg{cfg}")
     assert np.isfinite(out).all() and np.isfinite(lse).all()
+    check(x, out, lse, g, what=f"cfg{cfg} ({x.n_inst} instances)", strict_lse=cfg != 2)
 
 
 @pytest.mark.parametrize("cfg,n_q,n_inst", [(1, 4, None), (1, 1, 8), (2, 4, None)])
