@@ -16,10 +16,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsda.so")
 
 SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED, SDA_ERR_WORKSPACE, SDA_ERR_LAUNCH = 0, -1, -2, -3, -4
+SDA_ERR_SCRATCH = -5
+SCRATCH_BYTES = 32 << 20  # the device array behind sda_decode_attn_batch_noalloc, per GPU
 PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN, MAX_CHUNKS = 16, 256, 64, 64, 65535
 PROMPT_MAX_ROWS = 65535 * 48
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
+            "sda_decode_attn_batch_noalloc",
             "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_fused_chunk_cells",
             "sda_fused_single_launch", "sda_kv_append_batch", "sda_status_string")
 
@@ -55,6 +58,10 @@ def library() -> C.CDLL:
         lib.sda_decode_attn_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, i64, vp, i32,
                                               vp, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]
         lib.sda_decode_attn_batch.restype = C.c_int
+        lib.sda_decode_attn_batch_noalloc.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, i64,
+                                                      vp, i32, vp, i32, i32, f32, i32, vp, vp, vp,
+                                                      vp]
+        lib.sda_decode_attn_batch_noalloc.restype = C.c_int
         lib.sda_chunk_batch.argtypes = [C.POINTER(_Pool), i32, vp, i64, i32, vp, i64, vp, i32, vp,
                                         i32, i32, f32, i32, vp, vp, sz, vp]
         lib.sda_chunk_batch.restype = C.c_int
@@ -283,6 +290,25 @@ def decode_attn_batch(pool: Pool, page_table, sel, n_sel, max_sel: int, q, softm
     if st != SDA_OK:
         raise SdaError(st, "sda_decode_attn_batch")
     return ws
+
+
+def decode_attn_batch_noalloc(pool: Pool, page_table, sel, n_sel, max_sel: int, q,
+                              softmax_scale: float, chunk_cells: int, out, lse, gather_out=None,
+                              stream=None, n_logical_pages: int | None = None):
+    """decode_attn_batch without a workspace: the chunk partials go to the
+    library's own device array (SCRATCH_BYTES per GPU); the call allocates
+    nothing.  Calls that overlap on one GPU share that array and race."""
+    n_inst, n_q, n_qheads = _check_decode(pool, page_table, sel, n_sel, max_sel, q, gather_out,
+                                          None, out=out, lse=lse)
+    nlp = _n_logical(page_table, n_logical_pages)
+    ps = pool.c_struct()
+    st = library().sda_decode_attn_batch_noalloc(
+        C.byref(ps), n_inst, _ptr(page_table), int(page_table.shape[1]), nlp, _ptr(sel),
+        int(sel.shape[1]), _ptr(n_sel), int(max_sel), _ptr(q), n_q, n_qheads,
+        float(softmax_scale), int(chunk_cells), _ptr(out), _ptr(lse), _ptr(gather_out),
+        _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_decode_attn_batch_noalloc")
 
 
 def _n_logical(page_table, n_logical_pages):

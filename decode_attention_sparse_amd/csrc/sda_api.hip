@@ -6,8 +6,16 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sda.h"
 #include "sda_internal.h"
+
+// The chunk partials of sda_decode_attn_batch_noalloc: one array per GPU,
+// loaded with the library's code object and kept until the process ends.
+// In host code its name is only a handle for hipGetSymbolAddress; kernels
+// get the device address that call returns (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[SDA_SCRATCH_BYTES];
 
 namespace {
 
@@ -116,15 +124,25 @@ void set_pool(sda::Params *p, const sda_pool *pool) {
     p->n_phys_pages = pool->n_phys_pages;
 }
 
-int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
-        int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
-        const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
-        int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
-        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream,
-        int passes = kBoth) {
+// A validated decode call: its parameters (all but the partials' pointers),
+// the partials' layout and whether it runs as one chunk-kernel launch.
+struct Call {
+    sda::Params p;
+    Layout L;
+    bool single;
+    int passes;
+};
+
+// Host-side validation of a decode call (everything but the workspace) into
+// c; SDA_OK with c->p.n_inst == 0 means there is nothing to launch.
+int prepare(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
+            int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
+            const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
+            int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
+            float *lse, int32_t *gather_out, int passes, Call *c) {
     int st = check_pool(pool);
     if (st != SDA_OK) return st;
-    Layout L;
+    Layout &L = c->L;
     st = layout_of(n_inst, n_q, n_qheads, pool->head_dim, max_sel, chunk_cells, &L);
     if (st != SDA_OK) return st;
     // the fused call may run finer chunks (same layout, smaller chunk size)
@@ -136,17 +154,17 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     if (n_logical_pages < 0 || pt_stride < n_logical_pages || sel_stride < max_sel)
         return SDA_ERR_INVALID_ARG;
     if (!isfinite(softmax_scale)) return SDA_ERR_INVALID_ARG;
+    sda::Params &p = c->p;
+    memset(&p, 0, sizeof p);
+    c->passes = passes;
+    c->single = false;
     if (n_inst == 0) return SDA_OK;
     if (!q || !aligned(q, 16)) return SDA_ERR_INVALID_ARG;
     if ((passes & kMerge) && (!out || !lse || !aligned(out, 16) || !aligned(lse, 4)))
         return SDA_ERR_INVALID_ARG;
     if (n_logical_pages > 0 && !page_table) return SDA_ERR_INVALID_ARG;
     if (max_sel > 0 && !sel) return SDA_ERR_INVALID_ARG;
-    if (L.total > 0 && (!workspace || workspace_bytes < L.total || !aligned(workspace, kAlign)))
-        return SDA_ERR_WORKSPACE;
 
-    sda::Params p;
-    memset(&p, 0, sizeof p);
     set_pool(&p, pool);
     p.page_table = page_table;
     p.pt_stride = pt_stride;
@@ -162,21 +180,75 @@ int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
     p.chunk = run_chunk;
     p.n_chunks = L.n_chunks;
-    char *ws = static_cast<char *>(workspace);
-    p.acc = L.total ? reinterpret_cast<float *>(ws + L.acc_off) : nullptr;
-    p.m = L.total ? reinterpret_cast<float *>(ws + L.m_off) : nullptr;
-    p.l = L.total ? reinterpret_cast<float *>(ws + L.l_off) : nullptr;
     p.gather_out = gather_out;
     p.out = out;
     p.lse = lse;
+    // a fused call that runs as one launch leaves the partials untouched
+    c->single = passes == kBoth && sda::chunk_writes_output(p);
+    return SDA_OK;
+}
 
+// Bytes of partials a prepared call reads and writes (0 for a single launch).
+size_t partial_bytes(const Call &c) { return c.single ? 0 : c.L.total; }
+
+// Launches a prepared call with its partials at workspace (at least
+// partial_bytes(c) bytes, 256-byte aligned, when that is not 0).
+int launch(Call &c, void *workspace, void *stream) {
+    if (c.p.n_inst == 0) return SDA_OK;
+    sda::Params &p = c.p;
+    char *ws = static_cast<char *>(workspace);
+    const bool has = partial_bytes(c) > 0;
+    p.acc = has ? reinterpret_cast<float *>(ws + c.L.acc_off) : nullptr;
+    p.m = has ? reinterpret_cast<float *>(ws + c.L.m_off) : nullptr;
+    p.l = has ? reinterpret_cast<float *>(ws + c.L.l_off) : nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();  // clear a stale error so it is not blamed on us
-    if (passes == kBoth && sda::chunk_writes_output(p))
+    if (c.single)
         return sda::launch_chunk_final(p, s) == hipSuccess ? SDA_OK : SDA_ERR_LAUNCH;
-    if ((passes & kChunk) && p.n_chunks > 0 && sda::launch_chunk(p, s) != hipSuccess)
+    if ((c.passes & kChunk) && p.n_chunks > 0 && sda::launch_chunk(p, s) != hipSuccess)
         return SDA_ERR_LAUNCH;
-    if ((passes & kMerge) && sda::launch_merge(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
+    if ((c.passes & kMerge) && sda::launch_merge(p, s) != hipSuccess) return SDA_ERR_LAUNCH;
+    return SDA_OK;
+}
+
+// A call with the caller's workspace.  The public entry points ask for the
+// whole layout's size even when the call is a single launch that does not
+// touch it.
+int run(const sda_pool *pool, int32_t n_inst, const int32_t *page_table, int64_t pt_stride,
+        int32_t n_logical_pages, const int32_t *sel, int64_t sel_stride,
+        const int32_t *n_sel_dev, int32_t n_sel_host, int32_t max_sel, const float *q,
+        int32_t n_q, int32_t n_qheads, float softmax_scale, int32_t chunk_cells, float *out,
+        float *lse, int32_t *gather_out, void *workspace, size_t workspace_bytes, void *stream,
+        int passes = kBoth) {
+    Call c;
+    int st = prepare(pool, n_inst, page_table, pt_stride, n_logical_pages, sel, sel_stride,
+                     n_sel_dev, n_sel_host, max_sel, q, n_q, n_qheads, softmax_scale, chunk_cells,
+                     out, lse, gather_out, passes, &c);
+    if (st != SDA_OK || n_inst == 0) return st;
+    if (c.L.total > 0 && (!workspace || workspace_bytes < c.L.total || !aligned(workspace, kAlign)))
+        return SDA_ERR_WORKSPACE;
+    return launch(c, workspace, stream);
+}
+
+// Device address of the current device's scratch array, resolved once per
+// device with that device current and kept for later calls.
+constexpr int kMaxDevices = 256;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices];
+
+int scratch_ptr(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SDA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return SDA_ERR_LAUNCH;
+        }
+        scratch_addr[dev] = p;
+    }
+    *ptr = scratch_addr[dev];
     return SDA_OK;
 }
 
@@ -244,6 +316,28 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
     return run(pool, n_inst, page_table, pt_stride, n_logical_pages, sel, sel_stride, n_sel, 0,
                max_sel, q, n_q, n_qheads, softmax_scale, chunk_cells, out, lse, gather_out,
                workspace, workspace_bytes, stream);
+}
+
+int sda_decode_attn_batch_noalloc(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                                  int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
+                                  int64_t sel_stride, const int32_t *n_sel, int32_t max_sel,
+                                  const float *q, int32_t n_q, int32_t n_qheads,
+                                  float softmax_scale, int32_t chunk_cells, float *out,
+                                  float *lse, int32_t *gather_out, void *stream) {
+    if (n_inst > 0 && !n_sel) return SDA_ERR_INVALID_ARG;
+    Call c;
+    int st = prepare(pool, n_inst, page_table, pt_stride, n_logical_pages, sel, sel_stride, n_sel,
+                     0, max_sel, q, n_q, n_qheads, softmax_scale, chunk_cells, out, lse,
+                     gather_out, kBoth, &c);
+    if (st != SDA_OK || n_inst == 0) return st;
+    const size_t need = partial_bytes(c);
+    if (need > SDA_SCRATCH_BYTES) return SDA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        st = scratch_ptr(&ws);
+        if (st != SDA_OK) return st;
+    }
+    return launch(c, ws, stream);
 }
 
 int sda_chunk_batch(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
@@ -365,6 +459,9 @@ const char *sda_status_string(int status) {
         case SDA_ERR_UNSUPPORTED: return "SDA_ERR_UNSUPPORTED: unsupported geometry";
         case SDA_ERR_WORKSPACE: return "SDA_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case SDA_ERR_LAUNCH: return "SDA_ERR_LAUNCH: kernel launch failed";
+        case SDA_ERR_SCRATCH:
+            return "SDA_ERR_SCRATCH: the call's chunk partials exceed the library's fixed "
+                   "device scratch array (SDA_SCRATCH_BYTES)";
         default: return "unknown sda status";
     }
 }

@@ -40,7 +40,9 @@
  *   - Every array argument is a DEVICE pointer unless marked "host".  The
  *     caller owns all memory; the library never allocates, frees, copies to
  *     the host or synchronises, and keeps no state between calls, so calls
- *     may be captured into a HIP graph and replayed.
+ *     may be captured into a HIP graph and replayed.  (The one exception,
+ *     sda_decode_attn_batch_noalloc, keeps its partials in a device array
+ *     the library holds per GPU and remembers that array's address.)
  *   - Arguments are validated on the host before anything is launched; a
  *     non-zero status means nothing was launched.  Unsupported geometry
  *     returns SDA_ERR_UNSUPPORTED so that a caller can fall back.
@@ -73,7 +75,9 @@ typedef enum {
     SDA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride/alignment */
     SDA_ERR_UNSUPPORTED = -2, /* geometry this library does not implement */
     SDA_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
-    SDA_ERR_LAUNCH = -4       /* the HIP runtime rejected a kernel launch */
+    SDA_ERR_LAUNCH = -4,      /* the HIP runtime rejected a kernel launch */
+    SDA_ERR_SCRATCH = -5      /* sda_decode_attn_batch_noalloc: the call needs more
+                                 than SDA_SCRATCH_BYTES of chunk partials */
 } sda_status;
 
 /* The INT8 pools, indexed by physical cell = physical page * 16 + slot.
@@ -199,6 +203,37 @@ int sda_decode_attn_batch(const sda_pool *pool, int32_t n_inst, const int32_t *p
                           const float *q, int32_t n_q, int32_t n_qheads, float softmax_scale,
                           int32_t chunk_cells, float *out, float *lse, int32_t *gather_out,
                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* sda_decode_attn_batch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and
+ * the same results bit for bit.  The chunk partials go to a device array the
+ * library holds instead, SDA_SCRATCH_BYTES per GPU, resident from the
+ * library's load until the process ends; the call itself allocates nothing.
+ *   - The array used is the current device's (hipGetDevice): the stream and
+ *     every pointer must belong to that device.  The first call on a device
+ *     resolves the array's address (hipGetSymbolAddress); make that first
+ *     call outside stream capture.
+ *   - A call whose partials exceed SDA_SCRATCH_BYTES returns SDA_ERR_SCRATCH
+ *     without launching: the partials of the fused chunk size,
+ *     sda_workspace_bytes at chunk_cells = sda_fused_chunk_cells(n_inst,
+ *     max_sel, chunk_cells), or 0 when sda_fused_single_launch says the call
+ *     is one launch.
+ *   - Every call on a GPU shares that GPU's array and leaves its partials
+ *     there.  Nothing in it has to start at zero (each chunk pass writes
+ *     every partial its merge reads), but calls that overlap on one GPU
+ *     (other streams, other host threads) race on it and give wrong results:
+ *     serialise them.
+ * Returns the statuses of sda_decode_attn_batch except SDA_ERR_WORKSPACE,
+ * plus SDA_ERR_SCRATCH (and SDA_ERR_LAUNCH if the array's address cannot be
+ * resolved). */
+#define SDA_SCRATCH_BYTES ((size_t)32 << 20)
+int sda_decode_attn_batch_noalloc(const sda_pool *pool, int32_t n_inst, const int32_t *page_table,
+                                  int64_t pt_stride, int32_t n_logical_pages, const int32_t *sel,
+                                  int64_t sel_stride, const int32_t *n_sel, int32_t max_sel,
+                                  const float *q, int32_t n_q, int32_t n_qheads,
+                                  float softmax_scale, int32_t chunk_cells, float *out,
+                                  float *lse, int32_t *gather_out, void *stream);
 
 /* The two passes of sda_decode_attn_batch, callable on their own.
  *

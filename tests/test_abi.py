@@ -51,10 +51,17 @@ def test_header_constants_match_binding():
         "PROMPT_MAX_ROWS": api.PROMPT_MAX_ROWS}
 
 
+def test_scratch_size_matches_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define SDA_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == api.SCRATCH_BYTES
+
+
 def test_status_strings():
     lib = api.library()
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert lib.sda_status_string(st)
+    assert b"SCRATCH" in lib.sda_status_string(api.SDA_ERR_SCRATCH)
 
 
 def _al(x):
@@ -369,3 +376,34 @@ def test_binding_rejects_bad_tensors(change, msg):
             a[key] = val
     with pytest.raises(ValueError, match=msg):
         api.decode_attn_batch(**a)
+
+
+def test_noalloc_rejects_before_launch():
+    """sda_decode_attn_batch_noalloc validates like sda_decode_attn_batch and
+    refuses a call whose chunk partials exceed the fixed device array, all
+    before it touches a device (no GPU here)."""
+    lib = api.library()
+    p = _pool()
+    def call(**kw):
+        a = dict(n_inst=2, pt=FAKE, pts=4, nlp=4, sel=FAKE, sels=10, nsel=FAKE, max_sel=10,
+                 q=FAKE, n_q=1, nh=12, scale=0.0625, chunk=256, out=FAKE, lse=FAKE, g=None)
+        a.update(kw)
+        return lib.sda_decode_attn_batch_noalloc(
+            C.byref(p), a["n_inst"], a["pt"], a["pts"], a["nlp"], a["sel"], a["sels"], a["nsel"],
+            a["max_sel"], a["q"], a["n_q"], a["nh"], a["scale"], a["chunk"], a["out"], a["lse"],
+            a["g"], None)
+    assert call(nsel=None) == api.SDA_ERR_INVALID_ARG
+    assert call(pts=3) == api.SDA_ERR_INVALID_ARG
+    assert call(sels=9) == api.SDA_ERR_INVALID_ARG
+    assert call(out=None) == api.SDA_ERR_INVALID_ARG
+    assert call(q=FAKE + 4) == api.SDA_ERR_INVALID_ARG
+    assert call(n_q=5, nh=13) == api.SDA_ERR_UNSUPPORTED
+    assert call(chunk=96) == api.SDA_ERR_UNSUPPORTED
+    assert call(n_inst=0) == api.SDA_OK
+    # 128 instances x 64 rows x 4,096 cells: four chunks per instance, whose
+    # partials (33.8 MB) exceed the array
+    big = dict(n_inst=128, n_q=4, nh=16, max_sel=4096, sels=4096, chunk=256)
+    assert not api.fused_single_launch(128, 4, 16, 4096, 256)
+    need = api.workspace_bytes(128, 4, 16, 4096, api.fused_chunk_cells(128, 4096, 256))
+    assert need > api.SCRATCH_BYTES
+    assert call(**big) == api.SDA_ERR_SCRATCH
