@@ -295,3 +295,78 @@ def make_append(name: str | None = None, seed: int | None = None, pos0=None, spr
     pos0 = np.broadcast_to(np.asarray(pos0, np.int32), (n_inst,)).copy()
     return AppendInputs(page_table=pt, pos0=pos0, k_new=k_new, v_new=v_new, pool_cells=cells,
                         workload=str(spec.get("workload", name or "custom_append")), seed=seed)
+
+
+# QSA block scoring and selection (the step that produces the selected cell
+# list).  The pages give the scorer's arguments (pooled block keys, dead
+# flags, indexer queries, per-row extents) but not its geometry; the
+# workload takes config 3's shape: 64 instances (16 sequences x 4 KV heads)
+# with 131,072-cell contexts cut into 512 blocks of 256 cells, 2 query
+# positions, and the top 64 blocks (16,384 cells, config 3's selection
+# size), with 4 indexer heads of 128 dims (one 2 KB pooled key per block).
+QSA_CONFIGS = {
+    "qsa_select_64inst_128k_2q": dict(n_inst=64, n_rows=2, n_heads=4, idx_dim=128,
+                                      block_cells=256, max_blocks=512, k_blocks=64,
+                                      context=131072 - 100, dead_frac=0.02),
+}
+
+
+@dataclasses.dataclass
+class QsaInputs:
+    pooled: np.ndarray     # float32 [n_inst][max_blocks][n_heads][idx_dim]
+    dead: np.ndarray       # uint8 [n_inst][max_blocks], 1 = dead block
+    q_idx: np.ndarray      # float32 [n_inst][n_rows][n_heads][idx_dim]
+    n_visible: np.ndarray  # int32 [n_inst][n_rows]: cells visible to each query row
+    block_cells: int
+    k_blocks: int
+    workload: str
+    seed: int
+
+    @property
+    def n_inst(self) -> int:
+        return int(self.pooled.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.pooled.shape[1])
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.q_idx.shape[1])
+
+
+def make_qsa(name: str | None = None, seed: int | None = None, context=None,
+             **overrides) -> QsaInputs:
+    """Pooled keys and indexer queries N(0, 1) (queries scaled by
+    1/sqrt(n_heads * idx_dim)), a fraction dead_frac of the blocks dead at
+    random; query row r of an instance sees context - n_rows + 1 + r cells
+    (consecutive verify positions at the end of its context).  context may be
+    a number or one per instance."""
+    spec = dict(QSA_CONFIGS[name]) if name is not None else {}
+    spec.update(overrides)
+    n_inst, n_rows = int(spec["n_inst"]), int(spec["n_rows"])
+    H, D = int(spec["n_heads"]), int(spec["idx_dim"])
+    R, B = int(spec["block_cells"]), int(spec["max_blocks"])
+    seed = 20261500 if seed is None else seed
+    if context is None:
+        context = spec.get("context", B * R)
+    ctx = np.broadcast_to(np.asarray(context, np.int64), (n_inst,))
+    children = np.random.SeedSequence(seed).spawn(n_inst)
+    pooled = np.empty((n_inst, B, H, D), np.float32)
+    q = np.empty((n_inst, n_rows, H, D), np.float32)
+    dead = np.zeros((n_inst, B), np.uint8)
+    frac = float(spec.get("dead_frac", 0.0))
+
+    def fill(i):
+        rng = np.random.Generator(np.random.PCG64(children[i]))
+        pooled[i] = rng.standard_normal((B, H, D), dtype=np.float32)
+        q[i] = rng.standard_normal((n_rows, H, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * D))
+        if frac > 0:
+            dead[i] = (rng.random(B) < frac).astype(np.uint8)
+
+    with _cf.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(n_inst)))
+    vis = (ctx[:, None] - n_rows + 1 + np.arange(n_rows)[None, :]).clip(0, 2**31 - 1).astype(np.int32)
+    return QsaInputs(pooled=pooled, dead=dead, q_idx=q, n_visible=vis, block_cells=R,
+                     k_blocks=int(spec["k_blocks"]),
+                     workload=str(spec.get("workload", name or "custom_qsa")), seed=int(seed))

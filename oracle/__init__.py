@@ -28,6 +28,7 @@ _f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
 _i8p = np.ctypeslib.ndpointer(np.int8, flags="C_CONTIGUOUS")
 _u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
 
 
 def build(force: bool = True, extra_flags: tuple = ()) -> str:
@@ -72,6 +73,11 @@ def _load():
     lib.oracle_prompt_attend.argtypes = [_i8p, _u16p, _i8p, _u16p, C.c_int64, C.c_int64, _i32p,
                                          C.c_int64, C.c_int64, _f32p, C.c_int64, C.c_int64,
                                          C.c_double, _i64p, C.c_int64, _f64p, _f64p]
+    lib.oracle_qsa_scores.restype = None
+    lib.oracle_qsa_scores.argtypes = [C.c_int64] * 6 + [_f32p, _u8p, _f32p, _i32p, _f64p]
+    lib.oracle_qsa_select.restype = None
+    lib.oracle_qsa_select.argtypes = [C.c_int64] * 4 + [_f64p, _i32p, C.c_int64, _i32p,
+                                                         C.c_int64, _i32p]
     lib.oracle_merge.restype = None
     lib.oracle_merge.argtypes = [C.c_int64, C.c_int64, C.c_int64, _f64p, _f64p, _f64p, _f64p,
                                  _f64p]
@@ -218,3 +224,36 @@ def merge(acc, m, l):
     lse = np.zeros((k * R,), np.float64)
     lib.oracle_merge(k * R, nc, D, a, mm, ll, out, lse)
     return out.reshape(k, R, D), lse.reshape(k, R)
+
+
+def qsa_scores(x) -> np.ndarray:
+    """Block scores float64 [n_inst][n_rows][max_blocks] of QSA inputs x
+    (pooled [n_inst][max_blocks][n_heads][idx_dim], dead [n_inst][max_blocks],
+    q_idx [n_inst][n_rows][n_heads][idx_dim], n_visible [n_inst][n_rows],
+    block_cells)."""
+    lib = _load()
+    pooled = _c(x.pooled, np.float32)
+    n_inst, max_blocks, n_heads, idx_dim = pooled.shape
+    q = _c(x.q_idx, np.float32)
+    n_rows = q.shape[1]
+    out = np.empty((n_inst, n_rows, max_blocks), np.float64)
+    lib.oracle_qsa_scores(n_inst, n_rows, n_heads, idx_dim, max_blocks, int(x.block_cells),
+                          pooled, _c(x.dead, np.uint8), q, _c(x.n_visible, np.int32), out)
+    return out
+
+
+def qsa_select(scores, n_visible, block_cells: int, k_blocks: int):
+    """Top-k selection from scores [n_inst][n_rows][max_blocks]: returns
+    (sel int32 [n_inst][k_blocks * block_cells], n_sel int32 [n_inst]);
+    entries past n_sel[i] are -1."""
+    lib = _load()
+    sc = _c(scores, np.float64)
+    n_inst, n_rows, max_blocks = sc.shape
+    stride = max(int(k_blocks) * int(block_cells), 1)
+    sel = np.full((n_inst, stride), -1, np.int32)
+    n_sel = np.zeros((n_inst,), np.int32)
+    lib.oracle_qsa_select(n_inst, n_rows, max_blocks, int(block_cells), sc,
+                          _c(n_visible, np.int32), int(k_blocks), sel, stride, n_sel)
+    if np.any(n_sel > stride):
+        raise ValueError("more selected cells than k_blocks * block_cells")
+    return sel, n_sel

@@ -368,3 +368,115 @@ void oracle_merge(int64_t n_units, int64_t n_chunks, int64_t head_dim, const dou
         lse[u] = M + log(L);
     }
 }
+
+/* ------------------------------------------------------------------------
+ * QSA block scorer and top-k selection (the step that produces the selected
+ * cell list the attention above reads).
+ *
+ * Source: Strata round-9 page, section "R9-gpu-9: QSA_ROWS at five and six
+ * queries": a block scorer for a few query rows takes pooled block keys,
+ * per-block dead flags, indexer queries, per-row extents ("steps"), the row
+ * count and the block capacity, and writes block scores; its geometry is an
+ * indexer head dimension, an indexer head count and a block size, and its
+ * tests compare the full scores and the selected ids (equal keys, dead-tail
+ * transitions, partial blocks, several live extents under one capacity).
+ * Section "R9-gpu-8" names the top-k that turns the scores into the
+ * selection.  The pages fix no arithmetic; the readings taken here:
+ *   - block b holds logical cells [b * R, (b + 1) * R) (R = block_cells);
+ *   - score of query row r for block b: the sum over indexer heads h of the
+ *     dot product of the row's indexer query q[r][h][.] with the block's
+ *     pooled key pooled[b][h][.]; -inf when the block is dead or when its
+ *     first cell is not visible to the row (b * R >= n_visible[r]);
+ *   - selection: each block's combined score is its maximum over the rows
+ *     (a block any verify position asks for); the k blocks with the highest
+ *     combined scores are taken, equal scores in increasing block order,
+ *     blocks at -inf never; the selected blocks, in increasing order, give
+ *     their cells below the instance's extent E = max_r n_visible[r]
+ *     (clipped to the capacity), so the list is sorted and a block at the
+ *     end of the context contributes only its visible cells.
+ * ------------------------------------------------------------------------ */
+
+/* scores [n_inst][n_rows][max_blocks] (fp64) from pooled fp32
+ * [n_inst][max_blocks][n_heads][idx_dim], dead uint8 [n_inst][max_blocks]
+ * (non-zero: dead), q_idx fp32 [n_inst][n_rows][n_heads][idx_dim] and
+ * n_visible int32 [n_inst][n_rows]. */
+void oracle_qsa_scores(int64_t n_inst, int64_t n_rows, int64_t n_heads, int64_t idx_dim,
+                       int64_t max_blocks, int64_t block_cells, const float *pooled,
+                       const uint8_t *dead, const float *q_idx, const int32_t *n_visible,
+                       double *scores) {
+    const int64_t hd = n_heads * idx_dim;
+#pragma omp parallel for schedule(static)
+    for (int64_t u = 0; u < n_inst * n_rows; ++u) {
+        const int64_t i = u / n_rows; /* row u % n_rows of instance i */
+        const float *q = q_idx + u * hd;
+        for (int64_t b = 0; b < max_blocks; ++b) {
+            double s = -INFINITY;
+            if (!dead[i * max_blocks + b] && b * block_cells < (int64_t)n_visible[u]) {
+                const float *k = pooled + (i * max_blocks + b) * hd;
+                s = 0.0;
+                for (int64_t h = 0; h < n_heads; ++h) {
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < idx_dim; ++d)
+                        dot += (double)q[h * idx_dim + d] * (double)k[h * idx_dim + d];
+                    s += dot;
+                }
+            }
+            scores[u * max_blocks + b] = s;
+        }
+    }
+}
+
+/* ranking of the blocks by combined score, for qsort: higher first, equal
+ * scores in increasing block order */
+typedef struct {
+    double c;
+    int64_t b;
+} ranked_t;
+
+static int rank_cmp(const void *x, const void *y) {
+    const ranked_t *a = x, *b = y;
+    if (a->c > b->c) return -1;
+    if (a->c < b->c) return 1;
+    return (a->b > b->b) - (a->b < b->b);
+}
+
+/* Top-k selection from scores [n_inst][n_rows][max_blocks] (any values; the
+ * tests pass the kernel's own fp32 scores as well as the oracle's): writes
+ * the selected cells to sel [n_inst][sel_stride] and their count to
+ * n_sel [n_inst]. */
+void oracle_qsa_select(int64_t n_inst, int64_t n_rows, int64_t max_blocks, int64_t block_cells,
+                       const double *scores, const int32_t *n_visible, int64_t k_blocks,
+                       int32_t *sel, int64_t sel_stride, int32_t *n_sel) {
+    ranked_t *rk = malloc((size_t)(max_blocks > 0 ? max_blocks : 1) * sizeof *rk);
+    int64_t *take = malloc((size_t)(max_blocks > 0 ? max_blocks : 1) * sizeof *take);
+    for (int64_t i = 0; i < n_inst; ++i) {
+        int64_t extent = 0;
+        for (int64_t r = 0; r < n_rows; ++r)
+            if ((int64_t)n_visible[i * n_rows + r] > extent) extent = n_visible[i * n_rows + r];
+        if (extent > max_blocks * block_cells) extent = max_blocks * block_cells;
+        for (int64_t b = 0; b < max_blocks; ++b) {
+            double c = -INFINITY;
+            for (int64_t r = 0; r < n_rows; ++r) {
+                double s = scores[(i * n_rows + r) * max_blocks + b];
+                if (s > c) c = s;
+            }
+            rk[b].c = c;
+            rk[b].b = b;
+            take[b] = 0;
+        }
+        qsort(rk, (size_t)max_blocks, sizeof *rk, rank_cmp);
+        for (int64_t j = 0; j < k_blocks && j < max_blocks && rk[j].c > -INFINITY; ++j)
+            take[rk[j].b] = 1;
+        int64_t n = 0;
+        for (int64_t b = 0; b < max_blocks; ++b) {
+            if (!take[b]) continue;
+            for (int64_t c = b * block_cells; c < (b + 1) * block_cells && c < extent; ++c) {
+                if (n < sel_stride) sel[i * sel_stride + n] = (int32_t)c; /* never past the row */
+                ++n;
+            }
+        }
+        n_sel[i] = (int32_t)n;
+    }
+    free(rk);
+    free(take);
+}

@@ -668,6 +668,172 @@ def pin_append_then_attend(O):
         assert abs(lse[0, 0, h] - exact) <= bound * (1 + 1e-6) + 1e-12
 
 
+# ----------------------------------------------------------------------------
+# QSA block scorer and top-k selection.  Readings (the pages give only the
+# scorer's arguments and tests): score = sum over indexer heads of the dot
+# product of the row's indexer query with the block's pooled key, -inf for a
+# dead block or one whose first cell the row cannot see; selection = the k
+# blocks with the highest maximum-over-rows score, equal scores by increasing
+# block index, expanded to their cells below the largest row extent.
+
+def qsa_case(pooled, q, dead, n_visible, R, k):
+    return gen.QsaInputs(pooled=np.asarray(pooled, np.float32), dead=np.asarray(dead, np.uint8),
+                         q_idx=np.asarray(q, np.float32),
+                         n_visible=np.asarray(n_visible, np.int32), block_cells=R, k_blocks=k,
+                         workload="pin", seed=0)
+
+
+def pin_qsa_hand_example(O):
+    """Two rows, two heads of two dims, four 16-cell blocks, worked out by
+    hand: row 0 sees 40 cells (blocks 0-2), row 1 all 64; block 2 is dead.
+    Row 0: b0 = (1+2) + 0 = 3, b1 = 3 + 2 = 5.  Row 1: b0 = 2 + 1 = 3,
+    b1 = 0 + 0 = 0, b3 = 4 + 2 = 6.  Combined: b0 3, b1 5, b3 6."""
+    pooled = [[[1, 2], [0, -1]], [[3, 0], [1, 1]], [[5, 5], [5, 5]], [[-1, 4], [2, 0]]]
+    q = [[[1, 1], [2, 0]], [[0, 1], [1, -1]]]
+    x = qsa_case([pooled], [q], [[0, 0, 1, 0]], [[40, 64]], 16, 2)
+    ninf = -np.inf
+    want = np.array([[[3, 5, ninf, ninf], [3, 0, ninf, 6]]])
+    assert np.array_equal(O.qsa_scores(x), want)
+    s = O.qsa_scores(x)
+    for k, blocks in ((2, [1, 3]), (3, [0, 1, 3]), (4, [0, 1, 3]), (1, [3]), (0, [])):
+        sel, n = O.qsa_select(s, x.n_visible, 16, k)
+        cells = [c for b in blocks for c in range(16 * b, 16 * b + 16)]
+        assert n[0] == len(cells) and list(sel[0, :n[0]]) == cells, (k, sel[0, :n[0]])
+    # row 1 sees 52 cells: block 3 contributes cells 48..51 only
+    sel, n = O.qsa_select(s, np.array([[40, 52]]), 16, 2)
+    assert list(sel[0, :n[0]]) == list(range(16, 32)) + [48, 49, 50, 51]
+
+
+def pin_qsa_unit_queries(O):
+    """A query that is a unit vector on (head h, dim d) scores each live
+    block with that component of its pooled key."""
+    rng = np.random.default_rng(61)
+    B, H, D = 9, 3, 8
+    pooled = rng.standard_normal((1, B, H, D)).astype(np.float32)
+    for h, d in ((0, 0), (2, 7), (1, 3)):
+        q = np.zeros((1, 1, H, D), np.float32)
+        q[0, 0, h, d] = 1
+        x = qsa_case(pooled, q, np.zeros((1, B)), [[B * 32]], 32, 3)
+        assert np.array_equal(O.qsa_scores(x)[0, 0], pooled[0, :, h, d].astype(np.float64))
+
+
+def pin_qsa_linearity(O):
+    """Scores are linear in the query: s(q1) + s(q2) = s(q1 + q2) and
+    s(-2 q) = -2 s(q), exactly for small-integer inputs."""
+    rng = np.random.default_rng(62)
+    B, H, D = 12, 2, 16
+    pooled = rng.integers(-8, 9, (1, B, H, D)).astype(np.float32)
+    q1 = rng.integers(-8, 9, (1, 1, H, D)).astype(np.float32)
+    q2 = rng.integers(-8, 9, (1, 1, H, D)).astype(np.float32)
+    mk = lambda q: O.qsa_scores(qsa_case(pooled, q, np.zeros((1, B)), [[B * 16]], 16, 1))
+    assert np.array_equal(mk(q1) + mk(q2), mk(q1 + q2))
+    assert np.array_equal(mk(-2 * q1), -2 * mk(q1))
+
+
+def pin_qsa_heads_add(O):
+    """The score is the sum of the per-head scores (each head scored as a
+    one-head scorer on its slice), and permuting the heads of both the query
+    and the keys changes nothing."""
+    rng = np.random.default_rng(63)
+    B, H, D = 10, 4, 8
+    pooled = rng.integers(-5, 6, (1, B, H, D)).astype(np.float32)
+    q = rng.integers(-5, 6, (1, 2, H, D)).astype(np.float32)
+    vis = [[B * 16, B * 16]]
+    full = O.qsa_scores(qsa_case(pooled, q, np.zeros((1, B)), vis, 16, 1))
+    parts = sum(O.qsa_scores(qsa_case(pooled[:, :, h:h + 1], q[:, :, h:h + 1], np.zeros((1, B)),
+                                      vis, 16, 1)) for h in range(H))
+    assert np.array_equal(full, parts)
+    perm = [2, 0, 3, 1]
+    permuted = O.qsa_scores(qsa_case(pooled[:, :, perm], q[:, :, perm], np.zeros((1, B)), vis, 16, 1))
+    assert np.array_equal(full, permuted)
+
+
+def pin_qsa_masks(O):
+    """A dead block scores -inf for every row; block b is visible to a row
+    exactly when b * R < n_visible (boundaries R b and R b + 1)."""
+    rng = np.random.default_rng(64)
+    B, H, D, R = 6, 1, 4, 16
+    pooled = rng.standard_normal((1, B, H, D)).astype(np.float32)
+    q = rng.standard_normal((1, 3, H, D)).astype(np.float32)
+    dead = np.zeros((1, B))
+    dead[0, 4] = 1
+    x = qsa_case(pooled, q, dead, [[3 * R, 3 * R + 1, 0]], R, 2)
+    s = O.qsa_scores(x)
+    assert np.all(np.isneginf(s[0, :, 4]))
+    assert np.all(np.isfinite(s[0, 0, :3])) and np.all(np.isneginf(s[0, 0, 3:]))
+    assert np.all(np.isfinite(s[0, 1, :4])) and np.all(np.isneginf(s[0, 1, 4:]))
+    assert np.all(np.isneginf(s[0, 2]))
+
+
+def _numpy_select(scores, n_visible, R, k):
+    """Top-k with numpy: lexsort by (-combined score, block index)."""
+    n_inst, _, B = scores.shape
+    out = []
+    for i in range(n_inst):
+        c = scores[i].max(axis=0)
+        order = np.lexsort((np.arange(B), -c))
+        blocks = sorted(int(b) for b in order[:k] if c[b] > -np.inf)
+        ext = min(int(np.max(n_visible[i])), B * R)
+        out.append([cell for b in blocks for cell in range(b * R, min(b * R + R, ext))])
+    return out
+
+
+def pin_qsa_select_numpy(O):
+    """Selection against numpy's lexsort on random scores with injected
+    ties, -inf entries, partial last blocks and several k."""
+    rng = np.random.default_rng(65)
+    for trial in range(12):
+        n_inst, n_rows, B, R = 3, int(rng.integers(1, 5)), int(rng.integers(1, 40)), 16
+        sc = rng.integers(-6, 7, (n_inst, n_rows, B)).astype(np.float64)  # many ties
+        sc[rng.random(sc.shape) < 0.2] = -np.inf
+        vis = rng.integers(0, B * R + 30, (n_inst, n_rows))
+        for k in (0, 1, 3, B // 2, B, B + 2):
+            sel, n = O.qsa_select(sc, vis, R, k)
+            want = _numpy_select(sc, vis, R, k)
+            for i in range(n_inst):
+                assert list(sel[i, :n[i]]) == want[i], (trial, k, i)
+
+
+def pin_qsa_select_brute(O):
+    """Brute force on tiny inputs: among all block subsets of size
+    min(k, live blocks), exactly one ranks every member above every
+    non-member (higher score, or equal score and lower index); the oracle's
+    selection is that subset."""
+    import itertools
+    rng = np.random.default_rng(66)
+    for trial in range(40):
+        B, R = int(rng.integers(1, 8)), 16
+        sc = rng.integers(-3, 4, (1, 2, B)).astype(np.float64)
+        sc[rng.random(sc.shape) < 0.3] = -np.inf
+        c = sc[0].max(axis=0)
+        live = [b for b in range(B) if c[b] > -np.inf]
+        k = int(rng.integers(0, B + 2))
+        kk = min(k, len(live))
+        above = lambda s, u: c[s] > c[u] or (c[s] == c[u] and s < u)
+        good = [set(S) for S in itertools.combinations(live, kk)
+                if all(above(s, u) for s in S for u in live if u not in S)]
+        assert len(good) == 1
+        sel, n = O.qsa_select(sc, np.array([[B * R, B * R]]), R, k)
+        got = sorted({int(v) // R for v in sel[0, :n[0]]})
+        assert got == sorted(good[0]), (trial, got, good)
+
+
+def pin_qsa_select_special(O):
+    """All scores equal: the lowest k blocks.  No live block: nothing.  k at
+    least the live count: every live block.  Extent 0: no cells."""
+    B, R = 10, 32
+    sel, n = O.qsa_select(np.zeros((1, 3, B)), np.array([[B * R] * 3]), R, 4)
+    assert list(sel[0, :n[0]]) == list(range(4 * R))
+    sel, n = O.qsa_select(np.full((2, 1, B), -np.inf), np.array([[B * R], [B * R]]), R, 4)
+    assert list(n) == [0, 0]
+    sc = np.full((1, 1, B), -np.inf)
+    sc[0, 0, [7, 2, 5]] = [1.0, -3.0, 0.5]
+    sel, n = O.qsa_select(sc, np.array([[B * R]]), R, 9)
+    assert list(sel[0, :n[0]]) == [c for b in (2, 5, 7) for c in range(b * R, b * R + R)]
+    sel, n = O.qsa_select(sc, np.array([[0]]), R, 9)
+    assert n[0] == 0
+
+
 ALL_PINS = [pin_half_decode, pin_textbook, pin_gather_exhaustive, pin_one_cell, pin_two_cells,
             pin_zero_query, pin_identical_keys, pin_worked_example, pin_merge_closed_form,
             pin_empty_and_masked, pin_permutation, pin_chunking, pin_score_shift,
@@ -675,4 +841,6 @@ ALL_PINS = [pin_half_decode, pin_textbook, pin_gather_exhaustive, pin_one_cell, 
             pin_brute_force_subsets, pin_prompt_textbook, pin_prompt_first_cell,
             pin_prompt_is_decode_of_prefix, pin_prompt_causal, pin_half_encode,
             pin_append_quantiser, pin_append_exact_rows, pin_append_placement,
-            pin_append_then_attend]
+            pin_append_then_attend, pin_qsa_hand_example, pin_qsa_unit_queries,
+            pin_qsa_linearity, pin_qsa_heads_add, pin_qsa_masks, pin_qsa_select_numpy,
+            pin_qsa_select_brute, pin_qsa_select_special]

@@ -74,6 +74,23 @@ MUTANTS = {
     "append_kv_swapped": ("quantise_row(v_new + t * head_dim, head_dim, v_codes + ph * head_dim,",
                           "quantise_row(k_new + t * head_dim, head_dim, v_codes + ph * head_dim,"),
     "append_scale_stride_ignored": ("k_scales + ph * scale_stride);", "k_scales + ph);"),
+    "qsa_dead_ignored": ("if (!dead[i * max_blocks + b] && b * block_cells < (int64_t)n_visible[u]) {",
+                         "if (b * block_cells < (int64_t)n_visible[u]) {"),
+    "qsa_visible_off_by_one": ("if (!dead[i * max_blocks + b] && b * block_cells < (int64_t)n_visible[u]) {",
+                               "if (!dead[i * max_blocks + b] && b * block_cells <= (int64_t)n_visible[u]) {"),
+    "qsa_head_dropped": ("for (int64_t h = 0; h < n_heads; ++h) {", "for (int64_t h = 1; h < n_heads; ++h) {"),
+    "qsa_dims_reversed": ("dot += (double)q[h * idx_dim + d] * (double)k[h * idx_dim + d];",
+                          "dot += (double)q[h * idx_dim + d] * (double)k[h * idx_dim + idx_dim - 1 - d];"),
+    "qsa_first_row_only": ("for (int64_t r = 0; r < n_rows; ++r) {\n                double s",
+                           "for (int64_t r = 0; r < 1; ++r) {\n                double s"),
+    "qsa_ties_reversed": ("return (a->b > b->b) - (a->b < b->b);", "return (a->b < b->b) - (a->b > b->b);"),
+    "qsa_lowest_scores": ("if (a->c > b->c) return -1;\n    if (a->c < b->c) return 1;",
+                          "if (a->c > b->c) return 1;\n    if (a->c < b->c) return -1;"),
+    "qsa_extent_not_clipped": ("c < (b + 1) * block_cells && c < extent;", "c < (b + 1) * block_cells;"),
+    "qsa_extent_min_of_rows": ("if ((int64_t)n_visible[i * n_rows + r] > extent) extent",
+                               "if ((int64_t)n_visible[i * n_rows + r] < extent) extent"),
+    "qsa_k_plus_one": ("for (int64_t j = 0; j < k_blocks && j < max_blocks", "for (int64_t j = 0; j <= k_blocks && j < max_blocks"),
+    "qsa_takes_masked": ("&& rk[j].c > -INFINITY; ++j)", "; ++j)"),
 }
 
 
