@@ -20,11 +20,13 @@ SDA_ERR_SCRATCH = -5
 SCRATCH_BYTES = 32 << 20  # the device array behind sda_decode_attn_batch_noalloc, per GPU
 PAGE_SIZE, HEAD_DIM, MAX_ROWS, CHUNK_ALIGN, MAX_CHUNKS = 16, 256, 64, 64, 65535
 PROMPT_MAX_ROWS = 65535 * 48
+QSA_MAX_ROWS, QSA_HD_ALIGN, QSA_MAX_HD, QSA_MAX_BLOCKS, QSA_MAX_K = 8, 64, 1024, 16384, 4096
 
 EXPORTED = ("sda_workspace_bytes", "sda_decode_attn_step", "sda_decode_attn_batch",
             "sda_decode_attn_batch_noalloc",
             "sda_chunk_batch", "sda_merge_batch", "sda_prompt_attn_batch", "sda_fused_chunk_cells",
-            "sda_fused_single_launch", "sda_kv_append_batch", "sda_status_string")
+            "sda_fused_single_launch", "sda_kv_append_batch", "sda_qsa_block_scores",
+            "sda_qsa_select", "sda_status_string")
 
 
 class SdaError(RuntimeError):
@@ -77,6 +79,10 @@ def library() -> C.CDLL:
         lib.sda_fused_chunk_cells.restype = C.c_int
         lib.sda_fused_single_launch.argtypes = [i32, i32, i32, i32, i32, C.POINTER(i32)]
         lib.sda_fused_single_launch.restype = C.c_int
+        lib.sda_qsa_block_scores.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        lib.sda_qsa_block_scores.restype = C.c_int
+        lib.sda_qsa_select.argtypes = [i32, i32, i32, i32, vp, vp, i32, vp, i64, vp, vp]
+        lib.sda_qsa_select.restype = C.c_int
         lib.sda_status_string.argtypes = [C.c_int]
         lib.sda_status_string.restype = C.c_char_p
         _lib = lib
@@ -411,6 +417,45 @@ def kv_append_batch(pool: Pool, page_table, pos0, k_new, v_new, stream=None,
                                        _ptr(v_new), n_new, _stream(stream))
     if st != SDA_OK:
         raise SdaError(st, "sda_kv_append_batch")
+
+
+def qsa_block_scores(pooled, dead, q_idx, n_visible, block_cells: int, scores, stream=None):
+    """Block scores: pooled float32 [n_inst][max_blocks][n_heads][idx_dim],
+    dead uint8 [n_inst][max_blocks], q_idx float32 [n_inst][n_rows][n_heads]
+    [idx_dim], n_visible int32 [n_inst][n_rows] (cells each row sees);
+    scores float32 [n_inst][n_rows][max_blocks] is written."""
+    _check(pooled, "pooled", torch.float32, (None, None, None, None))
+    n_inst, max_blocks, n_heads, idx_dim = (int(v) for v in pooled.shape)
+    _check(q_idx, "q_idx", torch.float32, (n_inst, None, n_heads, idx_dim))
+    n_rows = int(q_idx.shape[1])
+    _check(dead, "dead", torch.uint8, (n_inst, max_blocks))
+    _check(n_visible, "n_visible", torch.int32, (n_inst, n_rows))
+    _check(scores, "scores", torch.float32, (n_inst, n_rows, max_blocks))
+    _on(pooled=pooled, dead=dead, q_idx=q_idx, n_visible=n_visible, scores=scores)
+    st = library().sda_qsa_block_scores(n_inst, n_rows, n_heads, idx_dim, int(block_cells),
+                                        max_blocks, _ptr(pooled), _ptr(dead), _ptr(q_idx),
+                                        _ptr(n_visible), _ptr(scores), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_qsa_block_scores")
+
+
+def qsa_select(scores, n_visible, block_cells: int, k_blocks: int, sel, n_sel, stream=None):
+    """Top-k blocks of scores [n_inst][n_rows][max_blocks] expanded to sorted
+    cells: sel int32 [n_inst][>= k_blocks * block_cells] and n_sel int32
+    [n_inst] are written (the sel / n_sel arguments of decode_attn_batch)."""
+    _check(scores, "scores", torch.float32, (None, None, None))
+    n_inst, n_rows, max_blocks = (int(v) for v in scores.shape)
+    _check(n_visible, "n_visible", torch.int32, (n_inst, n_rows))
+    _check(sel, "sel", torch.int32, (n_inst, None))
+    if int(sel.shape[1]) < int(k_blocks) * int(block_cells):
+        raise ValueError("sel rows are shorter than k_blocks * block_cells")
+    _check(n_sel, "n_sel", torch.int32, (n_inst,))
+    _on(scores=scores, n_visible=n_visible, sel=sel, n_sel=n_sel)
+    st = library().sda_qsa_select(n_inst, n_rows, int(block_cells), max_blocks, _ptr(scores),
+                                  _ptr(n_visible), int(k_blocks), _ptr(sel), int(sel.shape[1]),
+                                  _ptr(n_sel), _stream(stream))
+    if st != SDA_OK:
+        raise SdaError(st, "sda_qsa_select")
 
 
 def to_device(x, device="cuda", interleave_scales=False):

@@ -452,6 +452,70 @@ int sda_kv_append_batch(const sda_pool_mut *pool, int32_t n_inst, const int32_t 
     return SDA_OK;
 }
 
+int sda_qsa_block_scores(int32_t n_inst, int32_t n_rows, int32_t n_heads, int32_t idx_dim,
+                         int32_t block_cells, int32_t max_blocks, const float *pooled,
+                         const uint8_t *dead, const float *q_idx, const int32_t *n_visible,
+                         float *scores, void *stream) {
+    if (n_inst < 0 || n_rows < 1 || n_heads < 1 || idx_dim < 1 || block_cells < 1 ||
+        max_blocks < 1)
+        return SDA_ERR_INVALID_ARG;
+    const int64_t hd = (int64_t)n_heads * idx_dim;
+    if (n_rows > SDA_QSA_MAX_ROWS || hd % SDA_QSA_HD_ALIGN || hd > SDA_QSA_MAX_HD ||
+        block_cells % SDA_PAGE_SIZE || (int64_t)max_blocks * block_cells > INT32_MAX ||
+        n_inst > 65535)
+        return SDA_ERR_UNSUPPORTED;
+    if (n_inst == 0) return SDA_OK;
+    if (!pooled || !dead || !q_idx || !n_visible || !scores || !aligned(pooled, 16) ||
+        !aligned(q_idx, 16) || !aligned(scores, 4))
+        return SDA_ERR_INVALID_ARG;
+    sda::QsaParams p;
+    memset(&p, 0, sizeof p);
+    p.pooled = pooled;
+    p.dead = dead;
+    p.q_idx = q_idx;
+    p.n_visible = n_visible;
+    p.scores = scores;
+    p.n_inst = n_inst;
+    p.n_rows = n_rows;
+    p.hd = (int32_t)hd;
+    p.block_cells = block_cells;
+    p.max_blocks = max_blocks;
+    (void)hipGetLastError();
+    return sda::launch_qsa_scores(p, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SDA_OK
+               : SDA_ERR_LAUNCH;
+}
+
+int sda_qsa_select(int32_t n_inst, int32_t n_rows, int32_t block_cells, int32_t max_blocks,
+                   const float *scores, const int32_t *n_visible, int32_t k_blocks,
+                   int32_t *sel, int64_t sel_stride, int32_t *n_sel, void *stream) {
+    if (n_inst < 0 || n_rows < 1 || block_cells < 1 || max_blocks < 1 || k_blocks < 0)
+        return SDA_ERR_INVALID_ARG;
+    if (n_rows > SDA_QSA_MAX_ROWS || block_cells % SDA_PAGE_SIZE ||
+        max_blocks > SDA_QSA_MAX_BLOCKS || k_blocks > SDA_QSA_MAX_K ||
+        (int64_t)max_blocks * block_cells > INT32_MAX)
+        return SDA_ERR_UNSUPPORTED;
+    if (sel_stride < (int64_t)k_blocks * block_cells) return SDA_ERR_INVALID_ARG;
+    if (n_inst == 0) return SDA_OK;
+    if (!scores || !n_visible || !n_sel || (k_blocks > 0 && !sel)) return SDA_ERR_INVALID_ARG;
+    sda::QsaParams p;
+    memset(&p, 0, sizeof p);
+    p.scores = const_cast<float *>(scores);
+    p.n_visible = n_visible;
+    p.sel = sel;
+    p.n_sel = n_sel;
+    p.sel_stride = sel_stride;
+    p.n_inst = n_inst;
+    p.n_rows = n_rows;
+    p.block_cells = block_cells;
+    p.max_blocks = max_blocks;
+    p.k_blocks = k_blocks;
+    (void)hipGetLastError();
+    return sda::launch_qsa_select(p, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SDA_OK
+               : SDA_ERR_LAUNCH;
+}
+
 const char *sda_status_string(int status) {
     switch (status) {
         case SDA_OK: return "SDA_OK";

@@ -123,6 +123,25 @@ struct AppendParams {
     int32_t n_new;
 };
 
+// QSA block scoring and selection (already validated).
+constexpr int kQsaMaxRows = 8;
+constexpr int kQsaMaxHd = 1024;        // n_heads * idx_dim, a multiple of 64
+constexpr int kQsaMaxBlocks = 16384;   // blocks per instance the selection holds in LDS
+constexpr int kQsaMaxK = 4096;
+struct QsaParams {
+    const float *pooled;       // [n_inst][max_blocks][hd]
+    const uint8_t *dead;       // [n_inst][max_blocks]
+    const float *q_idx;        // [n_inst][n_rows][hd]
+    const int32_t *n_visible;  // [n_inst][n_rows]
+    float *scores;             // [n_inst][n_rows][max_blocks]
+    int32_t *sel;              // [n_inst][sel_stride]
+    int32_t *n_sel;            // [n_inst]
+    int64_t sel_stride;
+    int32_t n_inst, n_rows, hd, block_cells, max_blocks, k_blocks;
+};
+hipError_t launch_qsa_scores(const QsaParams &p, hipStream_t s);
+hipError_t launch_qsa_select(const QsaParams &p, hipStream_t s);
+
 hipError_t launch_chunk(const Params &p, hipStream_t s);
 // Whether a call with both passes runs as one chunk-kernel launch that writes
 // the head outputs (every instance has at most two multi-tile chunks), and

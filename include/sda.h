@@ -343,6 +343,69 @@ int sda_kv_append_batch(const sda_pool_mut *pool, int32_t n_inst, const int32_t 
                         int64_t pt_stride, int32_t n_logical_pages, const int32_t *pos0,
                         const float *k_new, const float *v_new, int32_t n_new, void *stream);
 
+/* QSA block scoring and top-k selection: the step that produces the
+ * selected cell list (sel, n_sel) the decode entry points read.  The Strata
+ * round-9 page (section "R9-gpu-9: QSA_ROWS at five and six queries") gives
+ * the scorer's arguments -- pooled block keys, dead flags, indexer queries,
+ * per-row extents, the row count and the block capacity -- and its geometry
+ * (indexer head dimension, indexer head count, block size); section
+ * "R9-gpu-8" names the top-k.  The arithmetic is this library's reading:
+ *
+ *   block b of an instance holds logical cells [b * R, (b + 1) * R),
+ *   R = block_cells;
+ *   scores[i][r][b] = sum over indexer heads h of the dot product of
+ *                     q_idx[i][r][h][.] and pooled[i][b][h][.] (fp32), or
+ *                     -inf when dead[i][b] != 0 or b * R >= n_visible[i][r];
+ *   selection: the k_blocks blocks with the highest combined score
+ *              max_r scores[i][r][b] (equal scores in increasing block
+ *              order, -inf never), in increasing block order, each giving
+ *              its cells below E = max_r n_visible[i][r] (clipped to
+ *              max_blocks * R): a sorted cell list.
+ *
+ * sda_qsa_block_scores:
+ *   n_inst        host, in [0, 65535] (0: nothing is launched)
+ *   n_rows        host, query rows per instance, 1..SDA_QSA_MAX_ROWS
+ *   n_heads, idx_dim  host, >= 1; n_heads * idx_dim a multiple of
+ *                 SDA_QSA_HD_ALIGN, at most SDA_QSA_MAX_HD
+ *   block_cells   host, a positive multiple of SDA_PAGE_SIZE
+ *   max_blocks    host, >= 1, max_blocks * block_cells <= 2^31 - 1
+ *   pooled        float [n_inst][max_blocks][n_heads][idx_dim], 16-byte aligned
+ *   dead          uint8 [n_inst][max_blocks]
+ *   q_idx         float [n_inst][n_rows][n_heads][idx_dim], 16-byte aligned
+ *   n_visible     DEVICE int32 [n_inst][n_rows]: cells each row can see
+ *   scores        float [n_inst][n_rows][max_blocks] (written)
+ *   stream        hipStream_t (NULL = default stream)
+ * A block no row can use is not read.  Returns SDA_OK, SDA_ERR_INVALID_ARG,
+ * SDA_ERR_UNSUPPORTED or SDA_ERR_LAUNCH. */
+#define SDA_QSA_MAX_ROWS 8
+#define SDA_QSA_HD_ALIGN 64
+#define SDA_QSA_MAX_HD 1024
+#define SDA_QSA_MAX_BLOCKS 16384
+#define SDA_QSA_MAX_K 4096
+int sda_qsa_block_scores(int32_t n_inst, int32_t n_rows, int32_t n_heads, int32_t idx_dim,
+                         int32_t block_cells, int32_t max_blocks, const float *pooled,
+                         const uint8_t *dead, const float *q_idx, const int32_t *n_visible,
+                         float *scores, void *stream);
+
+/* sda_qsa_select: top-k selection and expansion to cells, one workgroup per
+ * instance, from scores laid out as sda_qsa_block_scores writes them (any
+ * values: -inf is never selected; other non-finite values are unspecified).
+ *   n_inst        host, >= 0 (0: nothing is launched)
+ *   n_rows, block_cells, n_visible  as above
+ *   max_blocks    host, 1..SDA_QSA_MAX_BLOCKS
+ *   k_blocks      host, 0..SDA_QSA_MAX_K
+ *   sel           int32 [n_inst][sel_stride]: the first n_sel[i] entries are
+ *                 written (increasing logical cell ids); the rest untouched
+ *   sel_stride    host, >= k_blocks * block_cells
+ *   n_sel         int32 [n_inst] (written): cells selected, at most
+ *                 k_blocks * block_cells
+ * The outputs are exactly the sel, sel_stride and n_sel arguments of
+ * sda_decode_attn_batch (with max_sel = k_blocks * block_cells).  Returns
+ * SDA_OK, SDA_ERR_INVALID_ARG, SDA_ERR_UNSUPPORTED or SDA_ERR_LAUNCH. */
+int sda_qsa_select(int32_t n_inst, int32_t n_rows, int32_t block_cells, int32_t max_blocks,
+                   const float *scores, const int32_t *n_visible, int32_t k_blocks,
+                   int32_t *sel, int64_t sel_stride, int32_t *n_sel, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *sda_status_string(int status);
 

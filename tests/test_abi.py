@@ -48,7 +48,9 @@ def test_header_constants_match_binding():
     assert {k: int(v) for k, v in defs.items()} == {
         "PAGE_SIZE": api.PAGE_SIZE, "HEAD_DIM": api.HEAD_DIM, "MAX_ROWS": api.MAX_ROWS,
         "CHUNK_ALIGN": api.CHUNK_ALIGN, "MAX_CHUNKS": api.MAX_CHUNKS,
-        "PROMPT_MAX_ROWS": api.PROMPT_MAX_ROWS}
+        "PROMPT_MAX_ROWS": api.PROMPT_MAX_ROWS, "QSA_MAX_ROWS": api.QSA_MAX_ROWS,
+        "QSA_HD_ALIGN": api.QSA_HD_ALIGN, "QSA_MAX_HD": api.QSA_MAX_HD,
+        "QSA_MAX_BLOCKS": api.QSA_MAX_BLOCKS, "QSA_MAX_K": api.QSA_MAX_K}
 
 
 def test_scratch_size_matches_binding():
@@ -407,3 +409,42 @@ def test_noalloc_rejects_before_launch():
     need = api.workspace_bytes(128, 4, 16, 4096, api.fused_chunk_cells(128, 4096, 256))
     assert need > api.SCRATCH_BYTES
     assert call(**big) == api.SDA_ERR_SCRATCH
+
+
+def test_qsa_rejects_before_launch():
+    """The QSA entry points validate geometry and pointers on the host (no GPU
+    here: every call below must fail before anything is launched)."""
+    lib = api.library()
+    def scores(**kw):
+        a = dict(n_inst=2, n_rows=2, n_heads=4, idx_dim=128, R=256, B=512, pooled=FAKE,
+                 dead=FAKE, q=FAKE, vis=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.sda_qsa_block_scores(a["n_inst"], a["n_rows"], a["n_heads"], a["idx_dim"],
+                                        a["R"], a["B"], a["pooled"], a["dead"], a["q"],
+                                        a["vis"], a["out"], None)
+    assert scores(n_rows=0) == api.SDA_ERR_INVALID_ARG
+    assert scores(n_rows=9) == api.SDA_ERR_UNSUPPORTED
+    assert scores(idx_dim=100) == api.SDA_ERR_UNSUPPORTED        # 400 not a multiple of 64
+    assert scores(n_heads=16) == api.SDA_ERR_UNSUPPORTED         # 2048 > 1024
+    assert scores(R=100) == api.SDA_ERR_UNSUPPORTED              # not a multiple of 16
+    assert scores(R=0) == api.SDA_ERR_INVALID_ARG
+    assert scores(B=0) == api.SDA_ERR_INVALID_ARG
+    assert scores(B=1 << 24, R=256) == api.SDA_ERR_UNSUPPORTED   # more than 2^31 cells
+    assert scores(n_inst=70000) == api.SDA_ERR_UNSUPPORTED
+    assert scores(pooled=None) == api.SDA_ERR_INVALID_ARG
+    assert scores(q=FAKE + 4) == api.SDA_ERR_INVALID_ARG
+    assert scores(n_inst=0) == api.SDA_OK
+    def select(**kw):
+        a = dict(n_inst=2, n_rows=2, R=256, B=512, sc=FAKE, vis=FAKE, k=64, sel=FAKE,
+                 stride=64 * 256, nsel=FAKE)
+        a.update(kw)
+        return lib.sda_qsa_select(a["n_inst"], a["n_rows"], a["R"], a["B"], a["sc"], a["vis"],
+                                  a["k"], a["sel"], a["stride"], a["nsel"], None)
+    assert select(k=-1) == api.SDA_ERR_INVALID_ARG
+    assert select(k=4097) == api.SDA_ERR_UNSUPPORTED
+    assert select(B=16385) == api.SDA_ERR_UNSUPPORTED
+    assert select(stride=64 * 256 - 1) == api.SDA_ERR_INVALID_ARG
+    assert select(nsel=None) == api.SDA_ERR_INVALID_ARG
+    assert select(sel=None) == api.SDA_ERR_INVALID_ARG
+    assert select(sc=None) == api.SDA_ERR_INVALID_ARG
+    assert select(n_inst=0) == api.SDA_OK
