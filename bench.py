@@ -24,7 +24,10 @@ also timed as separate calls for reference; "prompt_attention" = the prompt
 workload of the same pages (32K-cell INT8 context, 2,048 causal queries x 12
 heads) through sda_prompt_attn_batch, with its matrix-core roofline;
 "kv_append" = the INT8 KV append of 64 x 2,048 new rows into 32K-cell pools
-through sda_kv_append_batch, cold, with its HBM roofline.
+through sda_kv_append_batch, cold, with its HBM roofline; "qsa_selection" =
+the QSA block scorer and top-k selection (64 instances x 512 blocks of 256
+cells, top 64) through sda_qsa_block_scores and sda_qsa_select, cold, with
+the scorer's HBM roofline.
 """
 from __future__ import annotations
 
@@ -223,6 +226,29 @@ def time_passes(cases, iters, flush=None):
         for k, (e0, e1, e2) in enumerate(row):
             res[k].append((e0.elapsed_time(e1), e1.elapsed_time(e2)))
     return res
+
+
+def time_passes_at(cases, iters, chunk, flush=None):
+    """time_passes at a given chunk size (the workload's stated one) instead
+    of the call's."""
+    import torch
+    evs = []
+    for _ in range(iters):
+        row = []
+        for c in cases:
+            if flush is not None:
+                flush()
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            c.chunk_pass(chunk)
+            e1.record()
+            c.merge_pass(chunk)
+            e2.record()
+            row.append((e0, e1, e2))
+        evs.append(row)
+    torch.cuda.synchronize()
+    return [[(e0.elapsed_time(e1), e1.elapsed_time(e2)) for (e0, e1, e2) in [r[k] for r in evs]]
+            for k in range(len(cases))]
 
 
 def graph_of(fn, reps):
@@ -489,6 +515,91 @@ def append_section(iters, flush):
     }
 
 
+def qsa_bytes(x):
+    """Algorithmic bytes of the scorer (the pooled keys of every block some
+    row can use, the queries, dead flags and extents read, the scores
+    written) and of the selection (the scores read, the cell list and counts
+    written), for inputs x and the cell counts n_sel."""
+    R = x.block_cells
+    first = np.arange(x.max_blocks)[None, :] * R
+    usable = (x.dead == 0) & (first < x.n_visible.max(axis=1)[:, None])
+    hd = x.pooled.shape[2] * x.pooled.shape[3]
+    n_scores = x.n_inst * x.n_rows * x.max_blocks
+    scorer = (int(usable.sum()) * hd * 4 + x.q_idx.size * 4 + x.dead.size + x.n_visible.size * 4
+              + n_scores * 4)
+    return scorer, usable
+
+
+def qsa_case():
+    import torch
+    from decode_attention_sparse_amd import api, inputs
+    x = inputs.make_qsa("qsa_select_64inst_128k_2q")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    pooled, dead, q, vis = t(x.pooled), t(x.dead), t(x.q_idx), t(x.n_visible)
+    scores = torch.empty((x.n_inst, x.n_rows, x.max_blocks), device="cuda")
+    sel = torch.empty((x.n_inst, x.k_blocks * x.block_cells), dtype=torch.int32, device="cuda")
+    n_sel = torch.empty((x.n_inst,), dtype=torch.int32, device="cuda")
+
+    def score():
+        api.qsa_block_scores(pooled, dead, q, vis, x.block_cells, scores)
+
+    def select():
+        api.qsa_select(scores, vis, x.block_cells, x.k_blocks, sel, n_sel)
+    return x, score, select, n_sel
+
+
+def qsa_section(iters, flush):
+    """The QSA selection workload: the scorer and the top-k selection, each
+    timed as eager calls with the caches evicted before each (HIP events on
+    the launch stream), and the two back to back as one selection."""
+    import torch
+    x, score, select, n_sel = qsa_case()
+    for _ in range(5):
+        flush()
+        score()
+        select()
+    torch.cuda.synchronize()
+    t = {"scores": [], "select": [], "both": []}
+    for _ in range(iters):
+        for name, fns in (("scores", (score,)), ("select", (select,)), ("both", (score, select))):
+            flush()
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            for f in fns:
+                f()
+            e1.record()
+            t[name].append((e0, e1))
+    torch.cuda.synchronize()
+    us = {k: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in t.items()}
+    cells = int(n_sel.cpu().numpy().sum())
+    scorer_bytes, usable = qsa_bytes(x)
+    select_bytes = x.n_inst * x.n_rows * x.max_blocks * 4 + cells * 4 + x.n_inst * 4
+    gbs = scorer_bytes / (us["scores"] * 1e-6) / 1e9
+    return {
+        "workload": x.workload,
+        "config": {"instances": x.n_inst, "query_rows": x.n_rows, "indexer_heads":
+                   int(x.pooled.shape[2]), "idx_dim": int(x.pooled.shape[3]),
+                   "block_cells": x.block_cells, "blocks_per_instance": x.max_blocks,
+                   "k_blocks": x.k_blocks, "visible_cells": [int(v) for v in x.n_visible[0]],
+                   "dead_blocks": int(x.dead.sum())},
+        "us_scores_median": round(us["scores"], 3),
+        "us_select_median": round(us["select"], 3),
+        "us_selection_median": round(us["both"], 3),
+        "selected_cells": cells,
+        "blocks_scored_per_s": round(x.n_inst * x.max_blocks / (us["both"] * 1e-6), 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "qsa_scores_kernel",
+                     "algorithmic_bytes_per_launch": scorer_bytes,
+                     "launch_us_median": round(us["scores"], 3),
+                     "note": f"pooled keys of the {int(usable.sum())} blocks some row can use, "
+                             "queries, flags and extents read, scores written"},
+        "select_GBps_algorithmic": round(select_bytes / (us["select"] * 1e-6) / 1e9, 1),
+        "timing": f"{iters} eager calls of each after 5 untimed ones, caches evicted before "
+                  "each by reading a 1 GiB buffer, HIP events around the call",
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -512,6 +623,9 @@ def main(argv=None):
     ap.add_argument("--no-append", action="store_true", help="skip the KV append workload")
     ap.add_argument("--only-append", action="store_true",
                     help="only three eager KV append calls (for profiling)")
+    ap.add_argument("--no-qsa", action="store_true", help="skip the QSA selection workload")
+    ap.add_argument("--only-qsa", action="store_true",
+                    help="only three eager QSA scorer + selection calls (for profiling)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size "
                          "reference dispatch for HBM byte counters)")
@@ -522,8 +636,8 @@ def main(argv=None):
         return 2
     # measured read ceilings for the access shapes of the chunk pass; run as a
     # child process before this process touches the GPU
-    ceiling = (None if (a.no_ceiling or a.only_batched or a.only_prompt or a.only_append)
-               else gather_ceiling())
+    ceiling = (None if (a.no_ceiling or a.only_batched or a.only_prompt or a.only_append
+                        or a.only_qsa) else gather_ceiling())
     import torch
     from decode_attention_sparse_amd import api, inputs
     api.library()
@@ -541,6 +655,15 @@ def main(argv=None):
         x, call = append_case()
         for _ in range(3):
             call()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": x.workload, "calls": 3}), flush=True)
+        return 0
+
+    if a.only_qsa:
+        x, score, select, _ = qsa_case()
+        for _ in range(3):
+            score()
+            select()
         torch.cuda.synchronize()
         print(json.dumps({"workload": x.workload, "calls": 3}), flush=True)
         return 0
@@ -687,10 +810,14 @@ def main(argv=None):
                      "bytes_per_step": bytes_sum, "call_us_per_step": round(call_us_sum, 3)},
         "per_query_count": per_q,
         "pages_600_cells_per_query_count": per_q600,
+        "value_cold": round(cells_step / (sum(cold_us.values()) * 1e-6), 1),
+        "ms_per_step_cold": round(sum(cold_us.values()) * 1e-3, 6),
         "cold_us_per_call_median": cold_us,
         "cold_us_per_call_p10_p90": cold_spread,
         "cold_note": "200 eager calls per query count, caches evicted before each by reading a "
-                     "1 GiB buffer, HIP events around each call",
+                     "1 GiB buffer, HIP events around each call; value_cold = the step's cells "
+                     "over the sum of the four cold medians (value: K back-to-back steps, warm, "
+                     "as the pages' 200-call loop)",
         "hbm_read_ceiling_measured": ceiling,
         "vs_baseline_ref": "pages' v3 kernel on RTX 2080 Ti, sum over q=1..4 of chunk+merge us (context, other hardware)",
         "wall_s_timed_region": round(wall, 3),
@@ -708,6 +835,11 @@ def main(argv=None):
             n_warm = warm_up([c], flush)
             d = summarize(c, time_calls([c], a.batched_iters, flush=flush)[0],
                           time_passes([c], a.batched_iters, flush=flush)[0])
+            st = time_passes_at([c], a.batched_iters, x.chunk, flush=flush)[0]
+            d[f"two_passes_at_stated_chunk_{x.chunk}_us"] = {
+                "chunk_us_median": round(float(np.median([u[0] for u in st])) * 1e3, 3),
+                "merge_us_median": round(float(np.median([u[1] for u in st])) * 1e3, 3),
+                "sum_us_median": round(float(np.median([u[0] + u[1] for u in st])) * 1e3, 3)}
             nch = -(-int(x.sel.shape[1]) // c.fused_chunk)
             d.update({"instances": x.n_inst, "n_q": x.n_q, "selected_cells_per_instance":
                       int(x.sel.shape[1]), "chunk": x.chunk, "call_chunk_cells": c.fused_chunk,
@@ -747,6 +879,15 @@ def main(argv=None):
         result["kv_append"] = d
         print(f"# {d['workload']}: {d['us_per_call_median']} us/call, {d['roofline']['achieved']} "
               f"GB/s ({d['roofline']['frac']*100:.1f}% of HBM peak)", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    # ---- QSA block scoring and top-k selection (the step before the path)
+    if not a.no_qsa:
+        d = qsa_section(a.batched_iters, flush)
+        result["qsa_selection"] = d
+        print(f"# {d['workload']}: scores {d['us_scores_median']} us ({d['roofline']['achieved']} "
+              f"GB/s, {d['roofline']['frac']*100:.1f}% of HBM peak), select "
+              f"{d['us_select_median']} us", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
 
     if not a.no_cpu:
