@@ -26,20 +26,31 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-PROBE_SRC = os.path.join(PKG, "probes", "gather_ceiling.hip")
+PROBES = {
+    # name: extra link flags.  gather_ceiling: the HBM read ceilings that
+    # `bench.py --gather-ceiling` reports; valu_chunk: the vector-ALU chunk
+    # pass variants timed beside the library (loads libsda.so at run time).
+    "gather_ceiling": [],
+    "valu_chunk": ["-ldl"],
+}
 PROBE_BIN = os.path.join(PKG, "probes", "gather_ceiling")
 
 
 def build_probe(verbose: bool = False) -> str:
-    """The standalone HBM read-ceiling probe run by `bench.py --gather-ceiling`."""
+    """The standalone measurement programs under probes/ (not part of the library)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = PROBE_BIN + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
-    os.replace(tmp, PROBE_BIN)
+    for name, link in PROBES.items():
+        src = os.path.join(PKG, "probes", name + ".hip")
+        out = os.path.join(PKG, "probes", name)
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", src, "-o", tmp, *link]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+        os.replace(tmp, out)
     return PROBE_BIN
 
 
