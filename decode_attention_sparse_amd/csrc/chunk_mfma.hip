@@ -221,33 +221,32 @@ struct RowBlock {
         for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
 
-    // One tile: the softmax and V accumulation of the tile whose scores are
-    // in su (V rows vb, V scales vs), and the scores of
-    // the next tile (K rows kb, K scales ks, bias 0 or -inf per cell) into su,
-    // or -inf everywhere when next_ok is false.  kCausal: cells of the next
-    // tile past index lim (this lane's row's last visible cell, counted from
-    // the tile's first cell) are masked too.  The two halves are independent
-    // (score() and stats() + accumulate()); a one-tile chunk runs them one
-    // after the other (tile()), with the same arithmetic.
+    // One step of the pipeline: the softmax and V accumulation of the tile
+    // whose scores are in su (V rows vb, V scales vs), and the scores of the
+    // next tile (K rows kb, K scales ks, biases bias_t) into su.  kCausal:
+    // cells of the next tile past index lim (this lane's row's last visible
+    // cell, counted from the tile's first cell) are masked too.  The two
+    // halves are independent (score() and stats() + accumulate()), so the
+    // matrix-core and vector work of neighbouring tiles interleave; a
+    // pipeline's first step runs only the scores, its last only the
+    // accumulation, and a one-tile chunk the two one after the other
+    // (tile()), with the same arithmetic.
     template <bool kCausal = false>
     __device__ __forceinline__ void step(const int8_t *kb, const float *ks_t, const float *bias_t,
-                                         bool next_ok, const int8_t *vb, const float *vs_t,
-                                         int dh, int lim = 0) {
+                                         const int8_t *vb, const float *vs_t, int dh, int lim = 0) {
         const Stats st = stats();
         v4f sn[4];
-        score<kCausal>(sn, kb, ks_t, bias_t, next_ok, lim);
+        score<kCausal>(sn, kb, ks_t, bias_t, lim);
         accumulate(st, vb, vs_t, dh);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
     }
 
     // A whole one-tile chunk: its scores, then their softmax and V
-    // accumulation.  The same state as step() on the tile followed by step()
-    // with next_ok false, without the halves that change nothing (the softmax
-    // of the initial -inf scores, the scores of a tile past the end).
+    // accumulation.
     __device__ __forceinline__ void tile(const int8_t *kb, const float *ks_t, const float *bias_t,
                                          const int8_t *vb, const float *vs_t, int dh) {
-        score(su, kb, ks_t, bias_t, true);
+        score(su, kb, ks_t, bias_t);
         accumulate(stats(), vb, vs_t, dh);
     }
 
@@ -273,13 +272,13 @@ struct RowBlock {
         return st;
     }
 
-    // Scores of a tile: u = (AB + C/2^8) * k_scale + bias, into sn (-inf
-    // everywhere when next_ok is false; kCausal and lim as in step()).
+    // Scores of a tile: u = (AB + C/2^8) * k_scale + bias, into sn (kCausal
+    // and lim as in step()).
     template <bool kCausal = false>
     __device__ __forceinline__ void score(v4f (&sn)[4], const int8_t *kb, const float *ks_t,
-                                          const float *bias_t, bool next_ok, int lim = 0) {
+                                          const float *bias_t, int lim = 0) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) sn[cb] = score_block(cb, kb, ks_t, bias_t, next_ok);
+        for (int cb = 0; cb < 4; ++cb) sn[cb] = score_block(cb, kb, ks_t, bias_t);
         if constexpr (kCausal) {
             if (__any(lim < kTile - 1)) {  // only tiles that reach past some row's position
 #pragma unroll
@@ -295,9 +294,9 @@ struct RowBlock {
     }
 
     // The scores of this lane's 4 cells of cell block cb (cells 16 cb to
-    // 16 cb + 15 of the tile), -inf when next_ok is false.
+    // 16 cb + 15 of the tile).
     __device__ __forceinline__ v4f score_block(int cb, const int8_t *kb, const float *ks_t,
-                                               const float *bias_t, bool next_ok) {
+                                               const float *bias_t) {
         const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
         v4i ka[4];
 #pragma unroll
@@ -317,7 +316,7 @@ struct RowBlock {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
-            sn[u] = next_ok ? fmaf(tq, ks[u], bs[u]) : -INFINITY;
+            sn[u] = fmaf(tq, ks[u], bs[u]);
         }
         return sn;
     }
@@ -335,7 +334,7 @@ struct RowBlock {
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int cb = kPer * dh + k;
-            xs[64 * cb + lane] = score_block(cb, kb, ks_t, bias_t, true);
+            xs[64 * cb + lane] = score_block(cb, kb, ks_t, bias_t);
         }
         __syncthreads();
 #pragma unroll
@@ -354,7 +353,9 @@ struct RowBlock {
         // fma(w, W, 2^23): X = 2^16 a + 2^8 b + c with balanced digits b, c in
         // [-128, 127] (a in [0, 127]): c = byte 0 of X, b = byte 1 of X + 2^7,
         // a = byte 2 of X + 2^7 + 2^15 (bit 23 of the float pattern, the
-        // exponent's lowest bit, is 0 in [2^23, 2^24))
+        // exponent's lowest bit, is 0 in [2^23, 2^24)).  Byte 1 of
+        // X + 2^7 + 2^15 is b + 2^7 modulo 2^8: b is read there, its top bit
+        // flipped.
         float psum = 0.f;
         float wt[4][4];
         float wmax = 0.f;
@@ -376,21 +377,20 @@ struct RowBlock {
         v4i xa, xb, xc;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            unsigned xs[4], x1[4], x2[4];
+            unsigned xs[4], x2[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 xs[u] = __float_as_uint(fmaf(wt[cb][u], W, kRound));
-                x1[u] = xs[u] + 128u;
                 x2[u] = xs[u] + 32896u;
             }
             const unsigned c01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
             const unsigned c23 = __builtin_amdgcn_perm(xs[3], xs[2], 0x04000c0cu);
-            const unsigned b01 = __builtin_amdgcn_perm(x1[1], x1[0], 0x0c0c0501u);
-            const unsigned b23 = __builtin_amdgcn_perm(x1[3], x1[2], 0x05010c0cu);
+            const unsigned b01 = __builtin_amdgcn_perm(x2[1], x2[0], 0x0c0c0501u);
+            const unsigned b23 = __builtin_amdgcn_perm(x2[3], x2[2], 0x05010c0cu);
             const unsigned a01 = __builtin_amdgcn_perm(x2[1], x2[0], 0x0c0c0602u);
             const unsigned a23 = __builtin_amdgcn_perm(x2[3], x2[2], 0x06020c0cu);
             xa[cb] = (int)(a01 | a23);
-            xb[cb] = (int)(b01 | b23);
+            xb[cb] = (int)((b01 | b23) ^ 0x80808080u);
             xc[cb] = (int)(c01 | c23);
         }
         l_part = fmaf(l_part, corr, psum);
@@ -746,39 +746,57 @@ void chunk_mfma_kernel(Params p, int cpw) {
     if constexpr (SP > 1) rb.shift(pipe * 2 * kBuf, pipe * 4 * kTile);
     // prompt: this row's last visible cell (its position)
     const int64_t lim_row = kPrompt ? pos0 + (row0 + row) / p.n_qheads : 0;
-    for (int t = -4; t < n_iter; ++t) {
-        if (t >= -1) {
-            // two pipelines: this step reads what the producer wrote in its
-            // step t - 1 (and earlier)
-            if constexpr (SP > 1)
-                if (!flag_wait(&ready_f[pipe], t - 1)) stuck_f = 1;
-            // Both halves of a step run every iteration (no validity branches,
-            // so the scheduler can interleave them); a tile outside
-            // [0, n_tiles) has all scores at -inf and changes nothing.
-            const bool next_ok = (t + 1 >= 0) && (t + 1 < n_tiles);
-            const int b1 = (t + 1) & 1, m1 = (t + 1) & 3;
-            const int b0 = t & 1, m0 = t & 3;
-            if constexpr (kPrompt) {
-                // the scores of tile t + 1, whose first cell is j_begin + 64 (t + 1)
-                const int64_t lim = lim_row - (j_begin + (int64_t)(t + 1) * kTile);
-                rb.template step<true>(kbuf[b1], ks_s[m1], bias_s[m1], next_ok, vbuf[b0], vs_s[m0],
-                                       dh, (int)max((int64_t)-1, min(lim, (int64_t)kTile)));
-            } else {
-                rb.step(kbuf_p[0][b1], ks_p[0][m1], bias_p[0][m1], next_ok, vbuf_p[0][b0],
-                        vs_p[0][m0], dh);
-            }
-            // end of a chunk: emit its partial, start afresh
-            if (!kPrompt && !kFinal && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
-                rb.emit(p, ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row, row, g, dh);
-                rb.reset();
-            }
-            if constexpr (SP > 1)
-                flag_post(&done_f[pipe][wave], t);  // this step's LDS reads are done
-        }
+    // Steps t = -4 .. n_iter - 1, one barrier each (the producer's count).
+    // The halves of step t are the scores of tile t + 1 and the softmax and
+    // V accumulation of tile t: step -1 runs only the former, step
+    // n_tiles - 1 only the latter, steps past a shorter pipeline's tiles
+    // neither; each form has a loop of its own (no branch inside a step).
+    auto sync = [&]() {
         if constexpr (SP == 1)
             __syncthreads();
         else
             __builtin_amdgcn_sched_barrier(0);  // keep steps apart, as the barrier did
+    };
+    // two pipelines: step t reads what the producer wrote in its step t - 1
+    // (and earlier)
+    auto begin_step = [&](int t) {
+        if constexpr (SP > 1)
+            if (!flag_wait(&ready_f[pipe], t - 1)) stuck_f = 1;
+    };
+    auto end_step = [&](int t) {
+        // end of a chunk: emit its partial, start afresh
+        if (!kPrompt && !kFinal && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
+            rb.emit(p, ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row, row, g, dh);
+            rb.reset();
+        }
+        if constexpr (SP > 1) flag_post(&done_f[pipe][wave], t);  // this step's LDS reads are done
+        sync();
+    };
+    // prompt: the mask limit of tile t + 1, whose first cell is j_begin + 64 (t + 1)
+    auto lim_next = [&](int t) {
+        return kPrompt ? (int)max((int64_t)-1, min(lim_row - (j_begin + (int64_t)(t + 1) * kTile),
+                                                   (int64_t)kTile))
+                       : 0;
+    };
+    for (int t = -4; t < -1; ++t) sync();
+    begin_step(-1);
+    if (n_tiles > 0) rb.template score<kPrompt>(rb.su, kbuf_p[0][0], ks_p[0][0], bias_p[0][0], lim_next(-1));
+    end_step(-1);
+    for (int t = 0; t < n_tiles - 1; ++t) {
+        begin_step(t);
+        rb.template step<kPrompt>(kbuf_p[0][(t + 1) & 1], ks_p[0][(t + 1) & 3], bias_p[0][(t + 1) & 3],
+                                  vbuf_p[0][t & 1], vs_p[0][t & 3], dh, lim_next(t));
+        end_step(t);
+    }
+    if (n_tiles > 0) {
+        const int t = n_tiles - 1;
+        begin_step(t);
+        rb.accumulate(rb.stats(), vbuf_p[0][t & 1], vs_p[0][t & 3], dh);
+        end_step(t);
+    }
+    for (int t = n_tiles; t < n_iter; ++t) {
+        begin_step(t);
+        end_step(t);
     }
     if constexpr (kPrompt)
         rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
@@ -958,8 +976,8 @@ __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out,
 }
 
 // Chunks of one tile (64 cells) in a latency-bound grid: workgroup =
-// (instance, chunk, blockIdx.z), holding the 16 RB query rows from row
-// 16 RB blockIdx.z on, with DS * RB compute waves and one producer wave
+// (instance, chunk, row group z), holding the 16 RB query rows from row
+// 16 RB z on, with DS * RB compute waves and one producer wave
 // that stages the tile in three round trips (the pipelined kernel takes five
 // steps for one tile).  The compute waves then score the tile and run its
 // softmax and V accumulation (RowBlock::tile: the arithmetic the pipelined
@@ -967,7 +985,14 @@ __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out,
 // group each score half the cell blocks and exchange them in LDS,
 // RowBlock::tile_shared), so the partial is bit for bit the same whichever
 // kernel or workgroup holds a row.
-template <int RB, int DS>
+//
+// kGrouped: one workgroup per (tile, row group), launched as a
+// one-dimensional grid of ceil(T / 8) * 8 * G workgroups (T tiles, G row
+// groups).  Workgroups go to the 8 XCDs in turn by linear id, so the id is
+// mapped to make the G workgroups of a tile share an XCD: each tile is then
+// gathered from memory into one L2 and staged again from there, instead of
+// once per row group.  Ids past the last tile exit at once.
+template <int RB, int DS, bool kGrouped = false>
 __global__ __launch_bounds__(64 * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu(2, 2)))  // at most 256 registers: no AGPR copies
 void chunk_tile_kernel(Params p) {
@@ -984,8 +1009,18 @@ void chunk_tile_kernel(Params p) {
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int i = blockIdx.x;  // instance
-    const int c = blockIdx.y;  // chunk = tile
+    int i = blockIdx.x;  // instance
+    int c = blockIdx.y;  // chunk = tile
+    int z = 0;           // row group
+    if constexpr (kGrouped) {
+        const int n_groups = (p.n_rows + 16 * RB - 1) / (16 * RB);
+        const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+        const int item = (k / n_groups) * 8 + xcd;  // the XCD's (k / G)-th tile
+        if (item >= p.n_inst * p.n_chunks) return;
+        i = item / p.n_chunks;
+        c = item % p.n_chunks;
+        z = k % n_groups;
+    }
     const int n = count_of(p, i);
     const int j_begin = c * kTile;
     if (j_begin >= n) return;  // this instance has fewer chunks
@@ -993,14 +1028,14 @@ void chunk_tile_kernel(Params p) {
 
     if (wave == kProducer) {
         // every row group's workgroup stages the tile; one writes gather_out
-        stage_tile(p, blockIdx.z == 0 ? p.gather_out : nullptr, i, j_begin, j_end, lane, kbuf,
+        stage_tile(p, z == 0 ? p.gather_out : nullptr, i, j_begin, j_end, lane, kbuf,
                    vbuf, ks_s, vs_s, bias_s, p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
         __syncthreads();
         if constexpr (kShared) __syncthreads();  // the compute waves' score exchange
         return;
     }
     const int g = lane >> 4, l16 = lane & 15;
-    const int row = ((int)blockIdx.z * RB + wave / DS) * 16 + l16;
+    const int row = (z * RB + wave / DS) * 16 + l16;
     const int dh = wave % DS;
     const int R = p.n_rows;
     RowBlock<kDB> rb;
@@ -1033,13 +1068,15 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
     // tile at once.  While the grid still fits one workgroup per CU with a
     // workgroup per 16-row group, each row group gets its own (its V
     // accumulation split over two waves): the tile's compute then takes the
-    // time of one group's, and the extra stagings of the tile are L2 hits.
-    // Otherwise all groups share one workgroup (a single group still splits
-    // its V accumulation; with more groups that measured slower).
+    // time of one group's, and the extra stagings of the tile are L2 hits
+    // (the groups of a tile share an XCD).  Otherwise all groups share one
+    // workgroup (a single group still splits its V accumulation; with more
+    // groups that measured slower).
     if (p.chunk == kTile && items <= kLatencyWorkgroups) {
         const int groups = (p.n_rows + 15) / 16;
         if (groups > 1 && items * groups <= kLatencyWorkgroups) {
-            chunk_tile_kernel<1, 2><<<dim3(p.n_inst, p.n_chunks, groups), 64 * 3, 0, s>>>(p);
+            const unsigned wgs = (unsigned)((items + 7) / 8) * 8u * (unsigned)groups;
+            chunk_tile_kernel<1, 2, true><<<dim3(wgs), 64 * 3, 0, s>>>(p);
             return hipGetLastError();
         }
         const dim3 grid(p.n_inst, p.n_chunks);
