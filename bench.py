@@ -62,15 +62,19 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "5435c9c410341dae1094edbb9b13fa06c0d9fced2e13c69cbfb9c9789276c28e", "fetch_bytes": 4279045, "write_bytes": 1634688},
+              "sources_sha256": "acd20df94ed8b9aba4e3b811d53bf0168e288bf34331122df69930e957b03117", "fetch_bytes": 1887193, "write_bytes": 1634714},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "5435c9c410341dae1094edbb9b13fa06c0d9fced2e13c69cbfb9c9789276c28e", "fetch_bytes": 262947267, "write_bytes": 25264128},
+               "sources_sha256": "acd20df94ed8b9aba4e3b811d53bf0168e288bf34331122df69930e957b03117", "fetch_bytes": 265250536, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "d5d07849bfcb217d37d5c658e92df99d7d050d612ce35dc00f09883bebb974a8", "fetch_bytes": 268718685, "write_bytes": 68157515},
+               "sources_sha256": "95af2b33a412217f20e26e1ecd52a5cdb0672137219aa000e2f965bfc4de32d0", "fetch_bytes": 268717967, "write_bytes": 68157440},
+    "qsa": {"sources": ("decode_attention_sparse_amd/csrc/qsa_select.hip",
+                        "decode_attention_sparse_amd/csrc/sda_internal.h",
+                        "decode_attention_sparse_amd/csrc/sda_api.hip"),
+            "sources_sha256": "4d4c98f78cced5dd7ea1e3f32c9af2c6da0597a73aa6d10c1646829a177f3e5a", "fetch_bytes": 67962699, "write_bytes": 274227},
 }
 
 
@@ -93,8 +97,8 @@ def sources_sha256(files) -> str:
 
 def measured_traffic(kernel):
     """Measured HBM bytes per launch of `kernel` ("chunk", "prompt",
-    "append"), or None when its sources differ from those the counters were
-    taken on."""
+    "append", "qsa"), or None when its sources differ from those the counters
+    were taken on."""
     m = MEASURED_TRAFFIC[kernel]
     if not m["sources_sha256"] or sources_sha256(m["sources"]) != m["sources_sha256"]:
         return None
@@ -588,7 +592,8 @@ def qsa_section(iters, flush):
         "selected_cells": cells,
         "blocks_scored_per_s": round(x.n_inst * x.max_blocks / (us["both"] * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("qsa"),
                      "kernel": "qsa_scores_kernel",
                      "algorithmic_bytes_per_launch": scorer_bytes,
                      "launch_us_median": round(us["scores"], 3),
@@ -801,12 +806,12 @@ def main(argv=None):
                      "launch_us_mean": k4_us,
                      "note": "latency-bound: one instance, 2,051 cells; "
                              "traffic = HBM bytes per launch (cold, counters), null if the "
-                             "kernel changed since they were taken; it exceeds the algorithmic "
-                             "bytes because each chunk's tile is staged by one workgroup per "
-                             "16-row group (up to three XCD caches fetch it) and each workgroup "
-                             "reads the whole page-table row to save a dependent round trip: "
-                             "re-reads that cost no time in this launch, whose duration is "
-                             "set by its round trips",
+                             "kernel changed since they were taken: 1.89 MB fetched (the "
+                             "1.05 MB of code rows once, the query rows and the page-table row "
+                             "once per XCD that holds a workgroup of the instance, the scales' "
+                             "sectors) and 1.63 MB of chunk partials written (33 chunks x 48 "
+                             "rows x 1 KB), which the merge reads back; the launch's duration "
+                             "is set by its round trips, not by these bytes",
                      "bytes_per_step": bytes_sum, "call_us_per_step": round(call_us_sum, 3)},
         "per_query_count": per_q,
         "pages_600_cells_per_query_count": per_q600,

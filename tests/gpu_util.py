@@ -54,12 +54,17 @@ def run_batch(x, chunk=None, n_q=None, gather=True, device="cuda", interleave=Fa
 
 def check(x, out, lse, g=None, inst_ids=None, what="", strict_out=True, strict_lse=True):
     """The outputs (and gather indices) of a decode call against the oracle,
-    on all instances or the sampled inst_ids.  Beyond the elementwise
+    on all instances or the sampled inst_ids (and finite on all of them).  Beyond the elementwise
     atol + rtol |ref| bound, strict_out / strict_lse assert the absolute
     bounds alone (max |dout| <= 1e-3, max |dlse| <= 1e-4), which float32
     meets wherever |lse| stays below about 100 (scores far larger, as in the
     heavy-tailed batched workload, leave float32 itself short of 1e-4)."""
     import oracle
+    # every row of every instance, sampled or not: a finite output (a kernel
+    # that gives up on a bounded wait writes NaN rows and still returns OK;
+    # lse is -inf only for rows with no visible cell)
+    assert np.isfinite(out).all(), f"{what}: non-finite outputs"
+    assert not (np.isnan(lse).any() or np.isposinf(lse).any()), f"{what}: NaN or +inf lse"
     ro, rl = oracle.attend(x, inst_ids)
     sl = slice(None) if inst_ids is None else np.asarray(inst_ids)
     e1 = assert_close(out[sl], ro, OUT_ATOL, OUT_RTOL, f"{what} out")
