@@ -84,6 +84,16 @@ constexpr int kStride = kDim + 16;   // LDS bytes per code row (padded)
 constexpr int kBuf = kTile * kStride;
 constexpr int kRows = kTile / 4;     // 1 KB staging loads per tile and pool (4 rows each)
 constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^23) to integers in the low bits
+// The low P.V digit leaves the matrix cores biased: its MFMA starts from
+// kLoBits (an inline constant: the bits of the float 1/(2 pi)) instead of 0,
+// and ends at kLoBits + n, which read as a float is (kLoUnits + n) 2^-26
+// exactly for |n| <= 2^21 (the float's binade is [1/8, 1/4) and its mantissa
+// field, 2,292,099, is at least 2^21 from both ends), so the sum needs no
+// int-to-float conversion; the offset, kLoUnits = 2^23 + 2,292,099 units of
+// 2^-26, is taken out once per tile.
+constexpr int kLoBits = 0x3E22F983;
+constexpr float kLoUnit = 0.15915494f;  // kLoUnits 2^-26, the float kLoBits
+constexpr float kTwo26 = 67108864.f;
 constexpr float kWTiny = 7.888609052210118e-31f;  // 2^-100: tiles whose weights stay below carry none
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
@@ -124,8 +134,9 @@ struct RowBlock {
     int k_off0, k_off1, v_off, m_off0, m_off1;
     float m_run;   // running max of this lane's row (base-2 units)
     float l_part;  // this lane's share of the row denominator
-    float frame;   // O = frame * o
-    v4f o[kDB];    // O^T[16 (kDB dh + db) + 4g + u][row] / frame
+    float frame;   // O = frame * (o - obias)
+    float obias;   // the offset o carries from the biased low P.V digit
+    v4f o[kDB];    // O^T[16 (kDB dh + db) + 4g + u][row] / frame + obias
     v4f su[4];     // scores of the tile the softmax runs on next: u, S = coef * u
 
     // qrow: this lane's query row, read at dims 64s + 16g + e (byte e of
@@ -217,9 +228,13 @@ struct RowBlock {
         m_run = -INFINITY;
         l_part = 0.f;
         frame = 1.f;
+        obias = 0.f;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) o[db] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
+
+    // Block db of the accumulator, O^T / frame: o without its offset.
+    __device__ __forceinline__ v4f acc(int db) const { return o[db] - obias; }
 
     // One step of the pipeline: the softmax and V accumulation of the tile
     // whose scores are in su (V rows vb, V scales vs), and the scores of the
@@ -234,12 +249,12 @@ struct RowBlock {
     template <bool kCausal = false>
     __device__ __forceinline__ void step(const int8_t *kb, const float *ks_t, const float *bias_t,
                                          const int8_t *vb, const float *vs_t, int dh, int lim = 0) {
-        const Stats st = stats();
-        v4f sn[4];
-        score<kCausal>(sn, kb, ks_t, bias_t, lim);
-        accumulate(st, vb, vs_t, dh);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) su[cb] = sn[cb];
+        // the softmax of the current tile first, so that its scores are dead
+        // before the next tile's arrive (one set of score registers)
+        const Digits d = prepare(stats(), vs_t);
+        __builtin_amdgcn_sched_barrier(0);
+        score<kCausal>(su, kb, ks_t, bias_t, lim);
+        pv(d, vb, dh);
     }
 
     // A whole one-tile chunk: its scores, then their softmax and V
@@ -346,6 +361,16 @@ struct RowBlock {
     // statistics st from stats()): probabilities, their digits, O^T += V^T P^T.
     __device__ __forceinline__ void accumulate(const Stats &st, const int8_t *vb,
                                                const float *vs_t, int dh) {
+        pv(prepare(st, vs_t), vb, dh);
+    }
+
+    // The probabilities' digits of a tile and their scale (the softmax half
+    // of accumulate()), then the products with the V rows (its P.V half).
+    struct Digits {
+        v4i xa, xb, xc;
+        float tau3l, tau3h;
+    };
+    __device__ __forceinline__ Digits prepare(const Stats &st, const float *vs_t) {
         const float m_use = st.m_use, corr = st.corr, frame_new = st.frame_new;
         // ---------------- probabilities and their digits for the current tile
         // weights w = p * v_scale; W = 2^16 / tau = 2^16 * 127 / (row max of
@@ -400,11 +425,17 @@ struct RowBlock {
         if (__any(frame < kRenorm)) {
 #pragma unroll
             for (int db = 0; db < kDB; ++db) o[db] *= frame;
+            obias *= frame;
             frame = 1.f;
         }
-        const float tau3 = live ? __builtin_amdgcn_rcpf(W * frame) : 0.f;  // tau / 2^16 / frame
-        const float tau3h = 256.f * tau3;
+        // tau3 = tau / 2^16 / frame, kept as tau3l = 2^26 tau3 and tau3h = 2^8 tau3
+        const float tau3l = live ? kTwo26 * __builtin_amdgcn_rcpf(W * frame) : 0.f;
+        return Digits{xa, xb, xc, tau3l, (1.f / 262144.f) * tau3l};
+    }
 
+    __device__ __forceinline__ void pv(const Digits &d, const int8_t *vb, int dh) {
+        const v4i xa = d.xa, xb = d.xb, xc = d.xc;
+        const float tau3l = d.tau3l, tau3h = d.tau3h;
         // ---------------- O^T += V^T P^T for this wave's blocks of 16 dims
         const int8_t *vp = vb + v_off + 16 * kDB * dh;
 #pragma unroll
@@ -415,14 +446,16 @@ struct RowBlock {
             const v4i va = {h0[0], h0[1], h1[0], h1[1]};
             const v4i hi = mfma_i8(va, xa, (v4i){0, 0, 0, 0});
             const v4i mid = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
-            const v4i lo = mfma_i8(va, xc, (v4i){0, 0, 0, 0});
+            const v4i lo = mfma_i8(va, xc, (v4i){kLoBits, kLoBits, kLoBits, kLoBits});
             // sum of X * v_code = 2^8 T + LO, with T = 2^8 HI + MID exact in
-            // int32 (|T| < 2^29, |LO| < 2^21)
+            // int32 (|T| < 2^29, |LO| <= 64 * 128 * 128 = 2^20); LO arrives
+            // biased, (kLoUnits + LO) 2^-26 as a float
             const v4i top = (hi << 8) + mid;
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                o[db][u] = fmaf((float)top[u], tau3h, fmaf((float)lo[u], tau3, o[db][u]));
+                o[db][u] = fmaf((float)top[u], tau3h, fmaf(__int_as_float(lo[u]), tau3l, o[db][u]));
         }
+        obias = fmaf(kLoUnit, tau3l, obias);  // kLoUnits tau3
     }
 
     // The partial's maximum: the base-2 running maximum back in natural-log
@@ -438,7 +471,7 @@ struct RowBlock {
         if (row < p.n_rows) {
             float *dst = p.acc + base * kDim + 16 * kDB * dh + 4 * g;
 #pragma unroll
-            for (int db = 0; db < kDB; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = o[db] * frame;
+            for (int db = 0; db < kDB; ++db) *reinterpret_cast<v4f *>(dst + 16 * db) = acc(db) * frame;
             if (g == 0 && dh == 0) {
                 p.m[base] = m_nat();
                 p.l[base] = l_row;
@@ -464,7 +497,7 @@ struct RowBlock {
         const float inv = 1.f / l_row;
 #pragma unroll
         for (int db = 0; db < kDB; ++db)
-            *reinterpret_cast<v4f *>(dst + 16 * db) = (o[db] * frame) * inv;
+            *reinterpret_cast<v4f *>(dst + 16 * db) = (acc(db) * frame) * inv;
         if (g == 0 && dh == 0) *lse_row = m_run * 0.69314718055994531f + logf(l_row);
     }
 };
@@ -520,13 +553,14 @@ __device__ __forceinline__ bool flag_wait(const int *flag, int step) {
 // (logical cells 0, 1, 2, ... up to the workgroup's last position), each
 // row masks the cells past its own position, and the rows are normalised in
 // place of a partial (one chunk spans the whole causal range).
-template <int RB, int DS, bool kPrompt, int SP = 1, bool kFinal = false>
+template <int RB, int DS, bool kPrompt, int SP = 1, bool kFinal = false, bool kMulti = false>
 __global__ __launch_bounds__(64 * SP * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu((RB == 1 || DS > 1) ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p, int cpw) {
     static_assert(SP == 1 || (SP == 2 && kFinal && DS == 1 && RB >= 2 && RB <= 3),
                   "two pipelines: final decode output, 2 or 3 row groups");
     static_assert(!(kPrompt && kFinal), "the prompt form always writes its rows");
+    static_assert(!kMulti || (!kPrompt && !kFinal), "several chunks per workgroup: decode partials");
     static_assert(SP == 1 || RB * 8 * 64 * 16 <= 2 * kBuf,
                   "the hand-over fits a pipeline's K (and V) buffers");
     constexpr int kPipe = DS * RB + 1;  // waves per pipeline
@@ -764,13 +798,16 @@ void chunk_mfma_kernel(Params p, int cpw) {
             if (!flag_wait(&ready_f[pipe], t - 1)) stuck_f = 1;
     };
     auto end_step = [&](int t) {
-        // end of a chunk: emit its partial, start afresh
-        if (!kPrompt && !kFinal && t >= 0 && ((t + 1) % tpc == 0 || t == n_tiles - 1)) {
-            rb.emit(p, ((int64_t)i * p.n_chunks + c0 + t / tpc) * R + row, row, g, dh);
-            rb.reset();
-        }
         if constexpr (SP > 1) flag_post(&done_f[pipe][wave], t);  // this step's LDS reads are done
         sync();
+    };
+    // end of a chunk (tile t its last): emit its partial, start afresh
+    auto emit = [&](int t) {
+        if constexpr (!kPrompt && !kFinal) {
+            const int c = kMulti ? c0 + t / tpc : c0;
+            rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
+            rb.reset();
+        }
     };
     // prompt: the mask limit of tile t + 1, whose first cell is j_begin + 64 (t + 1)
     auto lim_next = [&](int t) {
@@ -786,6 +823,8 @@ void chunk_mfma_kernel(Params p, int cpw) {
         begin_step(t);
         rb.template step<kPrompt>(kbuf_p[0][(t + 1) & 1], ks_p[0][(t + 1) & 3], bias_p[0][(t + 1) & 3],
                                   vbuf_p[0][t & 1], vs_p[0][t & 3], dh, lim_next(t));
+        if constexpr (kMulti)
+            if ((t + 1) % tpc == 0) emit(t);
         end_step(t);
     }
     if (n_tiles > 0) {
@@ -798,6 +837,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
         begin_step(t);
         end_step(t);
     }
+    if (n_tiles > 0) emit(n_tiles - 1);  // the (last) chunk's partial
     if constexpr (kPrompt)
         rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
     if constexpr (kFinal) {
@@ -820,7 +860,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
             __syncthreads();  // both pipelines' steps are over: their buffers are idle
             if (pipe == 1) {
 #pragma unroll
-                for (int db = 0; db < kDB; ++db) *xslot(db) = rb.o[db] * rb.frame;
+                for (int db = 0; db < kDB; ++db) *xslot(db) = rb.acc(db) * rb.frame;
                 if (g == 0) {
                     xm[row] = m_row;
                     xl[row] = l_row;
@@ -868,7 +908,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
             v4f o = (v4f){0.f, 0.f, 0.f, 0.f};
-            if (0 < nch) o = merge_acc(o, w[0], rb.o[db] * rb.frame);
+            if (0 < nch) o = merge_acc(o, w[0], rb.acc(db) * rb.frame);
             if constexpr (SP > 1)
                 if (1 < nch) o = merge_acc(o, w[1], *xslot(db));
             *reinterpret_cast<v4f *>(dst + 16 * db) = any ? o * inv : (v4f){0.f, 0.f, 0.f, 0.f};
@@ -1050,13 +1090,13 @@ void chunk_tile_kernel(Params p) {
     rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
 }
 
-template <int DS>
+template <int DS, bool kMulti>
 void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
     switch ((p.n_rows + 15) / 16) {
-        case 1: chunk_mfma_kernel<1, DS, false><<<grid, 64 * (DS + 1), 0, s>>>(p, cpw); break;
-        case 2: chunk_mfma_kernel<2, DS, false><<<grid, 64 * (2 * DS + 1), 0, s>>>(p, cpw); break;
-        case 3: chunk_mfma_kernel<3, 1, false><<<grid, 64 * 4, 0, s>>>(p, cpw); break;
-        default: chunk_mfma_kernel<4, 1, false><<<grid, 64 * 5, 0, s>>>(p, cpw); break;
+        case 1: chunk_mfma_kernel<1, DS, false, 1, false, kMulti><<<grid, 64 * (DS + 1), 0, s>>>(p, cpw); break;
+        case 2: chunk_mfma_kernel<2, DS, false, 1, false, kMulti><<<grid, 64 * (2 * DS + 1), 0, s>>>(p, cpw); break;
+        case 3: chunk_mfma_kernel<3, 1, false, 1, false, kMulti><<<grid, 64 * 4, 0, s>>>(p, cpw); break;
+        default: chunk_mfma_kernel<4, 1, false, 1, false, kMulti><<<grid, 64 * 5, 0, s>>>(p, cpw); break;
     }
 }
 
@@ -1098,10 +1138,15 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
     // A grid of at most one workgroup per CU is latency-bound: split the V
     // accumulation of each 16-row group over two waves while that still
     // leaves about one compute wave per SIMD (up to 32 rows).
+    // (a workgroup with several chunks emits partials inside its tile loop:
+    // a form of its own, so that the one-chunk form keeps that code out of
+    // the loop)
     if (items <= kLatencyWorkgroups && p.n_rows <= 32)
-        launch_rb<2>(p, grid, cpw, s);
+        launch_rb<2, false>(p, grid, cpw, s);  // cpw is 1 here
+    else if (cpw > 1)
+        launch_rb<1, true>(p, grid, cpw, s);
     else
-        launch_rb<1>(p, grid, cpw, s);
+        launch_rb<1, false>(p, grid, cpw, s);
     return hipGetLastError();
 }
 
