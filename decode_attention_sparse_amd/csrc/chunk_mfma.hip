@@ -94,13 +94,25 @@ constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^23) to inte
 constexpr int kLoBits = 0x3E22F983;
 constexpr float kLoUnit = 0.15915494f;  // kLoUnits 2^-26, the float kLoBits
 constexpr float kTwo26 = 67108864.f;
-constexpr float kWTiny = 7.888609052210118e-31f;  // 2^-100: tiles whose weights stay below carry none
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
 constexpr int64_t kLatencyWorkgroups = 256;         // grids up to one workgroup per CU
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// The tile's weight scale, from the producer wave that stages its V scales
+// (lane = cell, vsf its V scale, 0 for a masked cell): with vmax the
+// largest V scale of the tile, W = 127 * 2^16 / vmax (0 if vmax is 0); cell
+// c's slot gets vsf * W (a probability p <= 1 times it is the P.V weight on
+// the digit grid, at most 127 * 2^16), and *inv_w gets 1 / W (0 if W is 0).
+// Every producer form calls this, so all forms share the bits.
+__device__ __forceinline__ void put_v_scales(float *vs_slot, float *inv_w, float vsf, int lane) {
+    const float vmax = wave_max(vsf);
+    const float W = vmax > 0.f ? (65536.f * 127.f) * __builtin_amdgcn_rcpf(vmax) : 0.f;
+    vs_slot[lane] = vsf * W;
+    if (lane == 0) *inv_w = vmax * (1.f / (65536.f * 127.f));
 }
 
 // Sum over the four lanes l, l^16, l^32, l^48 (one query row), with the
@@ -132,6 +144,7 @@ struct RowBlock {
     v4i qa[4], qb[4], qc[4];  // query digits: B operands of S^T = K Q^T
     float coef;  // sigma * |scale_log2| / 2^8: S (base 2) = coef * (AB + C / 2^8) * k_scale
     int k_off0, k_off1, v_off, m_off0, m_off1;
+    int w_off;     // this pipeline's offset in the arrays of 1 / W (wave-uniform)
     float m_run;   // running max of this lane's row (base-2 units)
     float l_part;  // this lane's share of the row denominator
     float frame;   // O = frame * (o - obias)
@@ -208,20 +221,23 @@ struct RowBlock {
         // this lane's S cells (cb, 4g + u) live in LDS rows lds_row(cb, 4g + u)
         m_off0 = lds_row(0, 4 * g);
         m_off1 = lds_row(1, 4 * g) - 16;
+        w_off = 0;
         reset();
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) su[cb] = (v4f){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     }
 
     // Moves this lane's LDS offsets to another pipeline's buffers: code rows
-    // kv bytes on, scale and bias slots sc elements on.  (Not for the causal
-    // form, whose mask compares the slot offsets with cell indices.)
-    __device__ __forceinline__ void shift(int kv, int sc) {
+    // kv bytes on, scale and bias slots sc elements on, the 1 / W values sw
+    // on.  (Not for the causal form, whose mask compares the slot offsets
+    // with cell indices.)
+    __device__ __forceinline__ void shift(int kv, int sc, int sw) {
         k_off0 += kv;
         k_off1 += kv;
         v_off += kv;
         m_off0 += sc;
         m_off1 += sc;
+        w_off += sw;
     }
 
     __device__ __forceinline__ void reset() {
@@ -248,10 +264,11 @@ struct RowBlock {
     // (tile()), with the same arithmetic.
     template <bool kCausal = false>
     __device__ __forceinline__ void step(const int8_t *kb, const float *ks_t, const float *bias_t,
-                                         const int8_t *vb, const float *vs_t, int dh, int lim = 0) {
+                                         const int8_t *vb, const float *vs_t, const float *vw_t, int dh,
+                                         int lim = 0) {
         // the softmax of the current tile first, so that its scores are dead
         // before the next tile's arrive (one set of score registers)
-        const Digits d = prepare(stats(), vs_t);
+        const Digits d = prepare(stats(), vs_t, vw_t);
         __builtin_amdgcn_sched_barrier(0);
         score<kCausal>(su, kb, ks_t, bias_t, lim);
         pv(d, vb, dh);
@@ -260,9 +277,9 @@ struct RowBlock {
     // A whole one-tile chunk: its scores, then their softmax and V
     // accumulation.
     __device__ __forceinline__ void tile(const int8_t *kb, const float *ks_t, const float *bias_t,
-                                         const int8_t *vb, const float *vs_t, int dh) {
+                                         const int8_t *vb, const float *vs_t, const float *vw_t, int dh) {
         score(su, kb, ks_t, bias_t);
-        accumulate(stats(), vb, vs_t, dh);
+        accumulate(stats(), vb, vs_t, vw_t, dh);
     }
 
     // Softmax statistics of the tile whose scores are in su: the running max
@@ -344,7 +361,8 @@ struct RowBlock {
     template <int DS>
     __device__ __forceinline__ void tile_shared(const int8_t *kb, const float *ks_t,
                                                 const float *bias_t, const int8_t *vb,
-                                                const float *vs_t, int dh, v4f *xs, int lane) {
+                                                const float *vs_t, const float *vw_t, int dh, v4f *xs,
+                                                int lane) {
         constexpr int kPer = 4 / DS;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
@@ -354,14 +372,14 @@ struct RowBlock {
         __syncthreads();
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) su[cb] = xs[64 * cb + lane];
-        accumulate(stats(), vb, vs_t, dh);
+        accumulate(stats(), vb, vs_t, vw_t, dh);
     }
 
     // Softmax and V accumulation of the tile whose scores are in su (its
     // statistics st from stats()): probabilities, their digits, O^T += V^T P^T.
     __device__ __forceinline__ void accumulate(const Stats &st, const int8_t *vb,
-                                               const float *vs_t, int dh) {
-        pv(prepare(st, vs_t), vb, dh);
+                                               const float *vs_t, const float *vw_t, int dh) {
+        pv(prepare(st, vs_t, vw_t), vb, dh);
     }
 
     // The probabilities' digits of a tile and their scale (the softmax half
@@ -370,42 +388,30 @@ struct RowBlock {
         v4i xa, xb, xc;
         float tau3l, tau3h;
     };
-    __device__ __forceinline__ Digits prepare(const Stats &st, const float *vs_t) {
+    __device__ __forceinline__ Digits prepare(const Stats &st, const float *vs_t, const float *vw_t) {
         const float m_use = st.m_use, corr = st.corr, frame_new = st.frame_new;
         // ---------------- probabilities and their digits for the current tile
-        // weights w = p * v_scale; W = 2^16 / tau = 2^16 * 127 / (row max of
-        // w), and X = rint(w * W) < 2^23 lands in the low bits of
-        // fma(w, W, 2^23): X = 2^16 a + 2^8 b + c with balanced digits b, c in
-        // [-128, 127] (a in [0, 127]): c = byte 0 of X, b = byte 1 of X + 2^7,
-        // a = byte 2 of X + 2^7 + 2^15 (bit 23 of the float pattern, the
-        // exponent's lowest bit, is 0 in [2^23, 2^24)).  Byte 1 of
-        // X + 2^7 + 2^15 is b + 2^7 modulo 2^8: b is read there, its top bit
-        // flipped.
+        // weights w = p * v_scale on the tile's grid: X = rint(p * v_scale *
+        // W) with W = 127 * 2^16 / (the tile's largest V scale) (the slot
+        // holds v_scale * W per cell, and 1 / W after them; p <= 1, so X <=
+        // 127 * 2^16 < 2^23) lands in the low bits of fma(p, v_scale W, 2^23):
+        // X = 2^16 a + 2^8 b + c with balanced digits b, c in [-128, 127] (a
+        // in [0, 127]): c = byte 0 of X, b = byte 1 of X + 2^7, a = byte 2 of
+        // X + 2^7 + 2^15 (bit 23 of the float pattern, the exponent's lowest
+        // bit, is 0 in [2^23, 2^24)).  Byte 1 of X + 2^7 + 2^15 is b + 2^7
+        // modulo 2^8: b is read there, its top bit flipped.
         float psum = 0.f;
-        float wt[4][4];
-        float wmax = 0.f;
+        v4i xa, xb, xc;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int mo = 16 * cb + ((cb & 1) ? m_off1 : m_off0);
-            const v4f vs = *reinterpret_cast<const v4f *>(vs_t + mo);
+            const v4f vw = *reinterpret_cast<const v4f *>(vs_t + mo);
+            unsigned xs[4], x2[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -m_use));
                 psum += pr;
-                wt[cb][u] = pr * vs[u];
-                wmax = fmaxf(wmax, wt[cb][u]);
-            }
-        }
-        wmax = max4(wmax);
-        const bool live = wmax > kWTiny;
-        const float W = live ? (65536.f * 127.f) * __builtin_amdgcn_rcpf(wmax) : 0.f;
-        v4i xa, xb, xc;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            unsigned xs[4], x2[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                xs[u] = __float_as_uint(fmaf(wt[cb][u], W, kRound));
+                xs[u] = __float_as_uint(fmaf(pr, vw[u], kRound));
                 x2[u] = xs[u] + 32896u;
             }
             const unsigned c01 = __builtin_amdgcn_perm(xs[1], xs[0], 0x0c0c0400u);
@@ -428,8 +434,8 @@ struct RowBlock {
             obias *= frame;
             frame = 1.f;
         }
-        // tau3 = tau / 2^16 / frame, kept as tau3l = 2^26 tau3 and tau3h = 2^8 tau3
-        const float tau3l = live ? kTwo26 * __builtin_amdgcn_rcpf(W * frame) : 0.f;
+        // tau3 = 1 / (W frame), kept as tau3l = 2^26 tau3 and tau3h = 2^8 tau3
+        const float tau3l = (kTwo26 * vw_t[w_off]) * __builtin_amdgcn_rcpf(frame);
         return Digits{xa, xb, xc, tau3l, (1.f / 262144.f) * tau3l};
     }
 
@@ -572,6 +578,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     __shared__ __attribute__((aligned(16))) int phys_p[SP][4][kTile];
     __shared__ __attribute__((aligned(16))) float ks_p[SP][4][kTile];
     __shared__ __attribute__((aligned(16))) float vs_p[SP][4][kTile];
+    __shared__ float vw_p[SP][4];  // per slot: 1 / W of the tile (put_v_scales)
     __shared__ __attribute__((aligned(16))) float bias_p[SP][4][kTile];
     // two pipelines: per pipeline, the producer's last completed step and each
     // compute wave's; a flag that any wait gave up
@@ -641,6 +648,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
         (&ks_p[0][0][0])[e] = 0.f;
         (&vs_p[0][0][0])[e] = 0.f;
         (&bias_p[0][0][0])[e] = -INFINITY;
+        if (e < SP * 4) (&vw_p[0][0])[e] = 0.f;
     }
     if constexpr (SP > 1) {
         if (threadIdx.x < SP * (DS * RB + 1)) {
@@ -740,7 +748,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 const float ksf = ok ? half_bits_to_float((uint16_t)kh2) : 0.f;
                 const float vsf = ok ? half_bits_to_float((uint16_t)vh2) : 0.f;
                 ks_s[m2][lane] = ksf;
-                vs_s[m2][lane] = vsf;
+                put_v_scales(vs_s[m2], &vw_p[pipe][m2], vsf, lane);
                 bias_s[m2][lane] = ok ? 0.f : -INFINITY;
             }
             if (t + 3 >= 0 && t + 3 < n_tiles) {
@@ -777,7 +785,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     rb.init(p.q + (row_ok ? grow : (int64_t)i * R + row0) * kDim, row_ok, p.scale_log2, g, l16);
     // the steps below address pipeline 0's buffers; the lane offsets carry
     // the pipeline (one add here instead of a base register per buffer)
-    if constexpr (SP > 1) rb.shift(pipe * 2 * kBuf, pipe * 4 * kTile);
+    if constexpr (SP > 1) rb.shift(pipe * 2 * kBuf, pipe * 4 * kTile, pipe * 4);
     // prompt: this row's last visible cell (its position)
     const int64_t lim_row = kPrompt ? pos0 + (row0 + row) / p.n_qheads : 0;
     // Steps t = -4 .. n_iter - 1, one barrier each (the producer's count).
@@ -822,7 +830,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     for (int t = 0; t < n_tiles - 1; ++t) {
         begin_step(t);
         rb.template step<kPrompt>(kbuf_p[0][(t + 1) & 1], ks_p[0][(t + 1) & 3], bias_p[0][(t + 1) & 3],
-                                  vbuf_p[0][t & 1], vs_p[0][t & 3], dh, lim_next(t));
+                                  vbuf_p[0][t & 1], vs_p[0][t & 3], &vw_p[0][t & 3], dh, lim_next(t));
         if constexpr (kMulti)
             if ((t + 1) % tpc == 0) emit(t);
         end_step(t);
@@ -830,7 +838,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     if (n_tiles > 0) {
         const int t = n_tiles - 1;
         begin_step(t);
-        rb.accumulate(rb.stats(), vbuf_p[0][t & 1], vs_p[0][t & 3], dh);
+        rb.accumulate(rb.stats(), vbuf_p[0][t & 1], vs_p[0][t & 3], &vw_p[0][t & 3], dh);
         end_step(t);
     }
     for (int t = n_tiles; t < n_iter; ++t) {
@@ -929,6 +937,7 @@ constexpr int kPtLdsPages = 2048;  // page tables up to this size are staged who
 // scales and bias by cell).
 __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out, int i, int j0,
                                            int j_end, int lane, int8_t *kb, int8_t *vb, float *ks, float *vs,
+                                           float *vw,
                                            float *bias, int *pt_s) {
     const int g = lane >> 4, l16 = lane & 15;
     const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
@@ -1002,7 +1011,7 @@ __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out,
     const float ksf = ok ? half_bits_to_float((uint16_t)kh) : 0.f;
     const float vsf = ok ? half_bits_to_float((uint16_t)vh) : 0.f;
     ks[lane] = ksf;
-    vs[lane] = vsf;
+    put_v_scales(vs, vw, vsf, lane);
     bias[lane] = ok ? 0.f : -INFINITY;
     int8_t *kd = kb + l16 * kStride + 16 * g;
     int8_t *vd = vb + l16 * kStride + 16 * g;
@@ -1044,6 +1053,7 @@ void chunk_tile_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) int8_t vbuf[kBuf];
     __shared__ __attribute__((aligned(16))) float ks_s[kTile];
     __shared__ __attribute__((aligned(16))) float vs_s[kTile];
+    __shared__ float vw_s[1];
     __shared__ __attribute__((aligned(16))) float bias_s[kTile];
     __shared__ __attribute__((aligned(16))) int pt_s[kPtLdsPages];
 
@@ -1069,7 +1079,7 @@ void chunk_tile_kernel(Params p) {
     if (wave == kProducer) {
         // every row group's workgroup stages the tile; one writes gather_out
         stage_tile(p, z == 0 ? p.gather_out : nullptr, i, j_begin, j_end, lane, kbuf,
-                   vbuf, ks_s, vs_s, bias_s, p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
+                   vbuf, ks_s, vs_s, vw_s, bias_s, p.n_logical_pages <= kPtLdsPages ? pt_s : nullptr);
         __syncthreads();
         if constexpr (kShared) __syncthreads();  // the compute waves' score exchange
         return;
@@ -1082,11 +1092,11 @@ void chunk_tile_kernel(Params p) {
     rb.init(p.q + ((int64_t)i * R + (row < R ? row : 0)) * kDim, row < R, p.scale_log2, g, l16);
     __syncthreads();
     if constexpr (kShared)
-        rb.template tile_shared<DS>(kbuf, ks_s, bias_s, vbuf, vs_s,
+        rb.template tile_shared<DS>(kbuf, ks_s, bias_s, vbuf, vs_s, vw_s,
                                     __builtin_amdgcn_readfirstlane(dh),
                                     xs + 256 * (wave / DS), lane);
     else
-        rb.tile(kbuf, ks_s, bias_s, vbuf, vs_s, dh);
+        rb.tile(kbuf, ks_s, bias_s, vbuf, vs_s, vw_s, dh);
     rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
 }
 
