@@ -43,15 +43,16 @@
 //       MFMA chain; 2^8 A + B is formed in int32 (|.| < 2^30) before the
 //       conversion to fp32.  Score errors are at fp32 level relative to the
 //       wave's largest score.
-//   PV  x = p * v_scale / tau in [0, 127], tau = (the row's largest
-//       p * v_scale in the tile) / 127; X = rint(2^16 x) in [0, 127 * 2^16]
-//       is written as 2^16 a + 2^8 b + c (a in [0,127], b, c in [-128,127]);
+//   PV  x = p * v_scale / tau in [0, 127], tau = (the tile's largest
+//       v_scale) / 127 (p <= 1: it is taken against the running maximum,
+//       which includes the tile); X = rint(2^16 x) in [0, 127 * 2^16] is
+//       written as 2^16 a + 2^8 b + c (a in [0,127], b, c in [-128,127]);
 //       the tile's sums over cells of a, b and c times v_code (three MFMAs)
 //       are exact in int32, 2^8 A + B is formed in int32 (|.| < 2^29), and
 //       2^8 (2^8 A + B) + C is folded into the fp32 accumulator once per
-//       tile.  Each weight is represented to 2^-24 of the tile's largest
-//       weighted probability p * v_scale (the resolution of an fp32 sum of
-//       such terms), whatever the spread of the V scales.
+//       tile, the low sum arriving biased (no conversion).  Each weight is
+//       represented to 2^-24 of the tile's largest possible weight (its
+//       largest V scale), whatever the spread of the V scales across tiles.
 //
 // Pipeline.  Iteration t of the tile loop computes the scores of tile t+1
 // while it runs the softmax and the V accumulation of tile t, so matrix-core
