@@ -95,6 +95,13 @@ constexpr float kRound = 8388608.f;  // 2^23: adding it rounds [0, 2^23) to inte
 constexpr int kLoBits = 0x3E22F983;
 constexpr float kLoUnit = 0.15915494f;  // kLoUnits 2^-26, the float kLoBits
 constexpr float kTwo26 = 67108864.f;
+// The low q.k digit's MFMA chain starts from kMagicBits (1.5 * 2^23 as a
+// float): its int32 sum C, |C| <= 256 * 128 * 128 = 2^22, ends at
+// kMagicBits + C, which read as a float is 1.5 * 2^23 + C exactly; over 2^8
+// that is kScoreOffset + C / 2^8, and the producers store each cell's bias
+// less kScoreOffset * k_scale (exact: k_scale has 11 significant bits).
+constexpr int kMagicBits = 0x4B400000;
+constexpr float kScoreOffset = 49152.f;  // 1.5 * 2^23 / 2^8
 constexpr float kRenorm = 5.421010862427522e-20f;  // 2^-64
 constexpr int64_t kResidentWorkgroups = 512;        // 256 CUs x 2 workgroups (LDS-limited)
 constexpr int64_t kLatencyWorkgroups = 256;         // grids up to one workgroup per CU
@@ -334,7 +341,8 @@ struct RowBlock {
         v4i ka[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
-        v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0}, cc = {0, 0, 0, 0};
+        v4i aa = {0, 0, 0, 0}, bb = {0, 0, 0, 0};
+        v4i cc = {kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             aa = mfma_i8(ka[s], qa[s], aa);
@@ -348,7 +356,7 @@ struct RowBlock {
         v4f sn;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float tq = fmaf((float)cc[u], 1.f / 256.f, (float)ab[u]);
+            const float tq = fmaf(__int_as_float(cc[u]), 1.f / 256.f, (float)ab[u]);
             sn[u] = fmaf(tq, ks[u], bs[u]);
         }
         return sn;
@@ -750,7 +758,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 const float vsf = ok ? half_bits_to_float((uint16_t)vh2) : 0.f;
                 ks_s[m2][lane] = ksf;
                 put_v_scales(vs_s[m2], &vw_p[pipe][m2], vsf, lane);
-                bias_s[m2][lane] = ok ? 0.f : -INFINITY;
+                bias_s[m2][lane] = ok ? -kScoreOffset * ksf : -INFINITY;
             }
             if (t + 3 >= 0 && t + 3 < n_tiles) {
                 int ph = -1;
@@ -1013,7 +1021,7 @@ __device__ __forceinline__ void stage_tile(const Params &p, int32_t *gather_out,
     const float vsf = ok ? half_bits_to_float((uint16_t)vh) : 0.f;
     ks[lane] = ksf;
     put_v_scales(vs, vw, vsf, lane);
-    bias[lane] = ok ? 0.f : -INFINITY;
+    bias[lane] = ok ? -kScoreOffset * ksf : -INFINITY;
     int8_t *kd = kb + l16 * kStride + 16 * g;
     int8_t *vd = vb + l16 * kStride + 16 * g;
 #pragma unroll
