@@ -388,7 +388,9 @@ struct RowBlock {
     // statistics st from stats()): probabilities, their digits, O^T += V^T P^T.
     __device__ __forceinline__ void accumulate(const Stats &st, const int8_t *vb,
                                                const float *vs_t, const float *vw_t, int dh) {
-        pv(prepare(st, vs_t, vw_t), vb, dh);
+        const Digits d = prepare(st, vs_t, vw_t);
+        __builtin_amdgcn_sched_barrier(0);  // as in step(): the halves apart
+        pv<true>(d, vb, dh);
     }
 
     // The probabilities' digits of a tile and their scale (the softmax half
@@ -448,6 +450,11 @@ struct RowBlock {
         return Digits{xa, xb, xc, tau3l, (1.f / 262144.f) * tau3l};
     }
 
+    // kAlone: a tile with no scoring beside it (the last of a chunk, or the
+    // single-tile kernel): groups of four 16-dim blocks are kept apart, so
+    // that the compiler does not issue all the products first and hold every
+    // block's sums at once.
+    template <bool kAlone = false>
     __device__ __forceinline__ void pv(const Digits &d, const int8_t *vb, int dh) {
         const v4i xa = d.xa, xb = d.xb, xc = d.xc;
         const float tau3l = d.tau3l, tau3h = d.tau3h;
@@ -469,8 +476,18 @@ struct RowBlock {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 o[db][u] = fmaf((float)top[u], tau3h, fmaf(__int_as_float(lo[u]), tau3l, o[db][u]));
+            if constexpr (kAlone)
+                if ((db & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
         obias = fmaf(kLoUnit, tau3l, obias);  // kLoUnits tau3
+        if constexpr (kAlone) {
+            // the sums are complete here: otherwise the compiler may move
+            // their conversions past the following barrier, next to the
+            // partial's stores, and hold every block's sums until then
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) __asm__ volatile("" : "+v"(o[db]));
+            __asm__ volatile("" : "+v"(obias));
+        }
     }
 
     // The partial's maximum: the base-2 running maximum back in natural-log
