@@ -29,9 +29,11 @@ def sources():
 PROBES = {
     # name: extra link flags.  gather_ceiling: the HBM read ceilings that
     # `bench.py --gather-ceiling` reports; valu_chunk: the vector-ALU chunk
-    # pass variants timed beside the library (loads libsda.so at run time).
+    # pass variants timed beside the library (loads libsda.so at run time);
+    # simd_placement: which SIMDs the waves of a workgroup land on.
     "gather_ceiling": [],
     "valu_chunk": ["-ldl"],
+    "simd_placement": [],
 }
 PROBE_BIN = os.path.join(PKG, "probes", "gather_ceiling")
 

@@ -612,11 +612,18 @@ void chunk_mfma_kernel(Params p, int cpw) {
 
     // wave index: uniform, so that the role and pipeline branches are scalar
     const int wv = SP == 1 ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int pipe = SP == 1 ? 0 : wv / kPipe;
-    // role within the pipeline (kProducer: the producer).  Pipeline 1 puts its
-    // producer first, so that with waves dealt to the SIMDs in turn the two
-    // producers sit on different SIMDs.
-    const int wave = pipe == 0 ? wv : (wv - 1) % kPipe;
+    // Pipeline and role within it (kProducer: the producer; one pipeline: the
+    // last wave).  The hardware deals a workgroup's waves to the four SIMDs
+    // of its CU in a fixed cyclic order, so waves k and k + 4 share a SIMD;
+    // two pipelines lay out their roles so that the compute waves spread
+    // over the SIMDs: pipelines of three make the last two waves the
+    // producers (the four compute waves on four SIMDs; with each pipeline's
+    // three waves consecutive, some SIMD would hold two compute waves and
+    // another none), pipelines of four put pipeline 1's producer first
+    // (waves 3 and 4: the six compute waves two, two, one and one).
+    const int pipe = SP == 1 ? 0 : kPipe == 3 ? (wv < 4 ? wv / 2 : wv - 4) : wv / kPipe;
+    const int wave = SP == 1 ? wv : kPipe == 3 ? (wv < 4 ? wv % 2 : kProducer)
+                                               : (pipe == 0 ? wv : (wv - 1) % kPipe);
     const int lane = threadIdx.x & 63;
     int8_t (&kbuf)[2][kBuf] = kbuf_p[pipe];
     int8_t (&vbuf)[2][kBuf] = vbuf_p[pipe];

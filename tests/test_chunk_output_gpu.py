@@ -149,6 +149,7 @@ def test_graph_replay_two_pipelines():
 
 @pytest.mark.parametrize("kw,nch", [
     (dict(n_inst=180, n_q=3, pool_cells=1024, n_sel=700, chunk=256), 2),  # two pipelines, 36 rows
+    (dict(n_inst=180, n_q=2, pool_cells=1024, n_sel=700, chunk=256), 2),  # two pipelines, 24 rows
     (dict(n_inst=200, n_q=2, pool_cells=1024, n_sel=250, chunk=256), 1),  # one chunk, small grid
 ])
 def test_output_from_chunk_pass_masked(kw, nch):
