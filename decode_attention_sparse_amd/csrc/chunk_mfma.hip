@@ -589,8 +589,8 @@ template <int RB, int DS, bool kPrompt, int SP = 1, bool kFinal = false, bool kM
 __global__ __launch_bounds__(64 * SP * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu((RB == 1 || DS > 1) ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p, int cpw) {
-    static_assert(SP == 1 || (SP == 2 && kFinal && DS == 1 && RB >= 2 && RB <= 3),
-                  "two pipelines: final decode output, 2 or 3 row groups");
+    static_assert(SP == 1 || (SP == 2 && !kPrompt && !kMulti && DS == 1 && RB >= 2 && RB <= 3),
+                  "two pipelines: decode, one chunk each, 2 or 3 row groups");
     static_assert(!(kPrompt && kFinal), "the prompt form always writes its rows");
     static_assert(!kMulti || (!kPrompt && !kFinal), "several chunks per workgroup: decode partials");
     static_assert(SP == 1 || RB * 8 * 64 * 16 <= 2 * kBuf,
@@ -649,7 +649,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
         j_end = max(j_begin, min(j_begin + p.chunk, n));
         tpc = 1 << 30;
         n_iter = (min(p.chunk, n) + kTile - 1) / kTile;  // pipeline 0's
-    } else if constexpr (!kPrompt) {
+    } else if constexpr (!kPrompt && SP == 1) {
         // This workgroup runs chunks [c0, c0 + cpw) of instance i as one
         // stream of tiles: the gather pipeline runs on across chunk
         // boundaries, and the compute waves emit a partial at the end of
@@ -660,6 +660,18 @@ void chunk_mfma_kernel(Params p, int cpw) {
         if (j_begin >= n) return;  // this instance has fewer chunks
         j_end = (int)min((int64_t)j_begin + (int64_t)cpw * p.chunk, (int64_t)n);
         tpc = p.chunk / kTile;  // tiles per chunk
+    } else if constexpr (!kPrompt) {
+        // Two pipelines, each its own chunk (2 y + h) and partial: the two
+        // independent workgroups of the one-pipeline form in one, so that
+        // the waves' placement on the SIMDs is fixed (see the roles above).
+        // A pipeline past the instance's chunks has no tiles and emits
+        // nothing; the pipelines share no step, so it just ends.
+        const int n = count_of(p, i);
+        if ((int64_t)blockIdx.y * SP * p.chunk >= n) return;  // both pipelines empty
+        c0 = blockIdx.y * SP + pipe;
+        j_begin = (int)min((int64_t)c0 * p.chunk, (int64_t)n);
+        j_end = (int)min((int64_t)j_begin + p.chunk, (int64_t)n);
+        tpc = 1 << 30;  // one chunk: its partial after the loop
     } else {
         // rows [row0, row0 + 16 RB) sit at positions pos0 + r / n_qheads; the
         // cells run to the last of them, clipped to the page table
@@ -674,7 +686,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
     if constexpr (!kFinal) n_iter = n_tiles;
     // the last list entry, the target of the clamped list loads (a pipeline
     // with no tiles reads a valid entry: a final-output call has max_sel > 0)
-    const int j_last = kFinal ? max(j_end - 1, 0) : j_end - 1;
+    const int j_last = (kFinal || SP > 1) ? max(j_end - 1, 0) : j_end - 1;
 
     // scale slots read before their first write hold finite values
     for (int e = threadIdx.x; e < SP * 4 * kTile; e += 64 * SP * kPipe) {
@@ -802,7 +814,7 @@ void chunk_mfma_kernel(Params p, int cpw) {
                 __syncthreads();
             }
         }
-        if constexpr (SP > 1) {  // the end of both pipelines, then the compute waves' hand-over
+        if constexpr (kFinal && SP > 1) {  // the end of both pipelines, then the compute waves' hand-over
             __syncthreads();
             __syncthreads();
         }
@@ -1184,12 +1196,21 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
     // (a workgroup with several chunks emits partials inside its tile loop:
     // a form of its own, so that the one-chunk form keeps that code out of
     // the loop)
-    if (items <= kLatencyWorkgroups && p.n_rows <= 32)
+    if (items <= kLatencyWorkgroups && p.n_rows <= 32) {
         launch_rb<2, false>(p, grid, cpw, s);  // cpw is 1 here
-    else if (cpw > 1)
+    } else if (cpw == 1 && p.n_chunks > 1 && (p.n_rows + 15) / 16 == 2) {
+        // two 16-row groups, one chunk per workgroup: two workgroups of three
+        // waves would share a CU, and the second continues the first's cycle
+        // over the SIMDs, leaving one SIMD two compute waves and another none;
+        // one workgroup of two pipelines (pairs of chunks) places its four
+        // compute waves on four SIMDs
+        const dim3 g2(p.n_inst, (p.n_chunks + 1) / 2);
+        chunk_mfma_kernel<2, 1, false, 2, false, false><<<g2, 64 * 6, 0, s>>>(p, 1);
+    } else if (cpw > 1) {
         launch_rb<1, true>(p, grid, cpw, s);
-    else
+    } else {
         launch_rb<1, false>(p, grid, cpw, s);
+    }
     return hipGetLastError();
 }
 

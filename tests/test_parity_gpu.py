@@ -278,6 +278,33 @@ def test_several_chunks_per_workgroup():
                      OUT_ATOL, OUT_RTOL, f"partial acc/l inst {i}")
 
 
+def test_two_row_groups_paired_chunks():
+    """Two 16-row groups with one chunk per workgroup run as pairs of chunks
+    in one workgroup of two pipelines: an odd chunk count (the last pair's
+    second chunk past the list) and ragged counts (instances ending in either
+    chunk of a pair, or before the pair).  Every chunk's partial and the
+    outputs against the oracle on sampled instances."""
+    from decode_attention_sparse_amd import api
+    say("case: paired chunks, 24 rows")
+    x = gen.make(None, seed=47, n_inst=100, n_q=2, pool_cells=1024, n_sel=320, sel="uniform",
+                 chunk=64)
+    rng = np.random.default_rng(48)
+    counts = rng.integers(0, 321, size=100).astype(np.int32)
+    counts[[0, 1, 2, 3, 4, 5]] = [320, 0, 64, 65, 129, 257]
+    x = dataclasses.replace(x, n_sel=counts)
+    ids = [0, 1, 2, 3, 4, 5, 33, 99]
+    out, lse, g, ws = two_pass(x, 64)  # 5 chunks: 3 workgroups per instance
+    check(x, out, lse, g, inst_ids=ids, what="paired chunks")
+    acc, m, l = (t.cpu().numpy() for t in api.partials(ws, 100, 2, 12, 320, 64))
+    racc, rm, rl = oracle.chunk_partials(x, 64, 8, inst_ids=ids)
+    for k, i in enumerate(ids):
+        nch = -(-int(counts[i]) // 64)
+        assert_close(m[i, :nch], rm[k, :nch], LSE_ATOL, LSE_RTOL, f"partial m inst {i}")
+        assert_close(l[i, :nch], rl[k, :nch], 0, 1e-3, f"partial l inst {i}")
+        assert_close(acc[i, :nch] / l[i, :nch, :, None], racc[k, :nch] / rl[k, :nch, :, None],
+                     OUT_ATOL, OUT_RTOL, f"partial acc/l inst {i}")
+
+
 @pytest.mark.parametrize("n_q", [1, 4])
 def test_small_grid_large_page_table(n_q):
     """A small (latency-bound) grid whose page table is too large to be read
