@@ -858,6 +858,10 @@ void chunk_mfma_kernel(Params p, int cpw) {
     auto emit = [&](int t) {
         if constexpr (!kPrompt && !kFinal) {
             const int c = kMulti ? c0 + t / tpc : c0;
+            // two pipelines: a wait that gave up (never in a correct run)
+            // poisons the partial, so that the merged rows come out NaN
+            if constexpr (SP > 1)
+                if (*reinterpret_cast<volatile int *>(&stuck_f)) rb.l_part = NAN;
             rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
             rb.reset();
         }

@@ -50,14 +50,17 @@
  *   - SDA_OK means that the work was launched, not that it finished well:
  *     launches are asynchronous and no call reads anything back.  One
  *     device-side failure is reported in the outputs instead: the
- *     two-pipeline form of the fused decode calls (sda_decode_attn_step /
- *     _batch / _batch_noalloc when sda_fused_single_launch holds and a
- *     workgroup runs an instance's two chunks) synchronises its waves with
- *     bounded waits on LDS flags; a wait that gives up (tens of
- *     milliseconds, never in a correct run) writes NaN to the out and lse
- *     rows of that workgroup, and the call has still returned SDA_OK.  A
- *     finite output is therefore part of a successful call's result: a
- *     caller that needs certainty checks out and lse for NaN.
+ *     two-pipeline forms of the chunk pass (a workgroup running two chunks
+ *     side by side: the fused decode calls when sda_fused_single_launch
+ *     holds and an instance has two chunks, and chunk passes of 17-32 rows
+ *     with one chunk per workgroup, in the fused calls and in
+ *     sda_chunk_batch) synchronise their waves with bounded waits on LDS
+ *     flags; a wait that gives up (tens of milliseconds, never in a correct
+ *     run) writes NaN to the out and lse rows of that workgroup, or to the
+ *     denominators of its chunk partials, which the merge turns into NaN
+ *     rows, and the call has still returned SDA_OK.  A finite output is
+ *     therefore part of a successful call's result: a caller that needs
+ *     certainty checks out and lse for NaN.
  *   - Device-side contents are trusted for shape (n_sel[i] is clamped to
  *     [0, max_sel]); ids out of range are masked, never dereferenced.
  *   - Outputs (out, lse, gather_out, the workspace, and the pools of
