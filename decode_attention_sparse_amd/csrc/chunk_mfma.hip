@@ -589,10 +589,11 @@ template <int RB, int DS, bool kPrompt, int SP = 1, bool kFinal = false, bool kM
 __global__ __launch_bounds__(64 * SP * (DS * RB + 1))
 __attribute__((amdgpu_waves_per_eu((RB == 1 || DS > 1) ? 1 : 2, 2)))
 void chunk_mfma_kernel(Params p, int cpw) {
-    static_assert(SP == 1 || (SP == 2 && !kPrompt && !kMulti && DS == 1 && RB >= 2 && RB <= 3),
-                  "two pipelines: decode, one chunk each, 2 or 3 row groups");
+    static_assert(SP == 1 || (SP == 2 && !kPrompt && DS == 1 && RB >= 2 && RB <= 3),
+                  "two pipelines: decode, 2 or 3 row groups");
+    static_assert(!(kMulti && kFinal), "several chunks per workgroup: partials");
     static_assert(!(kPrompt && kFinal), "the prompt form always writes its rows");
-    static_assert(!kMulti || (!kPrompt && !kFinal), "several chunks per workgroup: decode partials");
+    static_assert(!kMulti || !kPrompt, "several chunks per workgroup: decode partials");
     static_assert(SP == 1 || RB * 8 * 64 * 16 <= 2 * kBuf,
                   "the hand-over fits a pipeline's K (and V) buffers");
     constexpr int kPipe = DS * RB + 1;  // waves per pipeline
@@ -661,17 +662,18 @@ void chunk_mfma_kernel(Params p, int cpw) {
         j_end = (int)min((int64_t)j_begin + (int64_t)cpw * p.chunk, (int64_t)n);
         tpc = p.chunk / kTile;  // tiles per chunk
     } else if constexpr (!kPrompt) {
-        // Two pipelines, each its own chunk (2 y + h) and partial: the two
-        // independent workgroups of the one-pipeline form in one, so that
-        // the waves' placement on the SIMDs is fixed (see the roles above).
-        // A pipeline past the instance's chunks has no tiles and emits
-        // nothing; the pipelines share no step, so it just ends.
+        // Two pipelines, each its own cpw chunks from (2 y + h) cpw and its
+        // partials: the two independent workgroups of the one-pipeline form
+        // in one, so that the waves' placement on the SIMDs is fixed (see
+        // the roles above).  A pipeline past the instance's chunks has no
+        // tiles and emits nothing; the pipelines share no step, so it just
+        // ends.
         const int n = count_of(p, i);
-        if ((int64_t)blockIdx.y * SP * p.chunk >= n) return;  // both pipelines empty
-        c0 = blockIdx.y * SP + pipe;
+        if ((int64_t)blockIdx.y * SP * cpw * p.chunk >= n) return;  // both pipelines empty
+        c0 = (blockIdx.y * SP + pipe) * cpw;
         j_begin = (int)min((int64_t)c0 * p.chunk, (int64_t)n);
-        j_end = (int)min((int64_t)j_begin + p.chunk, (int64_t)n);
-        tpc = 1 << 30;  // one chunk: its partial after the loop
+        j_end = (int)min((int64_t)j_begin + (int64_t)cpw * p.chunk, (int64_t)n);
+        tpc = kMulti ? p.chunk / kTile : 1 << 30;  // one chunk: its partial after the loop
     } else {
         // rows [row0, row0 + 16 RB) sit at positions pos0 + r / n_qheads; the
         // cells run to the last of them, clipped to the page table
@@ -1202,14 +1204,17 @@ hipError_t launch_chunk(const Params &p, hipStream_t s) {
     // the loop)
     if (items <= kLatencyWorkgroups && p.n_rows <= 32) {
         launch_rb<2, false>(p, grid, cpw, s);  // cpw is 1 here
-    } else if (cpw == 1 && p.n_chunks > 1 && (p.n_rows + 15) / 16 == 2) {
-        // two 16-row groups, one chunk per workgroup: two workgroups of three
-        // waves would share a CU, and the second continues the first's cycle
-        // over the SIMDs, leaving one SIMD two compute waves and another none;
-        // one workgroup of two pipelines (pairs of chunks) places its four
-        // compute waves on four SIMDs
-        const dim3 g2(p.n_inst, (p.n_chunks + 1) / 2);
-        chunk_mfma_kernel<2, 1, false, 2, false, false><<<g2, 64 * 6, 0, s>>>(p, 1);
+    } else if (p.n_chunks > cpw && (p.n_rows + 15) / 16 == 2) {
+        // two 16-row groups: two workgroups of three waves would share a CU,
+        // and the second continues the first's cycle over the SIMDs, leaving
+        // one SIMD two compute waves and another none; one workgroup of two
+        // pipelines (each with cpw chunks) places its four compute waves on
+        // four SIMDs
+        const dim3 g2(p.n_inst, (grid.y + 1) / 2);
+        if (cpw > 1)
+            chunk_mfma_kernel<2, 1, false, 2, false, true><<<g2, 64 * 6, 0, s>>>(p, cpw);
+        else
+            chunk_mfma_kernel<2, 1, false, 2, false, false><<<g2, 64 * 6, 0, s>>>(p, 1);
     } else if (cpw > 1) {
         launch_rb<1, true>(p, grid, cpw, s);
     } else {
