@@ -62,11 +62,11 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "65ea60db37f79a4ffb9e8aedc2b46a2b157f1c0beab78f7364d1e551ffe77026", "fetch_bytes": 1895146, "write_bytes": 1634688},
+              "sources_sha256": "915af14bbfaa51544aea14355dc531d2e2c0336565ae4b3153545fcfa78190f9", "fetch_bytes": 1895125, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "65ea60db37f79a4ffb9e8aedc2b46a2b157f1c0beab78f7364d1e551ffe77026", "fetch_bytes": 260156838, "write_bytes": 25264128},
+               "sources_sha256": "915af14bbfaa51544aea14355dc531d2e2c0336565ae4b3153545fcfa78190f9", "fetch_bytes": 260156151, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
