@@ -11,12 +11,18 @@
 // instance when the grid is large -- with DS * RB + 1 waves: compute wave w
 // owns query rows [16 (w / DS), 16 (w / DS) + 16) for the whole chunk (and
 // 256 / DS of the head dimensions), so every softmax statistic of a row
-// lives in one wave; the last wave is the producer: it runs the gather and
+// lives in one wave; one more wave is the producer: it runs the gather and
 // stages all code rows (the compute waves issue no global loads and hold no
 // staging registers).  Cells are processed in tiles of 64.  The compute
 // waves' state and per-tile step (RowBlock) are shared by all launches:
 //   chunk_mfma_kernel<RB, DS, false>           the pipelined chunk pass below
 //                                              (chunk partials);
+//   chunk_mfma_kernel<2, 1, false, 2>          the same for two 16-row
+//                                              groups, two pipelines (a
+//                                              chunk or run of chunks each)
+//                                              per workgroup, so that the
+//                                              compute waves sit on four
+//                                              SIMDs;
 //   chunk_mfma_kernel<RB, DS, false, 1, true>  the same for calls with one
 //                                              chunk per instance, writing
 //                                              the normalised outputs;
