@@ -74,7 +74,7 @@ MEASURED_TRAFFIC = {
     "qsa": {"sources": ("decode_attention_sparse_amd/csrc/qsa_select.hip",
                         "decode_attention_sparse_amd/csrc/sda_internal.h",
                         "decode_attention_sparse_amd/csrc/sda_api.hip"),
-            "sources_sha256": "4d4c98f78cced5dd7ea1e3f32c9af2c6da0597a73aa6d10c1646829a177f3e5a", "fetch_bytes": 67962699, "write_bytes": 274227},
+            "sources_sha256": "9338948246981d5312d74a9b53053de3204cfae85502097291edb62ed205a782", "fetch_bytes": 67962643, "write_bytes": 275488},
 }
 
 

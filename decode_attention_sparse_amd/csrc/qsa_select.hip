@@ -246,14 +246,26 @@ __global__ __launch_bounds__(kSelectThreads) void qsa_select_kernel(QsaParams p)
         off += cnt;
     }
     __syncthreads();
-    // cells of each selected block, one block per wave at a time
+    // cells of each selected block, one block per wave at a time: four
+    // consecutive cells per lane in one 16-byte store where the block's
+    // place in the list is 16-byte aligned and it lies wholly inside the
+    // list, single cells otherwise
     int32_t *out = p.sel + (int64_t)i * p.sel_stride;
+    const bool base_aligned = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
     for (int s = wave; s < min(blocks_total, kQsaMaxK); s += kSelectThreads / 64) {
         const int b = sel_block[s];
+        const int off = sel_off[s];
         const int64_t c0 = (int64_t)b * p.block_cells;
         const int cnt = (int)max((int64_t)0, min((int64_t)p.block_cells, extent - c0));
-        for (int c = lane; c < cnt; c += 64)
-            if (sel_off[s] + (int64_t)c < p.sel_stride) out[sel_off[s] + c] = (int32_t)(c0 + c);
+        if (base_aligned && (off & 3) == 0 && (cnt & 3) == 0 && off + (int64_t)cnt <= p.sel_stride) {
+            for (int c = 4 * lane; c < cnt; c += 256) {
+                const int v = (int)(c0 + c);
+                *reinterpret_cast<int4 *>(out + off + c) = make_int4(v, v + 1, v + 2, v + 3);
+            }
+        } else {
+            for (int c = lane; c < cnt; c += 64)
+                if (off + (int64_t)c < p.sel_stride) out[off + c] = (int32_t)(c0 + c);
+        }
     }
     if (tid == 0) p.n_sel[i] = cells_total;
 }

@@ -24,9 +24,10 @@ pytestmark = pytest.mark.gpu
 U32 = 2.0 ** -24
 
 
-def run_qsa(x, k_blocks=None):
+def run_qsa(x, k_blocks=None, pad=0):
     """Scores and selection on the GPU: numpy scores [n_inst][n_rows][B],
-    sel [n_inst][k R], n_sel [n_inst], plus the device sel and n_sel."""
+    sel [n_inst][k R], n_sel [n_inst], plus the device sel and n_sel.  With
+    pad > 0 the selection rows are pad entries longer than k R."""
     import torch
     from decode_attention_sparse_amd import api
     k = x.k_blocks if k_blocks is None else k_blocks
@@ -34,7 +35,7 @@ def run_qsa(x, k_blocks=None):
     pooled, dead, q, vis = t(x.pooled), t(x.dead), t(x.q_idx), t(x.n_visible)
     scores = torch.full((x.n_inst, x.n_rows, x.max_blocks), float("nan"), device="cuda")
     api.qsa_block_scores(pooled, dead, q, vis, x.block_cells, scores)
-    stride = max(k * x.block_cells, 1)
+    stride = max(k * x.block_cells, 1) + pad
     sel = torch.full((x.n_inst, stride), -7, dtype=torch.int32, device="cuda")
     n_sel = torch.full((x.n_inst,), -7, dtype=torch.int32, device="cuda")
     api.qsa_select(scores, vis, x.block_cells, k, sel, n_sel)
@@ -49,9 +50,11 @@ def score_bound(x):
     return 64 * U32 * np.einsum("irk,ibk->irb", a, b) + 1e-30
 
 
-def check_qsa(x, k_blocks=None, what=""):
+def check_qsa(x, k_blocks=None, what="", pad=0):
     k = x.k_blocks if k_blocks is None else k_blocks
-    got, sel, n_sel, _, _ = run_qsa(x, k)
+    got, sel, n_sel, _, _ = run_qsa(x, k, pad)
+    for i in range(x.n_inst):
+        assert (sel[i, n_sel[i]:] == -7).all(), f"{what}: instance {i} written past its list"
     ref = oracle.qsa_scores(x)
     ninf = np.isneginf(ref)
     assert np.array_equal(np.isneginf(got), ninf), f"{what}: -inf pattern differs"
@@ -130,6 +133,25 @@ def test_qsa_live_extents(extent):
                      block_cells=256, max_blocks=1024, k_blocks=32, dead_frac=0.02,
                      context=[extent - 300, extent - 256, extent])
     check_qsa(x, what=f"extent {extent}")
+
+
+@pytest.mark.parametrize("pad", [0, 1, 3])
+def test_qsa_ragged_rows_and_strides(pad):
+    """Lists whose rows start off a 16-byte boundary (row stride k R + pad)
+    and extents that end inside a block at every remainder mod 4, so the
+    cell lists are written both four cells per store and one at a time."""
+    say(f"case: QSA ragged extents, selection row stride k R + {pad}")
+    ctx = [4317, 4318, 4319, 4320, 4001]
+    x = gen.make_qsa(None, seed=11 + pad, n_inst=5, n_rows=2, n_heads=2, idx_dim=64,
+                     block_cells=48, max_blocks=90, k_blocks=12, dead_frac=0.05, context=ctx)
+    # the block holding each instance's last visible cell live and on top
+    pooled, dead = x.pooled.copy(), x.dead.copy()
+    for i, c in enumerate(ctx):
+        pooled[i, (c - 1) // 48] = 8 * x.q_idx[i, 0]
+        dead[i, (c - 1) // 48] = 0
+    x = dataclasses.replace(x, pooled=pooled, dead=dead)
+    _, sel, n_sel = check_qsa(x, what=f"pad {pad}", pad=pad)
+    assert list(n_sel % 4) == [1, 2, 3, 0, 1], n_sel
 
 
 def test_qsa_equal_keys():
