@@ -74,7 +74,7 @@ MEASURED_TRAFFIC = {
     "qsa": {"sources": ("decode_attention_sparse_amd/csrc/qsa_select.hip",
                         "decode_attention_sparse_amd/csrc/sda_internal.h",
                         "decode_attention_sparse_amd/csrc/sda_api.hip"),
-            "sources_sha256": "9338948246981d5312d74a9b53053de3204cfae85502097291edb62ed205a782", "fetch_bytes": 67962643, "write_bytes": 275488},
+            "sources_sha256": "5766a3aadb5a8357bd85ba797783d81c1cf954301a2b25432b9d56d9e82276eb", "fetch_bytes": 67963015, "write_bytes": 274933},
 }
 
 

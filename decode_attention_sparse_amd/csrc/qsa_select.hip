@@ -20,14 +20,20 @@
 // broadcasts), and the 16 partial sums of a row meet through lane swaps.
 // Blocks no row can use (dead, or past every row's extent) are not read.
 //
-// qsa_select_kernel: one workgroup per instance.  The combined scores
-// become order-preserving 32-bit keys in LDS (0 for -inf); a radix select
-// over four 8-bit digits (a 256-bin histogram per digit, the digit found by
-// a suffix scan across one wave) gives the key of the k-th largest block and
+// qsa_select_kernel: one workgroup per instance, or up to eight in grids
+// of fewer than 256 instances, each computing the same selection and
+// writing its share of the cell list (with one workgroup per instance the
+// writes took a quarter of the kernel's time).  The scores are loaded a few
+// blocks per thread at a time, all rows at once, and become
+// order-preserving 32-bit keys in LDS (0 for -inf); a radix select over
+// four 8-bit digits (a 256-bin histogram per digit, the digit found by a
+// suffix scan across one wave) gives the key of the k-th largest block and
 // how many blocks with exactly that key are taken; a scan in block order
 // then marks the selected blocks (all larger keys, and the first of the
 // equal ones), a second scan gives each its offset in the cell list, and
 // each wave writes the cells of one block at a time with coalesced stores.
+#include <algorithm>
+
 #include "sda_internal.h"
 
 namespace sda {
@@ -38,6 +44,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kScoreThreads = 256;        // 16 lanes per block, 16 blocks at a time
 constexpr int kScoreBlocksPerGroup = 64;  // blocks per workgroup
 constexpr int kSelectThreads = 256;
+constexpr int kKeyBatch = 4;  // blocks per thread whose scores are loaded together
 
 // Sum over the 16 lanes of a row of lanes (xor swaps within the row).
 __device__ __forceinline__ float sum16(float x) {
@@ -143,21 +150,50 @@ __global__ __launch_bounds__(kSelectThreads) void qsa_select_kernel(QsaParams p)
     const int i = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int B = p.max_blocks;
-    int64_t extent = 0;
-    for (int r = 0; r < p.n_rows; ++r)
-        extent = max(extent, (int64_t)p.n_visible[(int64_t)i * p.n_rows + r]);
-    extent = min(extent, (int64_t)B * p.block_cells);
-
-    // combined scores as keys; live blocks counted
+    // The loads below take clamped indices (a row past n_rows reads the last
+    // row again, a block past B block B - 1; neither changes a maximum), so
+    // that none is conditional and all are in flight at once.
+    const int last_row = p.n_rows - 1;
+    // combined scores as keys, kKeyBatch blocks per thread at a time; live
+    // blocks counted
+    const float *sc = p.scores + (int64_t)i * p.n_rows * B;
+    auto load = [&](int b0, float (&c)[kKeyBatch]) {
+#pragma unroll
+        for (int k = 0; k < kKeyBatch; ++k) c[k] = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kQsaMaxRows; ++r)
+#pragma unroll
+            for (int k = 0; k < kKeyBatch; ++k)
+                c[k] = fmaxf(c[k], sc[(int64_t)min(r, last_row) * B +
+                                      min(b0 + k * kSelectThreads, B - 1)]);
+    };
     int live = 0;
-    for (int b = tid; b < B; b += kSelectThreads) {
-        float c = -INFINITY;
-        for (int r = 0; r < p.n_rows; ++r)
-            c = fmaxf(c, p.scores[((int64_t)i * p.n_rows + r) * B + b]);
-        const unsigned k = key_of(c);
-        keys[b] = k;
-        live += k != 0u;
+    auto put = [&](int b0, const float (&c)[kKeyBatch]) {
+#pragma unroll
+        for (int k = 0; k < kKeyBatch; ++k) {
+            const int b = b0 + k * kSelectThreads;
+            if (b < B) {
+                const unsigned key = key_of(c[k]);
+                keys[b] = key;
+                live += key != 0u;
+            }
+        }
+    };
+    float c0[kKeyBatch];
+    load(tid, c0);
+    // lane r < n_rows: row r's extent (loaded beside the first scores, used
+    // after the keys)
+    int nv = p.n_visible[(int64_t)i * p.n_rows + min(lane, last_row)];
+    put(tid, c0);
+    for (int b0 = tid + kKeyBatch * kSelectThreads; b0 < B; b0 += kKeyBatch * kSelectThreads) {
+        float c[kKeyBatch];
+        load(b0, c);
+        put(b0, c);
     }
+    // the largest over lanes 0..7 (rows past n_rows repeat the last row)
+#pragma unroll
+    for (int d = 1; d < kQsaMaxRows; d <<= 1) nv = max(nv, __shfl_xor(nv, d, kQsaMaxRows));
+    const int64_t extent = min((int64_t)max(__shfl(nv, 0), 0), (int64_t)B * p.block_cells);
     int n_live;
     (void)block_scan(live, part, &n_live);  // (also orders the key writes before the reads below)
     const int kk = min(p.k_blocks, n_live);
@@ -252,7 +288,9 @@ __global__ __launch_bounds__(kSelectThreads) void qsa_select_kernel(QsaParams p)
     // list, single cells otherwise
     int32_t *out = p.sel + (int64_t)i * p.sel_stride;
     const bool base_aligned = (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-    for (int s = wave; s < min(blocks_total, kQsaMaxK); s += kSelectThreads / 64) {
+    const int split = gridDim.y;  // workgroups sharing this instance's writes
+    for (int s = wave + (kSelectThreads / 64) * blockIdx.y; s < min(blocks_total, kQsaMaxK);
+         s += (kSelectThreads / 64) * split) {
         const int b = sel_block[s];
         const int off = sel_off[s];
         const int64_t c0 = (int64_t)b * p.block_cells;
@@ -267,7 +305,7 @@ __global__ __launch_bounds__(kSelectThreads) void qsa_select_kernel(QsaParams p)
                 if (off + (int64_t)c < p.sel_stride) out[off + c] = (int32_t)(c0 + c);
         }
     }
-    if (tid == 0) p.n_sel[i] = cells_total;
+    if (tid == 0 && blockIdx.y == 0) p.n_sel[i] = cells_total;
 }
 
 }  // namespace
@@ -286,7 +324,13 @@ hipError_t launch_qsa_scores(const QsaParams &p, hipStream_t s) {
 }
 
 hipError_t launch_qsa_select(const QsaParams &p, hipStream_t s) {
-    qsa_select_kernel<<<dim3(p.n_inst), kSelectThreads, 0, s>>>(p);
+    // grids of fewer than 256 instances: up to eight workgroups per
+    // instance (one per CU at this LDS size), each computing the same
+    // selection and writing its share of the selected blocks' cells
+    const int per_wg = kSelectThreads / 64;
+    int split = (int)std::max<int64_t>(1, std::min<int64_t>(8, 256 / std::max(1, p.n_inst)));
+    split = std::max(1, std::min(split, (p.k_blocks + per_wg - 1) / per_wg));
+    qsa_select_kernel<<<dim3(p.n_inst, split), kSelectThreads, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -401,8 +401,9 @@ int sda_qsa_block_scores(int32_t n_inst, int32_t n_rows, int32_t n_heads, int32_
                          const uint8_t *dead, const float *q_idx, const int32_t *n_visible,
                          float *scores, void *stream);
 
-/* sda_qsa_select: top-k selection and expansion to cells, one workgroup per
- * instance, from scores laid out as sda_qsa_block_scores writes them (any
+/* sda_qsa_select: top-k selection and expansion to cells (one workgroup per
+ * instance, up to eight per instance when there are fewer than 256
+ * instances), from scores laid out as sda_qsa_block_scores writes them (any
  * values: -inf is never selected; other non-finite values are unspecified).
  *   n_inst        host, >= 0 (0: nothing is launched)
  *   n_rows, block_cells, n_visible  as above

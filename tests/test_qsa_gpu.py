@@ -110,6 +110,10 @@ GEOMS = {
                           max_blocks=50, dead_frac=0.5), 50),
     "k_zero": (dict(n_inst=2, n_rows=2, n_heads=1, idx_dim=64, block_cells=64, max_blocks=50),
                0),
+    # 256 or more instances: one selection workgroup each (below that, up
+    # to eight share an instance's writes, as in every other case here)
+    "many_instances_one_group_each": (dict(n_inst=300, n_rows=2, n_heads=1, idx_dim=64,
+                                           block_cells=16, max_blocks=40, dead_frac=0.1), 5),
     "max_blocks_16384": (dict(n_inst=2, n_rows=4, n_heads=1, idx_dim=64, block_cells=16,
                               max_blocks=16384, dead_frac=0.01), 4096),
 }
