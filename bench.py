@@ -74,7 +74,7 @@ MEASURED_TRAFFIC = {
     "qsa": {"sources": ("decode_attention_sparse_amd/csrc/qsa_select.hip",
                         "decode_attention_sparse_amd/csrc/sda_internal.h",
                         "decode_attention_sparse_amd/csrc/sda_api.hip"),
-            "sources_sha256": "5766a3aadb5a8357bd85ba797783d81c1cf954301a2b25432b9d56d9e82276eb", "fetch_bytes": 67963015, "write_bytes": 274933},
+            "sources_sha256": "3d99c9d643b4c40526849f675eee0e985dba29066397c14714fb08fea6227f44", "fetch_bytes": 68185156, "write_bytes": 262517},
 }
 
 
