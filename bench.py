@@ -62,11 +62,11 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "915af14bbfaa51544aea14355dc531d2e2c0336565ae4b3153545fcfa78190f9", "fetch_bytes": 1895125, "write_bytes": 1634688},
+              "sources_sha256": "074bee5814b91d11af9a219b23b3f095ce9e3b034076ded6d6ed07977295e47e", "fetch_bytes": 1886235, "write_bytes": 1634714},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "915af14bbfaa51544aea14355dc531d2e2c0336565ae4b3153545fcfa78190f9", "fetch_bytes": 260156151, "write_bytes": 25264128},
+               "sources_sha256": "074bee5814b91d11af9a219b23b3f095ce9e3b034076ded6d6ed07977295e47e", "fetch_bytes": 161504458, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
@@ -419,11 +419,12 @@ def prompt_section(reps, cpu_seconds):
         "query_rows_x_visible_cells": pairs,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_MFMA_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / INT8_MFMA_PEAK_TOPS, 4),
-                     "traffic": measured_traffic("prompt"), "kernel": "chunk_mfma_kernel (prompt form)",
+                     "traffic": measured_traffic("prompt"),
+                     "kernel": "prompt_dma_kernel (96-row workgroups of eight compute waves, one per CU)",
                      "algorithmic_flops_per_launch": flops, "launch_ms_mean": round(ms, 4),
                      "note": "flops of the fp32-accurate products (q.k and p.v, 2 x 256 each per "
                              "row and visible cell) against the int8 matrix peak that runs them; "
-                             "the digit splits issue 3 int8 products per q.k and 2 per p.v"},
+                             "the digit splits issue 3 int8 products per q.k and 3 per p.v"},
         "pages_2080ti_ms_per_chunk": PROMPT_PAGES_MS,
         "speedup_vs_pages_v3": round(PROMPT_PAGES_MS["v3"] / ms, 2),
         "timing": f"{reps} calls captured in one HIP graph, HIP events around its replay",

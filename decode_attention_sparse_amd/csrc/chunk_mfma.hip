@@ -148,16 +148,39 @@ __device__ __forceinline__ float sum4(float x) {
 // twice the prompt kernel's counted bank conflicts.)
 __device__ __forceinline__ int lds_row(int cb, int l) { return 16 * cb + (l ^ (8 * (cb & 1))); }
 
+// LDS layout of tiles staged by LDS-DMA loads (the prompt kernel with no
+// producer wave): such a load writes 64 lanes x 16 bytes contiguously, so
+// one instruction stages 4 code rows.  Tile cell c (block b = c / 4) sits at
+// kDmaBlock b + 64 sigma(b) + 256 (c % 4), and its 16-byte granule G
+// (bytes 16 G .. 16 G + 15) at slot G ^ (c % 4) of that row.  The blocks'
+// shifts sigma spread the rows that one read instruction touches over the 64
+// banks: for K reads (16 consecutive cells, one granule) sigma_K(b) = b % 4;
+// for the transposed V reads (cells 0-7 and 16-23, or 8-15 and 24-31, of a
+// 32-cell half, one granule) sigma_V(b) = (b & 1) | (((b >> 2) & 1) << 1).
+constexpr int kDmaBlock = 1280;           // 1 KB of rows and room for the shift
+constexpr int kDmaBuf = 16 * kDmaBlock;   // one tile of K or V rows
+__host__ __device__ constexpr int dma_sigma_k(int b) { return b & 3; }
+__host__ __device__ constexpr int dma_sigma_v(int b) { return (b & 1) | (((b >> 2) & 1) << 1); }
+__host__ __device__ constexpr int dma_row_k(int c) {
+    return kDmaBlock * (c >> 2) + 64 * dma_sigma_k(c >> 2) + 256 * (c & 3);
+}
+__host__ __device__ constexpr int dma_row_v(int c) {
+    return kDmaBlock * (c >> 2) + 64 * dma_sigma_v(c >> 2) + 256 * (c & 3);
+}
+
 // The state of one compute wave: query digits, per-lane LDS offsets, and the
 // running softmax statistics and accumulator of its 16 query rows (for the
 // head dimensions [256 dh / DS, 256 (dh + 1) / DS) it owns, kDB = 16 / DS
 // blocks of 16).  step() is one tile; both kernels run exactly this sequence
 // per chunk, so a chunk's partial does not depend on the kernel or launch.
-template <int kDB>
+template <int kDB, bool kDma = false>
 struct RowBlock {
+    // LDS bytes between the K rows of consecutive 16-cell blocks
+    static constexpr int kCbStride = kDma ? 4 * kDmaBlock : 16 * kStride;
     v4i qa[4], qb[4], qc[4];  // query digits: B operands of S^T = K Q^T
     float coef;  // sigma * |scale_log2| / 2^8: S (base 2) = coef * (AB + C / 2^8) * k_scale
     int k_off0, k_off1, v_off, m_off0, m_off1;
+    int v_offj[kDma ? 4 : 1];  // DMA layout: V read offsets for 16-dim blocks db % 4 = j
     int w_off;     // this pipeline's offset in the arrays of 1 / W (wave-uniform)
     float m_run;   // running max of this lane's row (base-2 units)
     float l_part;  // this lane's share of the row denominator
@@ -225,16 +248,33 @@ struct RowBlock {
             }
         }
         // per-lane constant LDS offsets (everything else is an immediate):
-        // K operand of cell block cb, slab s: row lds_row(cb, l16), bytes 64s + 16g
-        k_off0 = lds_row(0, l16) * kStride + 16 * g;
-        k_off1 = (lds_row(1, l16) - 16) * kStride + 16 * g;
-        // transposed V read: source role (b, h) = (l16 >> 1, l16 & 1) reads row
-        // lds_row(2r + (b >> 2), 4g + (b & 3)), bytes 16db + 8h
         const int tb = l16 >> 1, th = l16 & 1;
-        v_off = lds_row(tb >> 2, 4 * g + (tb & 3)) * kStride + 8 * th;
-        // this lane's S cells (cb, 4g + u) live in LDS rows lds_row(cb, 4g + u)
-        m_off0 = lds_row(0, 4 * g);
-        m_off1 = lds_row(1, 4 * g) - 16;
+        if constexpr (kDma) {
+            // K operand of cell block cb, slab s: cell 16 cb + l16, granule
+            // 4s + g, at dma_row_k(l16) + 16 ((4s + g) ^ (l16 % 4)) + cb
+            // kCbStride = (constant) + 64 s
+            k_off0 = k_off1 = dma_row_k(l16) + 16 * (g ^ (l16 & 3));
+            // transposed V read of cell c = 16 (tb >> 2) + 4g + (tb & 3) (and c
+            // + 32), bytes 16 db + 8 th: granule db at slot db ^ (c % 4), so
+            // the offset depends on db % 4 (one per value) and on db / 4
+            // (an immediate 64 (db / 4))
+            const int c = 16 * (tb >> 2) + 4 * g + (tb & 3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v_offj[j] = dma_row_v(c) + 16 * (j ^ (c & 3)) + 8 * th;
+            v_off = 0;
+            // this lane's S cells (cb, 4g + u) are tile cells 16 cb + 4g + u
+            m_off0 = m_off1 = 4 * g;
+        } else {
+            // K operand of cell block cb, slab s: row lds_row(cb, l16), bytes 64s + 16g
+            k_off0 = lds_row(0, l16) * kStride + 16 * g;
+            k_off1 = (lds_row(1, l16) - 16) * kStride + 16 * g;
+            // transposed V read: source role (b, h) = (l16 >> 1, l16 & 1) reads row
+            // lds_row(2r + (b >> 2), 4g + (b & 3)), bytes 16db + 8h
+            v_off = lds_row(tb >> 2, 4 * g + (tb & 3)) * kStride + 8 * th;
+            // this lane's S cells (cb, 4g + u) live in LDS rows lds_row(cb, 4g + u)
+            m_off0 = lds_row(0, 4 * g);
+            m_off1 = lds_row(1, 4 * g) - 16;
+        }
         w_off = 0;
         reset();
 #pragma unroll
@@ -343,7 +383,7 @@ struct RowBlock {
     // 16 cb + 15 of the tile).
     __device__ __forceinline__ v4f score_block(int cb, const int8_t *kb, const float *ks_t,
                                                const float *bias_t) {
-        const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + 16 * cb * kStride;
+        const int8_t *kp = kb + ((cb & 1) ? k_off1 : k_off0) + cb * kCbStride;
         v4i ka[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) ka[s] = *reinterpret_cast<const v4i *>(kp + 64 * s);
@@ -468,9 +508,13 @@ struct RowBlock {
         const int8_t *vp = vb + v_off + 16 * kDB * dh;
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
-            const v2i h0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)(vp + 16 * db));
-            const v2i h1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (v2i LDS_AS *)(vp + 32 * kStride + 16 * db));
+            // this lane's 8 bytes of V rows (cells) at dims 16 (kDB dh + db):
+            // padded rows, or the DMA layout (kDB dh is a multiple of 4, so
+            // the granule's slot is kDB dh + 4 (db / 4) + ((db % 4) ^ (c % 4)))
+            const int8_t *v0 = kDma ? vb + v_offj[db & 3] + 16 * kDB * dh + 64 * (db >> 2) : vp + 16 * db;
+            const int8_t *v1 = kDma ? v0 + 8 * kDmaBlock : v0 + 32 * kStride;
+            const v2i h0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)v0);
+            const v2i h1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i LDS_AS *)v1);
             const v4i va = {h0[0], h0[1], h1[0], h1[1]};
             const v4i hi = mfma_i8(va, xa, (v4i){0, 0, 0, 0});
             const v4i mid = mfma_i8(va, xb, (v4i){0, 0, 0, 0});
@@ -1157,6 +1201,231 @@ void chunk_tile_kernel(Params p) {
     rb.emit(p, ((int64_t)i * p.n_chunks + c) * R + row, row, g, dh);
 }
 
+// Prompt attention with no producer wave: one workgroup of eight compute
+// waves per CU holds six 16-row groups (96 rows).  Waves 0-3 take groups 0-3
+// whole; waves 4-7 take groups 4 and 5 two waves each, each wave scoring two
+// of a tile's four 16-cell blocks (the blocks meet in LDS) and accumulating
+// 128 of the 256 dimensions.  The hardware puts waves k and k + 4 on one
+// SIMD, so every SIMD runs one whole group and half of another: the vector
+// and matrix work is even over the four SIMDs (with two workgroups of three
+// groups and a producer, two SIMDs carry two groups each and two carry one).
+// Every wave stages part of each tile with LDS-DMA loads (no staging
+// registers): in step t waves 0-3 four 1 KB blocks each of K rows of tile
+// t + 2, waves 4-7 four of V rows of tile t + 1; wave 4 also maps tile t + 3's
+// cells to physical cells (into LDS, for those loads) and loads its scales.
+// The instance's page-table row is read into LDS once.  Each step ends with the
+// waves' own loads complete and one workgroup barrier.  Step t: softmax and
+// V accumulation of tile t, scores of tile t + 1 (as in the pipelined
+// kernel).  The arithmetic per row is RowBlock's, so a row's result is the
+// other prompt form's up to the order of the cells within a tile.
+constexpr int kDmaWaves = 8;
+constexpr int kDmaRows = 96;  // six 16-row groups
+
+// One LDS-DMA load: each lane's 16 bytes at src to LDS lds_dst + 16 lane
+// (lds_dst wave-uniform).  Written as inline assembly so that the compiler
+// does not see an LDS write in flight: it would otherwise wait for the load
+// before every LDS access that might alias it, i.e. within the step that
+// issued it.  The kernel waits for its loads itself (vmcnt) before the
+// barrier that publishes them.  M0 is used by no other instruction of the
+// kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 in the clobbers (see above)
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
+    const unsigned a = (unsigned)(uintptr_t)(LDS_AS const void *)lds_dst;
+    __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(a)
+                     : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__global__ __launch_bounds__(64 * kDmaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prompt_dma_kernel(Params p) {
+    __shared__ __attribute__((aligned(1024))) int8_t kbuf[2][kDmaBuf];
+    __shared__ __attribute__((aligned(1024))) int8_t vbuf[2][kDmaBuf];
+    __shared__ __attribute__((aligned(16))) float ks_s[4][kTile];
+    __shared__ __attribute__((aligned(16))) float vs_s[4][kTile];
+    __shared__ float vw_s[4];
+    __shared__ __attribute__((aligned(16))) float bias_s[4][kTile];
+    // shared scores of the split groups: [tile parity][group 4 or 5][block][lane]
+    __shared__ __attribute__((aligned(16))) v4f xs[2][2][4][64];
+    __shared__ __attribute__((aligned(16))) int pt_s[kPtLdsPages];
+    // physical cell (or -1) of tile cell c at [slot][16 (c % 4) + c / 4]: the
+    // four cells one lane loads in a wave's four blocks are adjacent
+    __shared__ __attribute__((aligned(16))) int phys_s[4][kTile];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int i = blockIdx.x;
+    const int R = p.n_rows;
+    const int row0 = blockIdx.y * kDmaRows;
+    const int64_t pos0 = p.pos0[i];
+    const int last_row = min(row0 + kDmaRows, R) - 1;
+    const int nlp = p.n_logical_pages;  // at most kPtLdsPages (the launch checks)
+    const int j_end = (int)max((int64_t)0, min(pos0 + last_row / p.n_qheads + 1, (int64_t)nlp * kPage));
+    const int n_tiles = (j_end + kTile - 1) / kTile;
+
+    // the page-table row, and scale slots that are read before their first
+    // write holding finite values
+    const int32_t *pt = p.page_table + (int64_t)i * p.pt_stride;
+    for (int e = threadIdx.x; e < nlp; e += 64 * kDmaWaves) pt_s[e] = pt[e];
+    for (int e = threadIdx.x; e < 4 * kTile; e += 64 * kDmaWaves) {
+        (&ks_s[0][0])[e] = 0.f;
+        (&vs_s[0][0])[e] = 0.f;
+        (&bias_s[0][0])[e] = -INFINITY;
+        if (e < 4) vw_s[e] = 0.f;
+    }
+    __syncthreads();
+
+    // physical cell of tile cell c of tile t, or -1 (past the cells, or an
+    // unmapped page)
+    auto phys_of = [&](int t, int c) {
+        const int j = t * kTile + c;
+        if (j >= j_end) return -1;
+        const int pte = pt_s[j >> 4];
+        return (pte >= 0 && (int64_t)pte < p.n_phys_pages) ? ((pte << 4) | (j & 15)) : -1;
+    };
+    // blocks 4w .. 4w + 3 (cells 16w .. 16w + 15) of tile t's K or V rows:
+    // lane L writes slot L % 16 of cell 4b + L / 16, which holds the row's
+    // granule (L % 16) ^ (L / 16); masked cells read cell 0 (weight 0)
+    auto dma_blocks = [&](const int8_t *codes, int8_t *buf, int w, bool is_v, int t) {
+        const int r = lane >> 4, q = lane & 15;
+        const v4i ph4 = *reinterpret_cast<const v4i *>(&phys_s[t & 3][16 * r + 4 * w]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int b = 4 * w + k;
+            const int8_t *src = codes + (int64_t)(ph4[k] < 0 ? 0 : ph4[k]) * kDim + 16 * (q ^ r);
+            dma16(src, buf + kDmaBlock * b + 64 * (is_v ? dma_sigma_v(b) : dma_sigma_k(b)));
+        }
+    };
+    // step t's staging: K rows of tile t + 2 (waves 0-3), V rows of tile t + 1
+    // (waves 4-7); wave 4 also maps tile t + 3's cells and loads its scales
+    // (written to LDS by scales_done once they arrive)
+    unsigned kh = 0, vh = 0;
+    int ph_s = -1;
+    auto stage = [&](int t) {
+        if (wave < 4) {
+            if (t + 2 >= 0 && t + 2 < n_tiles) dma_blocks(p.k_codes, kbuf[(t + 2) & 1], wave, false, t + 2);
+        } else {
+            // (the scale loads first: their use at the end of the step then
+            // waits for nothing issued after them)
+            if (wave == 4 && t + 3 < n_tiles) {
+                ph_s = phys_of(t + 3, lane);
+                phys_s[(t + 3) & 3][16 * (lane & 3) + (lane >> 2)] = ph_s;
+                const int64_t sc = (int64_t)(ph_s < 0 ? 0 : ph_s) * p.scale_stride;
+                kh = p.k_scales[sc];
+                vh = p.v_scales[sc];
+            }
+            if (t + 1 >= 0 && t + 1 < n_tiles) dma_blocks(p.v_codes, vbuf[(t + 1) & 1], wave - 4, true, t + 1);
+        }
+    };
+    auto scales_done = [&](int t) {
+        if (wave == 4 && t + 3 < n_tiles) {
+            const int m2 = (t + 3) & 3;
+            const bool ok = ph_s >= 0;
+            const float ksf = ok ? half_bits_to_float((uint16_t)kh) : 0.f;
+            const float vsf = ok ? half_bits_to_float((uint16_t)vh) : 0.f;
+            ks_s[m2][lane] = ksf;
+            put_v_scales(vs_s[m2], &vw_s[m2], vsf, lane);
+            bias_s[m2][lane] = ok ? -kScoreOffset * ksf : -INFINITY;
+        }
+    };
+    auto end_step = [&](int t) {
+        __builtin_amdgcn_sched_barrier(0);  // the step's work first
+        scales_done(t);
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS-DMA loads have landed
+        __syncthreads();
+    };
+
+    // this wave's rows: group rg, dimensions [128 dh, 128 dh + 128) when split
+    const bool whole = wave < 4;
+    const int rg = whole ? wave : 4 + ((wave - 4) >> 1);
+    const int dh = whole ? 0 : (wave - 4) & 1;
+    const int row = 16 * rg + l16;
+    const int64_t grow = (int64_t)i * R + row0 + row;
+    const bool row_ok = row0 + row < R;
+    const float *qrow = p.q + (row_ok ? grow : (int64_t)i * R + row0) * kDim;
+    const int64_t lim_row = pos0 + (row0 + row) / p.n_qheads;
+    // the mask limit of tile t + 1 (its first cell is 64 (t + 1))
+    auto lim_next = [&](int t) {
+        return (int)max((int64_t)-1, min(lim_row - (int64_t)(t + 1) * kTile, (int64_t)kTile));
+    };
+
+    if (whole) {
+        RowBlock<16, true> rb;
+        rb.init(qrow, row_ok, p.scale_log2, g, l16);
+        stage(-3);
+        end_step(-3);
+        stage(-2);
+        end_step(-2);
+        stage(-1);
+        if (n_tiles > 0) rb.template score<true>(rb.su, kbuf[0], ks_s[0], bias_s[0], lim_next(-1));
+        end_step(-1);
+        for (int t = 0; t < n_tiles - 1; ++t) {
+            stage(t);
+            rb.template step<true>(kbuf[(t + 1) & 1], ks_s[(t + 1) & 3], bias_s[(t + 1) & 3],
+                                   vbuf[t & 1], vs_s[t & 3], &vw_s[t & 3], 0, lim_next(t));
+            end_step(t);
+        }
+        if (n_tiles > 0) {
+            const int t = n_tiles - 1;
+            stage(t);
+            rb.accumulate(rb.stats(), vbuf[t & 1], vs_s[t & 3], &vw_s[t & 3], 0);
+            end_step(t);
+        }
+        rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, 0);
+    } else {
+        RowBlock<8, true> rb;
+        rb.init(qrow, row_ok, p.scale_log2, g, l16);
+        // this wave's two cell blocks of tile t + 1, masked, into LDS
+        auto score_half = [&](int t) {
+            const int8_t *kb = kbuf[(t + 1) & 1];
+            const float *ks_t = ks_s[(t + 1) & 3];
+            const float *bias_t = bias_s[(t + 1) & 3];
+            const int lim = lim_next(t);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int cb = 2 * dh + k;
+                v4f sn = rb.score_block(cb, kb, ks_t, bias_t);
+                if (__any(lim < kTile - 1)) {
+                    const int mo = 16 * cb + 4 * g;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (mo + u > lim) sn[u] = -INFINITY;
+                }
+                xs[(t + 1) & 1][rg - 4][cb][lane] = sn;
+            }
+        };
+        auto load_scores = [&](int t) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) rb.su[cb] = xs[t & 1][rg - 4][cb][lane];
+        };
+        stage(-3);
+        end_step(-3);
+        stage(-2);
+        end_step(-2);
+        stage(-1);
+        if (n_tiles > 0) score_half(-1);
+        end_step(-1);
+        for (int t = 0; t < n_tiles - 1; ++t) {
+            stage(t);
+            load_scores(t);
+            const auto d = rb.prepare(rb.stats(), vs_s[t & 3], &vw_s[t & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            score_half(t);
+            rb.pv(d, vbuf[t & 1], dh);
+            end_step(t);
+        }
+        if (n_tiles > 0) {
+            const int t = n_tiles - 1;
+            stage(t);
+            load_scores(t);
+            rb.accumulate(rb.stats(), vbuf[t & 1], vs_s[t & 3], &vw_s[t & 3], dh);
+            end_step(t);
+        }
+        rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
+    }
+}
+
 template <int DS, bool kMulti>
 void launch_rb(const Params &p, dim3 grid, int cpw, hipStream_t s) {
     switch ((p.n_rows + 15) / 16) {
@@ -1273,6 +1542,13 @@ hipError_t launch_prompt(const Params &p, hipStream_t s) {
     // they fit one to a CU, 48-row ones when the grid is larger (two to a
     // CU), and fewer rows use fewer groups.
     int rb = (p.n_rows + 15) / 16;
+    if (rb > 4 && p.n_logical_pages <= kPtLdsPages) {
+        // more than four row groups: 96-row workgroups of eight compute waves,
+        // one per CU, the vector and matrix work even over the SIMDs
+        const dim3 grid(p.n_inst, (p.n_rows + kDmaRows - 1) / kDmaRows);
+        prompt_dma_kernel<<<grid, 64 * kDmaWaves, 0, s>>>(p);
+        return hipGetLastError();
+    }
     if (rb > 4) rb = (int64_t)p.n_inst * ((p.n_rows + 63) / 64) <= kLatencyWorkgroups ? 4 : 3;
     const dim3 grid(p.n_inst, (p.n_rows + 16 * rb - 1) / (16 * rb));
     switch (rb) {

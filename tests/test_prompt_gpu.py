@@ -50,10 +50,35 @@ CASES = {
     "negative_pos0": (dict(n_q=10, pool_cells=256, pos0=-3, seed=9), []),
     "all_masked": (dict(n_q=6, pool_cells=128, seed=10), [(k, -1) for k in range(8)]),
     "three_instances": (dict(n_inst=3, n_q=9, pool_cells=1024, pos0=[100, 0, 700], seed=11), []),
-    # more than 256 workgroups of 64 rows: the launch takes 48-row workgroups
-    "many_instances_48row_groups": (dict(n_inst=300, n_q=6, pool_cells=256,
-                                         pos0=list(range(-5, 295)), seed=14), []),
+    # 300 workgroups of 96 rows: more than one per CU
+    "many_instances": (dict(n_inst=300, n_q=6, pool_cells=256,
+                            pos0=list(range(-5, 295)), seed=14), []),
 }
+
+
+# Page tables of more than 2,048 pages (not staged whole in LDS): the
+# launch takes the producer-wave form, 64-row workgroups while they fit one
+# to a CU, 48-row ones beyond; checked on sampled positions and instances.
+LARGE_TABLE = {
+    "large_table_64row_groups": dict(n_inst=1, n_q=9, pool_cells=40960, pos0=[40000], seed=17),
+    "large_table_48row_groups": dict(n_inst=130, n_q=8, pool_cells=32784,
+                                     pos0=list(range(32700, 32830)), seed=18),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LARGE_TABLE))
+def test_prompt_large_page_table(name):
+    kw = dict(LARGE_TABLE[name])
+    say(f"case: prompt {name} {kw}")
+    seed = kw.pop("seed")
+    pos0 = kw.pop("pos0")
+    x = gen.make_prompt(None, seed=seed, pos0=pos0, **kw)
+    out, lse = run_prompt(x)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ids = [0, x.n_inst - 1]
+    t_ids = [0, x.q.shape[1] - 1]
+    xs = dataclasses.replace(x, q=x.q[ids], pos0=x.pos0[ids], page_table=x.page_table[ids])
+    check(xs, out[ids], lse[ids], name, t_ids)
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
