@@ -111,3 +111,26 @@ def run_prompt(x, device="cuda", interleave=False):
     api.prompt_attn_batch(pool, dev["page_table"], dev["pos0"], dev["q"], x.softmax_scale, out, lse)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def f32_attend(q, k_hat, v_hat, scale, visible=None):
+    """Plain float32 softmax attention (numpy float32 products and sums) over
+    dequantised rows: the error level a float32 computation reaches."""
+    s = (q @ k_hat.T) * np.float32(scale)
+    if visible is not None:
+        s = np.where(visible, s, np.float32(-np.inf))
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True, dtype=np.float32)
+    return (p @ v_hat) / l, (m + np.log(l))[:, 0]
+
+
+def dequant(codes, scales, phys):
+    """float32 rows code * scale of the physical cells phys (-1: a zero row)."""
+    ok = phys >= 0
+    rows = np.where(ok[:, None], codes[np.where(ok, phys, 0)].astype(np.float32), np.float32(0))
+    return rows * scales[np.where(ok, phys, 0)].view(np.float16).astype(np.float32)[:, None]
+
+
+# GPU error may exceed a float32 computation's by at most this factor
+F32_FACTOR = 4.0

@@ -9,8 +9,8 @@ import pytest
 
 import oracle
 from decode_attention_sparse_amd import inputs as gen
-from tests.gpu_util import (LSE_ATOL, LSE_RTOL, OUT_ATOL, OUT_RTOL, assert_close, run_prompt,
-                            say)
+from tests.gpu_util import (F32_FACTOR, LSE_ATOL, LSE_RTOL, OUT_ATOL, OUT_RTOL, assert_close,
+                            dequant, f32_attend, run_prompt, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,28 +149,6 @@ def test_append_then_prompt_attention():
     e1 = assert_close(out[0], ro, OUT_ATOL, OUT_RTOL, "append+prompt out")
     e2 = assert_close(lse[0], rl, LSE_ATOL, LSE_RTOL, "append+prompt lse")
     say(f"  append + prompt: max|dout| {e1:.2e} max|dlse| {e2:.2e}")
-
-
-def f32_attend(q, k_hat, v_hat, scale, visible=None):
-    """Plain float32 softmax attention (numpy float32 products and sums) over
-    dequantised rows: the error level a float32 computation reaches."""
-    s = (q @ k_hat.T) * np.float32(scale)
-    if visible is not None:
-        s = np.where(visible, s, np.float32(-np.inf))
-    m = s.max(axis=1, keepdims=True)
-    p = np.exp(s - m)
-    l = p.sum(axis=1, keepdims=True, dtype=np.float32)
-    return (p @ v_hat) / l, (m + np.log(l))[:, 0]
-
-
-def dequant(codes, scales, phys):
-    ok = phys >= 0
-    rows = np.where(ok[:, None], codes[np.where(ok, phys, 0)].astype(np.float32), np.float32(0))
-    return rows * scales[np.where(ok, phys, 0)].view(np.float16).astype(np.float32)[:, None]
-
-
-# GPU error may exceed a float32 computation's by at most this factor
-F32_FACTOR = 4.0
 
 
 def test_append_wide_v_diffuse_attention():

@@ -1,7 +1,9 @@
 """GPU parity at the edges of the binary16 scale range: cells whose K or V
 scale is zero, the smallest subnormal (2^-24) or the smallest normal
 (2^-14) among cells with ordinary scales, through the decode entry point
-(fused call and the two passes) and prompt attention, against the oracle.
+(fused call and the two passes) and prompt attention, against the oracle;
+and V scales spread ever wider from cell to cell, against the error a
+plain float32 computation makes on the same pools.
 
 A zero K scale gives the cell a score of exactly 0 (it is not masked); a
 zero V scale makes the cell add nothing to the output but its weight to the
@@ -13,8 +15,10 @@ import dataclasses
 import numpy as np
 import pytest
 
+import oracle
 from decode_attention_sparse_amd import inputs as gen
-from tests.gpu_util import check, run_batch, run_prompt, say, two_pass
+from tests.gpu_util import (F32_FACTOR, OUT_ATOL, OUT_RTOL, check, dequant, f32_attend,
+                            run_batch, run_prompt, say, two_pass)
 from tests.test_prompt_gpu import check as check_prompt
 
 pytestmark = pytest.mark.gpu
@@ -69,3 +73,35 @@ def test_prompt_zero_and_tiny_scales():
     out, lse = run_prompt(x)
     assert np.isfinite(out).all() and np.isfinite(lse).all()
     check_prompt(x, out, lse, "prompt edge scales", t_ids=[0, 13, 27, 39])
+
+
+@pytest.mark.parametrize("octaves", [0, 4, 8, 12, 16, 20])
+def test_v_scale_spread_envelope(octaves):
+    """V scales spread over 2^+-octaves from cell to cell (clipped to the
+    binary16 range), K as drawn (scores of order one: attention spread over
+    many cells).  The P.V weights sit on a grid set by each tile's largest
+    V scale, so the cells with small scales in a tile carry fewer bits; the
+    output must stay within a few times a float32 computation's error at
+    every spread, and within the elementwise tolerance up to 2^+-12 (at
+    2^+-16 and beyond float32 itself comes near or past it)."""
+    rng = np.random.default_rng(500 + octaves)
+    x = gen.make(1).with_n_q(4)
+    v = x.v_scales.view(np.float16).astype(np.float64)
+    v = np.clip(v * np.exp2(rng.uniform(-octaves, octaves, v.shape)), 2.0**-24, 65504.0)
+    x = dataclasses.replace(x, v_scales=v.astype(np.float16).view(np.uint16))
+    out, lse, g, _ = run_batch(x)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attend(x)
+    phys = oracle.gather(x)[0]
+    fo, fl = f32_attend(x.q[0].reshape(-1, 256), dequant(x.k_codes, x.k_scales, phys),
+                        dequant(x.v_codes, x.v_scales, phys), x.softmax_scale)
+    go, ref = out[0].reshape(-1, 256), ro[0].reshape(-1, 256)
+    e_g, e_f = np.abs(go - ref), np.abs(fo - ref)
+    tol = OUT_ATOL + OUT_RTOL * np.abs(ref)
+    say(f"  spread 2^+-{octaves}: max|out| {np.abs(ref).max():.2e}; max|dout| GPU {e_g.max():.2e} "
+        f"float32 {e_f.max():.2e}; worst error / tolerance GPU {(e_g / tol).max():.3f} "
+        f"float32 {(e_f / tol).max():.3f}")
+    assert e_g.max() <= F32_FACTOR * e_f.max() + 1e-7
+    assert np.abs(lse[0].reshape(-1) - rl[0].reshape(-1)).max() <= 1e-5
+    if octaves <= 12:
+        check(x, out, lse, g, what=f"V scales over 2^+-{octaves}")
