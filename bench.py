@@ -62,11 +62,11 @@ MEASURED_TRAFFIC = {
     "chunk": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                           "decode_attention_sparse_amd/csrc/sda_internal.h",
                           "decode_attention_sparse_amd/csrc/sda_api.hip"),
-              "sources_sha256": "074bee5814b91d11af9a219b23b3f095ce9e3b034076ded6d6ed07977295e47e", "fetch_bytes": 1886235, "write_bytes": 1634714},
+              "sources_sha256": "5725351ac2ccf994f9db0bb3ae2a8d48e30566c829987aa6caceea6f03324df4", "fetch_bytes": 1879040, "write_bytes": 1634688},
     "prompt": {"sources": ("decode_attention_sparse_amd/csrc/chunk_mfma.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
-               "sources_sha256": "074bee5814b91d11af9a219b23b3f095ce9e3b034076ded6d6ed07977295e47e", "fetch_bytes": 161504458, "write_bytes": 25264128},
+               "sources_sha256": "5725351ac2ccf994f9db0bb3ae2a8d48e30566c829987aa6caceea6f03324df4", "fetch_bytes": 161506768, "write_bytes": 25264128},
     "append": {"sources": ("decode_attention_sparse_amd/csrc/kv_append.hip",
                            "decode_attention_sparse_amd/csrc/sda_internal.h",
                            "decode_attention_sparse_amd/csrc/sda_api.hip"),
@@ -807,7 +807,7 @@ def main(argv=None):
                      "launch_us_mean": k4_us,
                      "note": "latency-bound: one instance, 2,051 cells; "
                              "traffic = HBM bytes per launch (cold, counters), null if the "
-                             "kernel changed since they were taken: 1.89 MB fetched (the "
+                             "kernel changed since they were taken: 1.88 MB fetched (the "
                              "1.05 MB of code rows once, the query rows and the page-table row "
                              "once per XCD that holds a workgroup of the instance, the scales' "
                              "sectors) and 1.63 MB of chunk partials written (33 chunks x 48 "

@@ -50,8 +50,9 @@
 //       conversion to fp32.  Score errors are at fp32 level relative to the
 //       wave's largest score.
 //   PV  x = p * v_scale / tau in [0, 127], tau = (the tile's largest
-//       v_scale) / 127 (p <= 1: it is taken against the running maximum,
-//       which includes the tile); X = rint(2^16 x) in [0, 127 * 2^16] is
+//       v_scale) / 127 (p <= 1: it is taken against the tile's own maximum,
+//       and the factor from there to the running maximum goes with the
+//       tile's sums into the accumulator); X = rint(2^16 x) in [0, 127 * 2^16] is
 //       written as 2^16 a + 2^8 b + c (a in [0,127], b, c in [-128,127]);
 //       the tile's sums over cells of a, b and c times v_code (three MFMAs)
 //       are exact in int32, 2^8 A + B is formed in int32 (|.| < 2^29), and
@@ -337,9 +338,14 @@ struct RowBlock {
     }
 
     // Softmax statistics of the tile whose scores are in su: the running max
-    // moves to include it; the frame and the reference max it implies.
+    // moves to include it; the frame and the reference max it implies.  The
+    // tile's probabilities are taken against its own maximum t_use (its
+    // largest is 1, so its weights use the whole digit grid however far the
+    // tile lies below the running maximum) and scaled back by
+    // 2^(t_use - running max) <= 1 in the accumulator's factor and the
+    // denominator (prepare()).
     struct Stats {
-        float m_use, corr, frame_new;
+        float corr, frame_new, t_use;
     };
     __device__ __forceinline__ Stats stats() {
         float tmax = -INFINITY;
@@ -351,9 +357,11 @@ struct RowBlock {
         tmax = (tmax == -INFINITY) ? -INFINITY : tmax * coef;  // base-2 tile max
         const float m_new = fmaxf(m_run, tmax);
         Stats st;
-        st.m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        st.corr = __builtin_amdgcn_exp2f(m_run - st.m_use);
+        st.corr = __builtin_amdgcn_exp2f(m_run - ((m_new == -INFINITY) ? 0.f : m_new));
         st.frame_new = (m_run == -INFINITY) ? 1.f : frame * st.corr;
+        // (+inf for a row with no visible cell in the tile: every score is
+        // -inf, so its probabilities come out 0 all the same)
+        st.t_use = (tmax == -INFINITY) ? INFINITY : tmax;
         m_run = m_new;
         return st;
     }
@@ -443,15 +451,17 @@ struct RowBlock {
     // of accumulate()), then the products with the V rows (its P.V half).
     struct Digits {
         v4i xa, xb, xc;
-        float tau3l, tau3h;
+        float tau3l;
     };
     __device__ __forceinline__ Digits prepare(const Stats &st, const float *vs_t, const float *vw_t) {
-        const float m_use = st.m_use, corr = st.corr, frame_new = st.frame_new;
+        const float t_use = st.t_use, corr = st.corr, frame_new = st.frame_new;
         // ---------------- probabilities and their digits for the current tile
         // weights w = p * v_scale on the tile's grid: X = rint(p * v_scale *
         // W) with W = 127 * 2^16 / (the tile's largest V scale) (the slot
-        // holds v_scale * W per cell, and 1 / W after them; p <= 1, so X <=
-        // 127 * 2^16 < 2^23) lands in the low bits of fma(p, v_scale W, 2^23):
+        // holds v_scale * W per cell, and 1 / W after them; p <= 1 against
+        // the tile's maximum, so X <= 127 * 2^16 < 2^23; a rounding above 1
+        // by an ulp still stays below 2^23 and leaves a = 127) lands in the
+        // low bits of fma(p, v_scale W, 2^23):
         // X = 2^16 a + 2^8 b + c with balanced digits b, c in [-128, 127] (a
         // in [0, 127]): c = byte 0 of X, b = byte 1 of X + 2^7, a = byte 2 of
         // X + 2^7 + 2^15 (bit 23 of the float pattern, the exponent's lowest
@@ -466,7 +476,7 @@ struct RowBlock {
             unsigned xs[4], x2[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -m_use));
+                const float pr = __builtin_amdgcn_exp2f(fmaf(su[cb][u], coef, -t_use));
                 psum += pr;
                 xs[u] = __float_as_uint(fmaf(pr, vw[u], kRound));
                 x2[u] = xs[u] + 32896u;
@@ -481,7 +491,11 @@ struct RowBlock {
             xb[cb] = (int)((b01 | b23) ^ 0x80808080u);
             xc[cb] = (int)(c01 | c23);
         }
-        l_part = fmaf(l_part, corr, psum);
+        // the tile's factor to the running maximum, the same for the row's
+        // four lanes (0 for a row with no visible cell in the tile: it adds
+        // nothing)
+        const float scale = t_use == INFINITY ? 0.f : __builtin_amdgcn_exp2f(t_use - m_run);
+        l_part = fmaf(psum, scale, l_part * corr);
 
         // rare: fold the frame into the accumulator before it gets too small
         frame = frame_new;
@@ -491,9 +505,9 @@ struct RowBlock {
             obias *= frame;
             frame = 1.f;
         }
-        // tau3 = 1 / (W frame), kept as tau3l = 2^26 tau3 and tau3h = 2^8 tau3
-        const float tau3l = (kTwo26 * vw_t[w_off]) * __builtin_amdgcn_rcpf(frame);
-        return Digits{xa, xb, xc, tau3l, (1.f / 262144.f) * tau3l};
+        // tau3 = scale / (W frame), kept as tau3l = 2^26 tau3 and tau3h = 2^8 tau3
+        const float tau3l = ((kTwo26 * vw_t[w_off]) * __builtin_amdgcn_rcpf(frame)) * scale;
+        return Digits{xa, xb, xc, tau3l};
     }
 
     // kAlone: a tile with no scoring beside it (the last of a chunk, or the
@@ -503,7 +517,7 @@ struct RowBlock {
     template <bool kAlone = false>
     __device__ __forceinline__ void pv(const Digits &d, const int8_t *vb, int dh) {
         const v4i xa = d.xa, xb = d.xb, xc = d.xc;
-        const float tau3l = d.tau3l, tau3h = d.tau3h;
+        const float tau3l = d.tau3l, tau3h = (1.f / 262144.f) * tau3l;
         // ---------------- O^T += V^T P^T for this wave's blocks of 16 dims
         const int8_t *vp = vb + v_off + 16 * kDB * dh;
 #pragma unroll
@@ -947,8 +961,15 @@ void chunk_mfma_kernel(Params p, int cpw) {
         end_step(t);
     }
     if (n_tiles > 0) emit(n_tiles - 1);  // the (last) chunk's partial
-    if constexpr (kPrompt)
-        rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
+    if constexpr (kPrompt) {
+        // the row's output address formed only here, from an opaque copy of
+        // the row index: hoisted above the tile loop it would hold two 64-bit
+        // pointers across it
+        int r_late = row;
+        __asm__ volatile("" : "+v"(r_late));
+        const int64_t g_late = (int64_t)i * R + row0 + r_late;
+        rb.finish(row_ok ? p.out + g_late * kDim : nullptr, p.lse + g_late, g, dh);
+    }
     if constexpr (kFinal) {
         // each pipeline's partial as the chunk pass would emit it: acc = o *
         // frame, m = m_nat(), l = the row sum
@@ -1372,7 +1393,13 @@ void prompt_dma_kernel(Params p) {
             rb.accumulate(rb.stats(), vbuf[t & 1], vs_s[t & 3], &vw_s[t & 3], 0);
             end_step(t);
         }
-        rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, 0);
+        // the row's output address formed only here, from an opaque copy of
+        // the row index: hoisted above the tile loop it would hold two 64-bit
+        // pointers across it
+        int r_late = row;
+        __asm__ volatile("" : "+v"(r_late));
+        const int64_t g_late = (int64_t)i * R + row0 + r_late;
+        rb.finish(row_ok ? p.out + g_late * kDim : nullptr, p.lse + g_late, g, 0);
     } else {
         RowBlock<8, true> rb;
         rb.init(qrow, row_ok, p.scale_log2, g, l16);
@@ -1422,7 +1449,13 @@ void prompt_dma_kernel(Params p) {
             rb.accumulate(rb.stats(), vbuf[t & 1], vs_s[t & 3], &vw_s[t & 3], dh);
             end_step(t);
         }
-        rb.finish(row_ok ? p.out + grow * kDim : nullptr, p.lse + grow, g, dh);
+        // the row's output address formed only here, from an opaque copy of
+        // the row index: hoisted above the tile loop it would hold two 64-bit
+        // pointers across it
+        int r_late = row;
+        __asm__ volatile("" : "+v"(r_late));
+        const int64_t g_late = (int64_t)i * R + row0 + r_late;
+        rb.finish(row_ok ? p.out + g_late * kDim : nullptr, p.lse + g_late, g, dh);
     }
 }
 

@@ -134,3 +134,27 @@ def dequant(codes, scales, phys):
 
 # GPU error may exceed a float32 computation's by at most this factor
 F32_FACTOR = 4.0
+
+
+def f32_online(q, k_hat, v_hat, scale, visible=None, tile=64):
+    """float32 attention in the order a tiled kernel takes: per tile of
+    cells the scores, its maximum and probabilities (numpy float32), the
+    running maximum, denominator and accumulator rescaled and accumulated
+    tile after tile: the error level of a plain float32 online softmax."""
+    R, N = q.shape[0], k_hat.shape[0]
+    m = np.full(R, -np.inf, np.float32)
+    l = np.zeros(R, np.float32)
+    acc = np.zeros((R, v_hat.shape[1]), np.float32)
+    for t0 in range(0, N, tile):
+        s = (q @ k_hat[t0:t0 + tile].T) * np.float32(scale)
+        if visible is not None:
+            s = np.where(visible[:, t0:t0 + tile], s, np.float32(-np.inf))
+        m_new = np.maximum(m, s.max(axis=1))
+        ref = np.where(np.isneginf(m_new), np.float32(0), m_new)
+        corr = np.where(np.isneginf(m), np.float32(0), np.exp(m - ref)).astype(np.float32)
+        p = np.exp(s - ref[:, None]).astype(np.float32)
+        l = l * corr + p.sum(axis=1, dtype=np.float32)
+        acc = acc * corr[:, None] + p @ v_hat[t0:t0 + tile]
+        m = m_new
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return acc / l[:, None], m + np.log(l)

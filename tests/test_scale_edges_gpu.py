@@ -18,7 +18,7 @@ import pytest
 import oracle
 from decode_attention_sparse_amd import inputs as gen
 from tests.gpu_util import (F32_FACTOR, OUT_ATOL, OUT_RTOL, check, dequant, f32_attend,
-                            run_batch, run_prompt, say, two_pass)
+                            f32_online, run_batch, run_prompt, say, two_pass)
 from tests.test_prompt_gpu import check as check_prompt
 
 pytestmark = pytest.mark.gpu
@@ -105,3 +105,71 @@ def test_v_scale_spread_envelope(octaves):
     assert np.abs(lse[0].reshape(-1) - rl[0].reshape(-1)).max() <= 1e-5
     if octaves <= 12:
         check(x, out, lse, g, what=f"V scales over 2^+-{octaves}")
+    # the same through chunks of 2,048 cells (32 tiles accumulated in one
+    # partial) against a float32 online softmax in the same tile order
+    o2, l2, _, _ = two_pass(x, 2048)
+    oo, _ = f32_online(x.q[0].reshape(-1, 256), dequant(x.k_codes, x.k_scales, phys),
+                       dequant(x.v_codes, x.v_scales, phys), x.softmax_scale)
+    e_2, e_o = np.abs(o2[0].reshape(-1, 256) - ref).max(), np.abs(oo - ref).max()
+    say(f"  chunks of 2,048: max|dout| GPU {e_2:.2e} float32 online softmax {e_o:.2e}")
+    assert e_2 <= F32_FACTOR * e_o + 1e-7
+
+
+@pytest.mark.parametrize("octaves", [4, 8, 12])
+def test_k_scale_spread_envelope(octaves):
+    """K scales spread over 2^+-octaves from cell to cell: scores from order
+    one to the thousands, so attention peaks on few cells and the
+    log-sum-exp grows.  The query digits are exact to 2^-24 of each wave's
+    largest query value, so the scores carry float32-level error relative
+    to the largest score; outputs and log-sum-exps must stay within a few
+    times a float32 computation's error."""
+    rng = np.random.default_rng(600 + octaves)
+    x = gen.make(1).with_n_q(4)
+    k = x.k_scales.view(np.float16).astype(np.float64)
+    k = np.clip(k * np.exp2(rng.uniform(-octaves, octaves, k.shape)), 2.0**-24, 65504.0)
+    x = dataclasses.replace(x, k_scales=k.astype(np.float16).view(np.uint16))
+    out, lse, g, _ = run_batch(x)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    ro, rl = oracle.attend(x)
+    phys = oracle.gather(x)[0]
+    fo, fl = f32_attend(x.q[0].reshape(-1, 256), dequant(x.k_codes, x.k_scales, phys),
+                        dequant(x.v_codes, x.v_scales, phys), x.softmax_scale)
+    go, ref = out[0].reshape(-1, 256), ro[0].reshape(-1, 256)
+    gl, rlf = lse[0].reshape(-1), rl[0].reshape(-1)
+    e_o, f_o = np.abs(go - ref).max(), np.abs(fo - ref).max()
+    e_l, f_l = np.abs(gl - rlf).max(), np.abs(fl - rlf).max()
+    say(f"  K spread 2^+-{octaves}: max|lse| {np.abs(rlf).max():.1f}; max|dout| GPU {e_o:.2e} "
+        f"float32 {f_o:.2e}; max|dlse| GPU {e_l:.2e} float32 {f_l:.2e}")
+    assert e_o <= F32_FACTOR * f_o + 1e-7
+    assert e_l <= F32_FACTOR * f_l + 1e-6
+    check(x, out, lse, g, what=f"K scales over 2^+-{octaves}", strict_lse=False)
+
+
+@pytest.mark.parametrize("octaves", [0, 8, 12, 16])
+def test_prompt_v_scale_spread_envelope(octaves):
+    """Prompt attention with V scales spread over 2^+-octaves (32 tiles per
+    row): within a few times the error of a float32 online softmax taken in
+    the same tile order, on the sampled positions."""
+    rng = np.random.default_rng(700 + octaves)
+    x = gen.make_prompt(None, seed=71, n_inst=1, n_q=64, n_qheads=12, pool_cells=2048)
+    v = x.v_scales.view(np.float16).astype(np.float64)
+    v = np.clip(v * np.exp2(rng.uniform(-octaves, octaves, v.shape)), 2.0**-24, 65504.0)
+    x = dataclasses.replace(x, v_scales=v.astype(np.float16).view(np.uint16))
+    out, lse = run_prompt(x)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    t_ids = [0, 21, 42, 63]
+    ro, rl = oracle.prompt_attend(x, 0, t_ids)
+    cells = x.page_table.shape[1] * 16
+    c = np.arange(cells)
+    phys_all = x.page_table[0][c >> 4] * 16 + (c & 15)
+    nh = x.q.shape[2]
+    t = np.repeat(np.asarray(t_ids), nh)
+    vis = c[None, :] <= (int(x.pos0[0]) + t)[:, None]
+    fo, _ = f32_online(x.q[0][t_ids].reshape(-1, 256), dequant(x.k_codes, x.k_scales, phys_all),
+                       dequant(x.v_codes, x.v_scales, phys_all), x.softmax_scale, vis)
+    go, ref = out[0][t_ids].reshape(-1, 256), ro.reshape(-1, 256)
+    e_o, f_o = np.abs(go - ref).max(), np.abs(fo - ref).max()
+    say(f"  prompt V spread 2^+-{octaves}: max|out| {np.abs(ref).max():.2e}; max|dout| GPU "
+        f"{e_o:.2e} float32 online softmax {f_o:.2e}")
+    assert e_o <= F32_FACTOR * f_o + 1e-7
+    assert np.abs(lse[0][t_ids].reshape(-1) - rl.reshape(-1)).max() <= 1e-5
